@@ -1,0 +1,256 @@
+/*
+ * oasis.h -- C ABI of liboasis.so, the decode hot path of lookahead block
+ * scoring with sparse KV staging, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is OasisKV (arXiv 2608.08097, "OasisKV: Scaling In-Decode KV
+ * Cache Beyond HBM with Lookahead Sparse Prefetching").  Its per-layer decode
+ * chain, as the paperlayer summary's section 4 ("System Design") states it:
+ * draft (lookahead) queries scan per-block min/max key summaries to rank
+ * blocks; a top-K block set under a token budget is predicted; selection keeps
+ * resident predicted blocks and admits at most C new blocks per KV head per
+ * layer, evicting least-recently-selected ones; the admitted blocks are copied
+ * from off-GPU memory into an HBM working set; attention then runs over the
+ * staged blocks only.  One entry point below per step.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - bf16 tensors are passed as uint16_t bit patterns; every array is dense
+ *    row-major with the layout written next to it.
+ *  - Query head g belongs to KV head g / (H_q / H_kv).
+ *  - Request r has n_b(r) = ceil(ctx_len[r] / bs) blocks; token i of block b
+ *    is position b * bs + i and is valid iff that is < ctx_len[r].
+ *  - K/V pools are [B][H_kv][P][2][bs][D]: one block of one KV head is K
+ *    (bs x D) followed by V (bs x D), 2 * bs * D * 2 bytes contiguous.
+ *  - "device" pointers are HBM allocations of the current HIP device;
+ *    "pinned host" pointers come from hipHostMalloc (e.g. torch pin_memory).
+ *    The caller owns every buffer; no call allocates device memory.
+ *  - `stream` arguments are hipStream_t values passed as void* (NULL = the
+ *    null stream); events are hipEvent_t values passed as void*.  Calls only
+ *    enqueue work and return without synchronising the device, except where
+ *    a call says otherwise.
+ *  - Every call returns OASIS_OK or a negative error code; argument errors
+ *    are detected on the host before any work is enqueued, so a failed call
+ *    has no effect.  oasis_last_error() returns a per-thread message for the
+ *    last failure.  No C++ exception crosses this interface.
+ *  - Supported shapes: D = 128, bs = 16, 1 <= H_q / H_kv <= 16,
+ *    NB_max <= 16384; staging: S <= 2048 slots, K_sel <= 1024.  Others
+ *    return OASIS_EUNSUPPORTED.
+ *  - Device-resident indices (selections, slot tables, attention tables) are
+ *    range-checked by the kernels: an index outside its documented range is
+ *    skipped, never dereferenced.
+ */
+#ifndef OASIS_H
+#define OASIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OASIS_OK 0
+#define OASIS_EINVAL (-1)        /* null pointer, bad shape or bad value */
+#define OASIS_EUNSUPPORTED (-2)  /* valid but unsupported shape */
+#define OASIS_EHIP (-3)          /* the HIP runtime reported an error */
+#define OASIS_ENOSPACE (-4)      /* workspace or plan buffer too small */
+
+/* Copy engines for oasis_stage_blocks. */
+#define OASIS_COPY_KERNEL 0      /* device kernel reads the mapped pinned pool */
+#define OASIS_COPY_DMA 1         /* one hipMemcpyAsync per admitted block */
+
+typedef struct oasis_dims {
+    int32_t B;       /* requests in the batch (0 = nothing to do) */
+    int32_t H_q;     /* query heads */
+    int32_t H_kv;    /* KV heads; H_q % H_kv == 0 */
+    int32_t D;       /* head dimension (128) */
+    int32_t bs;      /* tokens per block (16) */
+    int32_t NB_max;  /* block capacity per (request, KV head) of the summary
+                        and score arrays and of a full pool */
+} oasis_dims;
+
+/* Library version string, e.g. "oasis 0.1.0 gfx950". */
+const char *oasis_version(void);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char *oasis_last_error(void);
+
+/* Blocks per KV head per layer per step admitted under a fetch-cap fraction
+ * (section 4 bounds the transfer to C blocks per KV head per layer; sections
+ * 5 and the agihunt summary give the cap as a fraction, default 0.05):
+ * C = max(1, floor(cap * K_b)) for 0 < cap < 1, K_b for cap >= 1 (fetch-all),
+ * 0 for cap <= 0 or NaN.  Returns -1 if K_b < 1. */
+int32_t oasis_fetch_cap_blocks(double cap, int32_t K_b);
+
+/* Per-block key summaries (section 4: coordinate-wise minimum and maximum of
+ * the block's keys, two vectors per block).
+ *   kv       [B][H_kv][NB_max][2][bs][D] bf16, device or pinned host
+ *   ctx_len  [B] int32, device
+ *   kminmax  [B][H_kv][NB_max][2][D] bf16, device; index 0 = min, 1 = max,
+ *            over the block's valid tokens only.  Entries of blocks
+ *            b >= n_b(r) are not written.
+ * Setup work, not part of a decode step. */
+int oasis_build_summaries(const oasis_dims *dims, const uint16_t *kv,
+                          const int32_t *ctx_len, uint16_t *kminmax,
+                          void *stream);
+
+/* Lookahead block scores (section 4: the draft queries scan the compressed
+ * per-block key summaries to rank blocks).  For KV head h of request r and
+ * block b < n_b(r):
+ *     s = sum_{j < J} sum_{g in group(h)} sum_d max(q[j,g,d] kmax[d], q[j,g,d] kmin[d])
+ * (the largest value q . k can take over the block's bounding box, summed
+ * over drafts and the group's query heads), accumulated in fp64 and rounded
+ * once to fp32.  Blocks b >= n_b(r) get -inf.
+ *   q_look   [B][J][H_q][D] bf16, device
+ *   kminmax  [B][H_kv][NB_max][2][D] bf16, device (from oasis_build_summaries)
+ *   ctx_len  [B] int32, device
+ *   scores   [B][H_kv][NB_max] fp32, device, written
+ * Requires J >= 1 and ctx_len[r] <= NB_max * bs (larger values are clamped to
+ * NB_max blocks). */
+int oasis_score_blocks(const oasis_dims *dims, const uint16_t *q_look,
+                       int32_t J, const uint16_t *kminmax,
+                       const int32_t *ctx_len, float *scores, void *stream);
+
+/* Top-K block selection under the token budget (sections 4 and 5: per KV
+ * head and layer, the K_b = budget / bs best-scoring blocks are predicted for
+ * the next step; default budget 2048 tokens).  Order: fp32 score descending,
+ * equal scores by lower block id, NaN below -inf (+0 and -0 equal).  When
+ * n_b(r) <= K_b every block is taken.
+ *   scores   [B][H_kv][NB_max] fp32, device; entries b >= n_b(r) ignored
+ *   ctx_len  [B] int32, device
+ *   sel      [B][H_kv][K_b] int32, device, written: chosen ids ascending,
+ *            then -1
+ *   n_sel    [B][H_kv] int32, device, written: min(n_b(r), K_b) */
+int oasis_select_topk(const oasis_dims *dims, const float *scores,
+                      const int32_t *ctx_len, int32_t K_b, int32_t *sel,
+                      int32_t *n_sel, void *stream);
+
+/* Staging of the predicted set into the HBM working set (section 4: selection
+ * preserves resident predicted blocks, admits at most C non-resident
+ * predicted blocks per KV head per layer and pairs them with
+ * least-recently-selected eviction targets; the admitted blocks are copied
+ * from the off-GPU pool into HBM before the next step's attention).
+ *
+ * State per (request r, KV head h) lives in a slot table of S slots:
+ * slot_block[s] is the block held by slot s (-1 = free) and slot_stamp[s] the
+ * last step at which that block was predicted or admitted.  The resident set
+ * R is the set of held blocks.  Initialise slot_block to -1 before step 0.
+ * Given the predicted set P (sel / n_sel) of step `step`:
+ *   1. blocks of P that are resident get stamp = step;
+ *   2. the admitted list A is the first min(C, |P \ R|) blocks of P \ R in
+ *      order of fp32 score descending, then block id ascending;
+ *   3. free capacity K_b - |R| is used first; each further admit evicts one
+ *      block of R \ P, taking them by stamp ascending, then block id
+ *      ascending;
+ *   4. admitted blocks are placed into slots that were free before this step
+ *      (ascending slot index in admission order), so a slot evicted now is
+ *      not overwritten until the next step: the attention still reading the
+ *      previous table is never raced.  S >= K_b + C guarantees such a slot
+ *      for every admit; with fewer slots, admits beyond the free slots are
+ *      dropped this step (an empty table, as at step 0, always has room);
+ *   5. each admitted block (8 KiB for bs = 16, D = 128) is copied from
+ *      host_pool[r][h][block] to ws_pool[r][h][slot].
+ * Step 0 with C = K_b is the uncapped initial fill.  Resident blocks that are
+ * no longer predicted stay resident (and attended) until evicted.
+ *
+ * The table for the next attention (tbl_slot / tbl_block / tbl_n, capacity
+ * K_b entries per (r, h)) lists every resident slot after the step, in
+ * ascending slot order.  It must not be a table that an attention still in
+ * flight reads: alternate two tables.
+ *
+ * Ordering: the slot-table update and plan run on `stream`.  Copies run on
+ * `copy_stream` (NULL = `stream`) after the plan and after `wait_event` (if
+ * not NULL), which must mark the end of every attention that read the
+ * table of the previous step.  `done_event` (if not NULL) is recorded on
+ * `copy_stream` after the last copy: make the next attention wait on it.
+ *
+ * Copy engines: OASIS_COPY_KERNEL enqueues a gather kernel that reads the
+ * pinned pool through its device mapping; it never blocks the caller.
+ * OASIS_COPY_DMA reads the plan back into `host_plan` (pinned host, at least
+ * oasis_stage_host_plan_bytes() bytes), BLOCKS THE CALLING THREAD until the
+ * plan kernel has finished, then enqueues one hipMemcpyAsync per admitted
+ * block (adjacent blocks into adjacent slots are merged) on copy_stream.
+ *
+ * Calls that overlap on the same slot table race; keep them ordered. */
+typedef struct oasis_stage_args {
+    const int32_t *sel;     /* [B][H_kv][K_sel] device, ascending, -1 padded */
+    const int32_t *n_sel;   /* [B][H_kv] device */
+    int32_t K_sel;          /* row stride of sel (normally K_b) */
+    const float *scores;    /* [B][H_kv][NB_max] fp32 device (admission order) */
+    int32_t K_b;            /* budget in blocks per (r, h) */
+    int32_t C;              /* fetch cap in blocks per (r, h) per step, 0..K_b */
+    int32_t S;              /* slots per (r, h); S >= K_b (see below) */
+    int32_t step;           /* step number, >= 0, increasing */
+    int32_t *slot_block;    /* [B][H_kv][S] device, in/out */
+    int32_t *slot_stamp;    /* [B][H_kv][S] device, in/out */
+    const int32_t *ctx_len; /* [B] device */
+    const void *host_pool;  /* [B][H_kv][NB_max][2][bs][D] bf16, pinned host */
+    void *ws_pool;          /* [B][H_kv][S][2][bs][D] bf16, device */
+    int32_t *tbl_slot;      /* [B][H_kv][K_b] device, written */
+    int32_t *tbl_block;     /* [B][H_kv][K_b] device, written */
+    int32_t *tbl_n;         /* [B][H_kv] device, written */
+    int32_t *plan;          /* device workspace, oasis_stage_plan_bytes() */
+    size_t plan_bytes;
+    void *host_plan;        /* pinned host, OASIS_COPY_DMA only */
+    size_t host_plan_bytes;
+    int32_t copy_mode;      /* OASIS_COPY_KERNEL or OASIS_COPY_DMA */
+    void *stream;
+    void *copy_stream;
+    void *wait_event;
+    void *done_event;
+} oasis_stage_args;
+
+/* Bytes of the device plan workspace and of the pinned host plan buffer:
+ * 4 * B * H_kv * (2 + 2 * max(C, 1)). */
+size_t oasis_stage_plan_bytes(const oasis_dims *dims, int32_t C);
+size_t oasis_stage_host_plan_bytes(const oasis_dims *dims, int32_t C);
+
+/* One staging step.  Once the plan kernel has run, the plan workspace holds
+ * int32 [B][H_kv][2 + 2 * max(C, 1)]: per (r, h) the admit count, the evict
+ * count, then the admitted (slot, block) pairs in admission order.  The
+ * host plan (OASIS_COPY_DMA) receives the same array. */
+int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *args);
+
+/* Sparse GQA decode attention over the listed blocks (sections 4 and 7:
+ * attention runs over the HBM working set only).  For query head g of
+ * request r, KV head h = g / G, the token set is every valid token of the
+ * blocks tbl[r][h][0 .. tbl_n[r][h]); with l_t = sm_scale * q . k_t:
+ *     out = sum_t exp(l_t - m) v_t / sum_t exp(l_t - m),  m = max_t l_t
+ *     lse = m + ln(sum_t exp(l_t - m))       (natural log)
+ * bf16 inputs, fp32 accumulation and online softmax, bf16 (round to nearest
+ * even) output.  An empty token set gives out = 0 and lse = -inf.
+ *   q          [B][H_q][D] bf16, device
+ *   kv_pool    [B][H_kv][P][2][bs][D] bf16, device (P = NB_max for a full
+ *              pool read through the selection; P = S for a working set)
+ *   tbl_slot   [B][H_kv][T] int32, device: pool slot of each entry
+ *   tbl_block  [B][H_kv][T] int32, device: logical block id of each entry
+ *              (masks the request's partial last block)
+ *   tbl_n      [B][H_kv] int32, device: entries used, clamped to [0, T]
+ *              Entries with slot outside [0, P) or block outside [0, n_b(r))
+ *              are skipped.
+ *   ctx_len    [B] int32, device
+ *   out        [B][H_q][D] bf16, device, written
+ *   lse        [B][H_q] fp32, device, written; may be NULL
+ *   ws         device workspace of oasis_attn_workspace_bytes(dims, T,
+ *              n_split) bytes (may be NULL when that is 0)
+ *   n_split    number of partitions of each table row (0 = chosen by the
+ *              library from the shape and the device's compute-unit count;
+ *              otherwise 1..64) */
+size_t oasis_attn_workspace_bytes(const oasis_dims *dims, int32_t T,
+                                  int32_t n_split);
+int32_t oasis_attn_num_splits(const oasis_dims *dims, int32_t T,
+                              int32_t n_split);
+int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q,
+                             const uint16_t *kv_pool, int32_t P,
+                             const int32_t *tbl_slot,
+                             const int32_t *tbl_block, const int32_t *tbl_n,
+                             int32_t T, const int32_t *ctx_len,
+                             float sm_scale, uint16_t *out, float *lse,
+                             void *ws, size_t ws_bytes, int32_t n_split,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OASIS_H */

@@ -1,0 +1,290 @@
+"""Python binding of liboasis.so: argument marshalling only.
+
+Each function carries the name of the C entry point it calls (include/oasis.h
+documents the semantics).  Tensors supply device memory, pinned host memory
+and streams; every step of the decode path runs in the library's HIP kernels.
+If the library is missing the import of this module raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboasis.so")
+
+OASIS_OK = 0
+OASIS_EINVAL = -1
+OASIS_EUNSUPPORTED = -2
+OASIS_EHIP = -3
+OASIS_ENOSPACE = -4
+OASIS_COPY_KERNEL = 0
+OASIS_COPY_DMA = 1
+
+_I32 = ctypes.c_int32
+_P = ctypes.c_void_p
+
+
+class OasisError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"oasis error {code}: {msg}")
+        self.code = code
+
+
+class oasis_dims(ctypes.Structure):
+    _fields_ = [("B", _I32), ("H_q", _I32), ("H_kv", _I32), ("D", _I32), ("bs", _I32),
+                ("NB_max", _I32)]
+
+
+class oasis_stage_args(ctypes.Structure):
+    _fields_ = [
+        ("sel", _P), ("n_sel", _P), ("K_sel", _I32), ("scores", _P), ("K_b", _I32), ("C", _I32),
+        ("S", _I32), ("step", _I32), ("slot_block", _P), ("slot_stamp", _P), ("ctx_len", _P),
+        ("host_pool", _P), ("ws_pool", _P), ("tbl_slot", _P), ("tbl_block", _P), ("tbl_n", _P),
+        ("plan", _P), ("plan_bytes", ctypes.c_size_t), ("host_plan", _P),
+        ("host_plan_bytes", ctypes.c_size_t), ("copy_mode", _I32), ("stream", _P),
+        ("copy_stream", _P), ("wait_event", _P), ("done_event", _P)]
+
+
+# name -> (restype, argtypes)
+_SIGNATURES = {
+    "oasis_version": (ctypes.c_char_p, []),
+    "oasis_last_error": (ctypes.c_char_p, []),
+    "oasis_fetch_cap_blocks": (_I32, [ctypes.c_double, _I32]),
+    "oasis_build_summaries": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _P, _P]),
+    "oasis_score_blocks": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _I32, _P, _P, _P, _P]),
+    "oasis_select_topk": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P]),
+    "oasis_stage_plan_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32]),
+    "oasis_stage_host_plan_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32]),
+    "oasis_stage_blocks": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args)]),
+    "oasis_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32, _I32]),
+    "oasis_attn_num_splits": (_I32, [ctypes.POINTER(oasis_dims), _I32, _I32]),
+    "oasis_sparse_decode_attn": (ctypes.c_int, [
+        ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
+        ctypes.c_size_t, _I32, _P]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m prefetch_block_scoring_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OASIS_OK:
+        raise OasisError(rc, _lib.oasis_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        s = torch.cuda.current_stream()
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _event(ev) -> Optional[int]:
+    if ev is None:
+        return None
+    if isinstance(ev, int):
+        return ev
+    if not ev.cuda_event:
+        ev.record()  # torch creates its event lazily on first record
+    return ev.cuda_event
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device: Optional[str] = "cuda"):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device == "cuda" and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def dims(B, H_q, H_kv, NB_max, D=128, bs=16) -> oasis_dims:
+    return oasis_dims(int(B), int(H_q), int(H_kv), int(D), int(bs), int(NB_max))
+
+
+# --------------------------------------------------------------------------
+
+
+def oasis_version() -> str:
+    return _lib.oasis_version().decode()
+
+
+def oasis_last_error() -> str:
+    return _lib.oasis_last_error().decode()
+
+
+def oasis_fetch_cap_blocks(cap: float, K_b: int) -> int:
+    return int(_lib.oasis_fetch_cap_blocks(float(cap), int(K_b)))
+
+
+def oasis_build_summaries(kv: torch.Tensor, ctx_len: torch.Tensor, kminmax=None, stream=None):
+    """kv bf16 [B][H_kv][NB_max][2][bs][D] (device or pinned host) ->
+    kminmax bf16 [B][H_kv][NB_max][2][D]."""
+    _need(kv, "kv", torch.bfloat16, 6, device=None)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    B, H_kv, NB, _, bs, D = kv.shape
+    if kminmax is None:
+        kminmax = torch.empty((B, H_kv, NB, 2, D), dtype=torch.bfloat16, device=ctx_len.device)
+    _need(kminmax, "kminmax", torch.bfloat16, 5)
+    d = dims(B, H_kv, H_kv, NB, D, bs)
+    _check(_lib.oasis_build_summaries(ctypes.byref(d), _ptr(kv), _ptr(ctx_len), _ptr(kminmax),
+                                      _stream(stream)))
+    return kminmax
+
+
+def oasis_score_blocks(q_look: torch.Tensor, kminmax: torch.Tensor, ctx_len: torch.Tensor,
+                       scores=None, bs: int = 16, stream=None):
+    """q_look bf16 [B][J][H_q][D], kminmax bf16 [B][H_kv][NB_max][2][D] ->
+    scores fp32 [B][H_kv][NB_max]."""
+    _need(q_look, "q_look", torch.bfloat16, 4)
+    _need(kminmax, "kminmax", torch.bfloat16, 5)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    B, J, H_q, D = q_look.shape
+    _, H_kv, NB, _, _ = kminmax.shape
+    if scores is None:
+        scores = torch.empty((B, H_kv, NB), dtype=torch.float32, device=q_look.device)
+    _need(scores, "scores", torch.float32, 3)
+    d = dims(B, H_q, H_kv, NB, D, bs)
+    _check(_lib.oasis_score_blocks(ctypes.byref(d), _ptr(q_look), J, _ptr(kminmax), _ptr(ctx_len),
+                                   _ptr(scores), _stream(stream)))
+    return scores
+
+
+def oasis_select_topk(scores: torch.Tensor, ctx_len: torch.Tensor, K_b: int, sel=None, n_sel=None,
+                      bs: int = 16, stream=None):
+    """scores fp32 [B][H_kv][NB_max] -> (sel int32 [B][H_kv][K_b], n_sel int32 [B][H_kv])."""
+    _need(scores, "scores", torch.float32, 3)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    B, H_kv, NB = scores.shape
+    if sel is None:
+        sel = torch.empty((B, H_kv, K_b), dtype=torch.int32, device=scores.device)
+    if n_sel is None:
+        n_sel = torch.empty((B, H_kv), dtype=torch.int32, device=scores.device)
+    _need(sel, "sel", torch.int32, 3)
+    _need(n_sel, "n_sel", torch.int32, 2)
+    d = dims(B, H_kv, H_kv, NB, 128, bs)
+    _check(_lib.oasis_select_topk(ctypes.byref(d), _ptr(scores), _ptr(ctx_len), int(K_b), _ptr(sel),
+                                  _ptr(n_sel), _stream(stream)))
+    return sel, n_sel
+
+
+def oasis_stage_plan_bytes(B: int, H_kv: int, C: int) -> int:
+    d = dims(B, H_kv, H_kv, 1)
+    return int(_lib.oasis_stage_plan_bytes(ctypes.byref(d), int(C)))
+
+
+def oasis_stage_blocks(*, sel, n_sel, scores, ctx_len, K_b: int, C: int, step: int, slot_block,
+                       slot_stamp, host_pool, ws_pool, tbl_slot, tbl_block, tbl_n, plan,
+                       host_plan=None, copy_mode: int = OASIS_COPY_KERNEL, stream=None,
+                       copy_stream=None, wait_event=None, done_event=None):
+    """One staging step (include/oasis.h).  host_pool: pinned bf16
+    [B][H_kv][NB_max][2][bs][D]; ws_pool: device bf16 [B][H_kv][S][2][bs][D];
+    slot tables int32 [B][H_kv][S]; tables int32 [B][H_kv][K_b]; plan: device
+    int32 of oasis_stage_plan_bytes() bytes."""
+    _need(sel, "sel", torch.int32, 3)
+    _need(n_sel, "n_sel", torch.int32, 2)
+    _need(scores, "scores", torch.float32, 3)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    _need(slot_block, "slot_block", torch.int32, 3)
+    _need(slot_stamp, "slot_stamp", torch.int32, 3)
+    _need(host_pool, "host_pool", torch.bfloat16, 6, device=None)
+    _need(ws_pool, "ws_pool", torch.bfloat16, 6)
+    _need(tbl_slot, "tbl_slot", torch.int32, 3)
+    _need(tbl_block, "tbl_block", torch.int32, 3)
+    _need(tbl_n, "tbl_n", torch.int32, 2)
+    B, H_kv, NB, _, bs, D = host_pool.shape
+    S = ws_pool.shape[2]
+    if tuple(slot_block.shape) != (B, H_kv, S) or tuple(slot_stamp.shape) != (B, H_kv, S):
+        raise ValueError("slot tables must be [B][H_kv][S]")
+    if tuple(tbl_slot.shape) != (B, H_kv, K_b) or tuple(tbl_block.shape) != (B, H_kv, K_b):
+        raise ValueError("attention tables must be [B][H_kv][K_b]")
+    if tuple(scores.shape) != (B, H_kv, NB) or sel.shape[:2] != (B, H_kv):
+        raise ValueError("scores / sel shape mismatch")
+    d = dims(B, H_kv, H_kv, NB, D, bs)
+    a = oasis_stage_args()
+    a.sel, a.n_sel, a.K_sel, a.scores = sel.data_ptr(), n_sel.data_ptr(), sel.shape[2], scores.data_ptr()
+    a.K_b, a.C, a.S, a.step = int(K_b), int(C), int(S), int(step)
+    a.slot_block, a.slot_stamp, a.ctx_len = slot_block.data_ptr(), slot_stamp.data_ptr(), ctx_len.data_ptr()
+    a.host_pool, a.ws_pool = host_pool.data_ptr(), ws_pool.data_ptr()
+    a.tbl_slot, a.tbl_block, a.tbl_n = tbl_slot.data_ptr(), tbl_block.data_ptr(), tbl_n.data_ptr()
+    a.plan, a.plan_bytes = plan.data_ptr(), plan.numel() * plan.element_size()
+    if host_plan is not None:
+        a.host_plan, a.host_plan_bytes = host_plan.data_ptr(), host_plan.numel() * host_plan.element_size()
+    a.copy_mode = int(copy_mode)
+    a.stream = _stream(stream)
+    a.copy_stream = _stream(copy_stream) if copy_stream is not None else None
+    a.wait_event = _event(wait_event)
+    a.done_event = _event(done_event)
+    _check(_lib.oasis_stage_blocks(ctypes.byref(d), ctypes.byref(a)))
+
+
+def oasis_attn_workspace_bytes(B: int, H_q: int, H_kv: int, T: int, n_split: int = 0) -> int:
+    d = dims(B, H_q, H_kv, 1)
+    return int(_lib.oasis_attn_workspace_bytes(ctypes.byref(d), int(T), int(n_split)))
+
+
+def oasis_attn_num_splits(B: int, H_q: int, H_kv: int, T: int, n_split: int = 0) -> int:
+    d = dims(B, H_q, H_kv, 1)
+    return int(_lib.oasis_attn_num_splits(ctypes.byref(d), int(T), int(n_split)))
+
+
+def oasis_sparse_decode_attn(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: torch.Tensor,
+                             tbl_block: torch.Tensor, tbl_n: torch.Tensor, ctx_len: torch.Tensor,
+                             sm_scale: Optional[float] = None, out=None, lse=None, ws=None,
+                             n_split: int = 0, want_lse: bool = False, stream=None):
+    """q bf16 [B][H_q][D], kv_pool bf16 [B][H_kv][P][2][bs][D], tables int32
+    [B][H_kv][T] and [B][H_kv] -> out bf16 [B][H_q][D] (and lse fp32 [B][H_q])."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 6)
+    _need(tbl_slot, "tbl_slot", torch.int32, 3)
+    _need(tbl_block, "tbl_block", torch.int32, 3)
+    _need(tbl_n, "tbl_n", torch.int32, 2)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    B, H_q, D = q.shape
+    _, H_kv, P, _, bs, _ = kv_pool.shape
+    T = tbl_slot.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    d = dims(B, H_q, H_kv, max(P, 1), D, bs)
+    need = int(_lib.oasis_attn_workspace_bytes(ctypes.byref(d), T, int(n_split)))
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _check(_lib.oasis_sparse_decode_attn(
+        ctypes.byref(d), _ptr(q), _ptr(kv_pool), int(P), _ptr(tbl_slot), _ptr(tbl_block), _ptr(tbl_n),
+        int(T), _ptr(ctx_len), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), int(n_split), _stream(stream)))
+    return (out, lse) if want_lse or lse is not None else out

@@ -1,0 +1,362 @@
+// Sparse GQA decode attention over the staged blocks (split-K flash decode).
+//
+// OasisKV (arXiv 2608.08097), paperlayer summary, sections 4 and 7: decode
+// attention runs only over the KV blocks held in the HBM working set.  For each
+// query head, softmax attention over the valid tokens of the listed blocks.
+//
+// Work split: a workgroup of four waves owns one (request, KV head) and one of
+// n_split contiguous ranges of its table; the waves take the range's entries
+// round-robin and keep private online-softmax states, merged in LDS at the end;
+// with n_split > 1 a second kernel merges the ranges by their log-sum-exp.
+//
+// Per 16-token block (8 KiB of K and V) a wave does:
+//   q . K   on the matrix cores: one v_mfma_f32_16x16x32_bf16 per 32 dims,
+//           A = K (16 tokens x 32 dims), B = Q^T (32 dims x 16 head slots, the
+//           group's G heads, the rest zero).  The G heads of a KV group share
+//           every K load, and the MFMA replaces G * 128 VALU FMAs per token.
+//           Each lane loads 16 bytes of one key row per MFMA; since the sum
+//           over dims may be taken in any order, A and B only have to agree on
+//           which dims a lane brings.
+//   softmax fp32, base-2 online max / sum per head on the MFMA output.
+//   p . V   on the VALU: lane (c, q) owns dims [8c, 8c + 8) of tokens
+//           q, q + 4, q + 8, q + 12; each V load is a fully used 1 KiB row
+//           group; the four token groups are summed once at the end.
+// Loads of the next block are issued before the current block is computed.
+#include "oasis_internal.h"
+
+#include <cmath>
+
+namespace oasis {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kVecPerBlock = (int)(kBlockBytes / 16);  // uint4 per K+V block (512)
+constexpr float kLn2 = 0.693147180559945309f;
+
+struct AttnArgs {
+    const uint16_t *q;
+    const uint16_t *kv;
+    int P;
+    const int32_t *tbl_slot;
+    const int32_t *tbl_block;
+    const int32_t *tbl_n;
+    int T;
+    const int32_t *ctx_len;
+    float scale_log2;  // sm_scale * log2(e)
+    int H_q, H_kv, n_split;
+    uint16_t *out;
+    float *lse;
+    float *ws;
+};
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// GP: head slots compiled in (a power of two >= G); G = H_q / H_kv at run time.
+template <int GP>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+    __shared__ float p_lds[kWaves][17][16];  // per wave: p[token][head]; row 16 = rescale
+    __shared__ float m_lds[kWaves][16];
+    __shared__ float l_lds[kWaves][16];
+    __shared__ float o_lds[kWaves][GP][kD];
+
+    const int rh = blockIdx.x;
+    const int split = blockIdx.y;
+    const int r = rh / a.H_kv;
+    const int h = rh - r * a.H_kv;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;  // MFMA row / column index
+    const int grp = lane >> 4;  // lane group 0..3
+    const int G = a.H_q / a.H_kv;
+
+    const int ctx = a.ctx_len[r];
+    const int nb = ctx <= 0 ? 0 : (ctx + kBs - 1) / kBs;
+    int n = a.tbl_n[rh];
+    n = n < 0 ? 0 : (n > a.T ? a.T : n);
+    const int per = (n + a.n_split - 1) / a.n_split;
+    const int i0 = split * per;
+    const int i1 = min(n, i0 + per);
+
+    // Q^T as the MFMA B operand: lane (col, grp) brings head `col`, dims
+    // kk * 32 + grp * 8 + [0, 8) for k-step kk.
+    bf16x8 qb[4];
+    if (col < G) {
+        const uint4 *qrow = reinterpret_cast<const uint4 *>(
+            a.q + ((size_t)r * a.H_q + (size_t)h * G + col) * kD);
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) qb[kk] = __builtin_bit_cast(bf16x8, qrow[kk * 4 + grp]);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) qb[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+
+    float acc[GP][8];
+#pragma unroll
+    for (int g = 0; g < GP; g++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[g][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int32_t *ts = a.tbl_slot + (size_t)rh * a.T;
+    const int32_t *tb = a.tbl_block + (size_t)rh * a.T;
+    const uint4 *pool = reinterpret_cast<const uint4 *>(a.kv) + (size_t)rh * a.P * kVecPerBlock;
+
+    // next valid entry at or after i (wave-uniform); returns i1 if none
+    auto next_valid = [&](int i, int &blk) -> const uint4 * {
+        for (; i < i1; i += kWaves) {
+            const int s = ts[i], b = tb[i];
+            if (s >= 0 && s < a.P && b >= 0 && b < nb) {
+                blk = b;
+                return pool + (size_t)s * kVecPerBlock;
+            }
+        }
+        return nullptr;
+    };
+    auto load = [&](const uint4 *src, uint4 (&kr)[4], uint4 (&vr)[4]) {
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) kr[kk] = src[col * 16 + kk * 4 + grp];
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) vr[qq] = src[256 + (qq * 4 + grp) * 16 + col];
+    };
+
+    int i = i0 + wave;
+    int blk_c = 0;
+    const uint4 *src_c = nullptr;
+    for (; i < i1; i += kWaves) {
+        const int s = ts[i], b = tb[i];
+        if (s >= 0 && s < a.P && b >= 0 && b < nb) {
+            blk_c = b;
+            src_c = pool + (size_t)s * kVecPerBlock;
+            break;
+        }
+    }
+    uint4 kc[4], vc[4];
+    if (src_c) load(src_c, kc, vc);
+
+    float(*pl)[16] = p_lds[wave];
+    while (src_c) {
+        int blk_n = 0;
+        const uint4 *src_n = next_valid(i + kWaves, blk_n);
+        uint4 kn[4], vn[4];
+        if (src_n) load(src_n, kn, vn);
+
+        // logits of head `col` for tokens 4 * grp + [0, 4)
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[kk]), qb[kk], c,
+                                                         0, 0, 0);
+        const int valid = ctx - blk_c * kBs;
+        float sv[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) sv[t] = (4 * grp + t < valid) ? c[t] * a.scale_log2 : -INFINITY;
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_(m_run - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const float p = exp2_(sv[t] - m_use);
+            pl[4 * grp + t][col] = p;
+            psum += p;
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        if (grp == 0) pl[16][col] = alpha;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+        for (int g = 0; g < GP; g++) {
+            const float al = pl[16][g];
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[g][e] *= al;
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) {
+            const int t = qq * 4 + grp;
+            const uint32_t w[4] = {vc[qq].x, vc[qq].y, vc[qq].z, vc[qq].w};
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                v[2 * e] = bf16_lo(w[e]);
+                v[2 * e + 1] = bf16_hi(w[e]);
+            }
+#pragma unroll
+            for (int g = 0; g < GP; g++) {
+                const float p = pl[t][g];
+#pragma unroll
+                for (int e = 0; e < 8; e++) acc[g][e] = fmaf(p, v[e], acc[g][e]);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        if (!src_n) break;
+        // advance: the entry just prefetched becomes current
+        {
+            int j = i + kWaves;
+            for (; j < i1; j += kWaves) {
+                const int s = ts[j], b = tb[j];
+                if (s >= 0 && s < a.P && b >= 0 && b < nb) break;
+            }
+            i = j;
+        }
+        src_c = src_n;
+        blk_c = blk_n;
+#pragma unroll
+        for (int x = 0; x < 4; x++) {
+            kc[x] = kn[x];
+            vc[x] = vn[x];
+        }
+    }
+
+    // sum the four token groups of this wave
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+    for (int g = 0; g < GP; g++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            float x = acc[g][e];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            acc[g][e] = x;
+        }
+    if (grp == 0) {
+#pragma unroll
+        for (int g = 0; g < GP; g++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) o_lds[wave][g][col * 8 + e] = acc[g][e];
+        m_lds[wave][col] = m_run;
+        l_lds[wave][col] = l_run;
+    }
+    __syncthreads();
+
+    // merge the waves; one thread per (head, dim)
+    for (int idx = tid; idx < G * kD; idx += kThreads) {
+        const int g = idx / kD, d = idx - g * kD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) M = fmaxf(M, m_lds[w][g]);
+        float o = 0.f, L = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) {
+                const float mw = m_lds[w][g];
+                const float f = (mw == -INFINITY) ? 0.f : exp2_(mw - M);
+                o += f * o_lds[w][g][d];
+                L += f * l_lds[w][g];
+            }
+        }
+        const size_t row = (size_t)r * a.H_q + (size_t)h * G + g;
+        if (a.n_split == 1) {
+            a.out[row * kD + d] = f32_to_bf16(L > 0.f ? o / L : 0.f);
+            if (d == 0 && a.lse)
+                a.lse[row] = (M == -INFINITY || !(L > 0.f)) ? -INFINITY : (M + __log2f(L)) * kLn2;
+        } else {
+            float *part = a.ws + (row * a.n_split + split) * (kD + 2);
+            part[d] = o;
+            if (d == 0) {
+                part[kD] = M;
+                part[kD + 1] = L;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kD) void attn_combine_kernel(const float *__restrict__ ws, int n_split,
+                                                          uint16_t *__restrict__ out,
+                                                          float *__restrict__ lse) {
+    const size_t row = blockIdx.x;
+    const int d = threadIdx.x;
+    const float *base = ws + row * n_split * (kD + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; s++) M = fmaxf(M, base[s * (kD + 2) + kD]);
+    float o = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < n_split; s++) {
+            const float ms = base[s * (kD + 2) + kD];
+            const float f = (ms == -INFINITY) ? 0.f : exp2_(ms - M);
+            o += f * base[s * (kD + 2) + d];
+            L += f * base[s * (kD + 2) + kD + 1];
+        }
+    }
+    out[row * kD + d] = f32_to_bf16(L > 0.f ? o / L : 0.f);
+    if (d == 0 && lse) lse[row] = (M == -INFINITY || !(L > 0.f)) ? -INFINITY : (M + __log2f(L)) * kLn2;
+}
+
+template <int GP>
+hipError_t launch_g(const oasis_dims &d, const AttnArgs &a, hipStream_t s) {
+    dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)a.n_split);
+    hipLaunchKernelGGL(attn_kernel<GP>, grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int attn_splits(const oasis_dims &d, int T, int n_split) {
+    if (n_split > 0) return n_split < 64 ? n_split : 64;
+    const long pairs = (long)d.B * d.H_kv;
+    if (pairs <= 0 || T <= 0) return 1;
+    // Enough workgroups to give every compute unit several four-wave groups,
+    // without splitting a row below eight entries (two per wave).
+    const long target = 4L * device_cu_count();
+    long s = (target + pairs - 1) / pairs;
+    const long cap = (T + 7) / 8;
+    if (s > cap) s = cap;
+    if (s > 64) s = 64;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+size_t attn_ws_bytes(const oasis_dims &d, int T, int n_split) {
+    const int s = attn_splits(d, T, n_split);
+    if (s <= 1) return 0;
+    return (size_t)d.B * d.H_q * s * (kD + 2) * sizeof(float);
+}
+
+hipError_t launch_attn(const oasis_dims &d, const uint16_t *q, const uint16_t *kv_pool, int P,
+                       const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n,
+                       int T, const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse,
+                       float *ws, int n_split, hipStream_t s) {
+    AttnArgs a;
+    a.q = q;
+    a.kv = kv_pool;
+    a.P = P;
+    a.tbl_slot = tbl_slot;
+    a.tbl_block = tbl_block;
+    a.tbl_n = tbl_n;
+    a.T = T;
+    a.ctx_len = ctx_len;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.H_q = d.H_q;
+    a.H_kv = d.H_kv;
+    a.n_split = n_split;
+    a.out = out;
+    a.lse = lse;
+    a.ws = ws;
+    const int G = d.H_q / d.H_kv;
+    hipError_t e;
+    if (G <= 1) e = launch_g<1>(d, a, s);
+    else if (G <= 2) e = launch_g<2>(d, a, s);
+    else if (G <= 4) e = launch_g<4>(d, a, s);
+    else if (G <= 8) e = launch_g<8>(d, a, s);
+    else e = launch_g<16>(d, a, s);
+    if (e != hipSuccess || n_split <= 1) return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(d.B * d.H_q)), dim3(kD), 0, s, ws,
+                       n_split, out, lse);
+    return hipGetLastError();
+}
+
+}  // namespace oasis

@@ -1,0 +1,294 @@
+// KV selection and staging into the HBM working set.
+//
+// OasisKV (arXiv 2608.08097), paperlayer summary, section 4: at most C blocks
+// per KV head are transferred per layer; selection keeps resident predicted
+// blocks and pairs admitted non-resident predicted blocks with
+// least-recently-selected eviction targets; the full cache stays in host
+// memory and the admitted blocks are staged into HBM before the next step.
+//
+// plan kernel: one workgroup per (request, KV head) updates that pair's slot
+//   table in LDS (the whole state is a few hundred integers) and emits the
+//   copy plan and the next attention table.  Admitted blocks go to slots that
+//   were free before this step, never to a slot evicted in this step, so the
+//   attention that still reads the previous table is not raced; with
+//   S >= K_b + C slots there are always enough of them.
+// gather kernel: one workgroup per admitted block copies its 8 KiB from the
+//   pinned host pool, read through the pool's device mapping over PCIe, into
+//   its slot; many workgroups keep many PCIe reads in flight.
+#include "oasis_internal.h"
+
+namespace oasis {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ int wg_exclusive_scan(int v, int *tmp, int *total) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) tmp[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        const int t = tmp[w];
+        before += (w < wave) ? t : 0;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - v;
+}
+
+// Compact the indices i in [0, n) with flag(i) into out[] in ascending order;
+// returns the count.  Thread t owns the contiguous range [t*per, t*per + per).
+template <class F>
+__device__ int wg_compact(int n, F flag, int *out, int *tmp) {
+    const int per = (n + kThreads - 1) / kThreads;
+    const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+    int c = 0;
+    for (int i = lo; i < hi; i++) c += flag(i) ? 1 : 0;
+    int total;
+    int pos = wg_exclusive_scan(c, tmp, &total);
+    for (int i = lo; i < hi; i++)
+        if (flag(i)) out[pos++] = i;
+    __syncthreads();
+    return total;
+}
+
+struct PlanArgs {
+    const int32_t *sel;
+    const int32_t *n_sel;
+    int K_sel;
+    const float *scores;
+    int K_b, C, S, step;
+    int32_t *slot_block;
+    int32_t *slot_stamp;
+    const int32_t *ctx_len;
+    int32_t *tbl_slot;
+    int32_t *tbl_block;
+    int32_t *tbl_n;
+    int32_t *plan;
+    int H_kv, NB_max;
+};
+
+__global__ __launch_bounds__(kThreads) void stage_plan_kernel(PlanArgs a) {
+    extern __shared__ int smem[];
+    const int S = a.S, K = a.K_sel;
+    int *sb = smem;              // [S] block held by each slot (-1 free)
+    int *st = sb + S;            // [S] stamp of each slot
+    int *in_p = st + S;          // [S] 1 if the slot's block is predicted
+    int *victim = in_p + S;      // [S] 1 if evicted this step
+    int *list_s = victim + S;    // [S] scratch list over slots
+    int *pv = list_s + S;        // [K] valid predicted ids, ascending
+    int *res_of = pv + K;        // [K] slot holding pv[k], -1 if not resident
+    int *cand = res_of + K;      // [K] indices k of non-resident predicted blocks
+    uint32_t *ckey = (uint32_t *)(cand + K);  // [K] rank keys of the candidates
+    int *adm = (int *)(ckey + K);            // [K] admitted block per admission rank
+    __shared__ int tmp[kWaves];
+
+    const int rh = blockIdx.x;
+    const int r = rh / a.H_kv;
+    const int tid = threadIdx.x;
+    const int nb = n_blocks_of(a.ctx_len[r], a.NB_max);
+    const int32_t *P = a.sel + (size_t)rh * K;
+    int np = a.n_sel[rh];
+    np = np < 0 ? 0 : (np > K ? K : np);
+    int32_t *slot_block = a.slot_block + (size_t)rh * S;
+    int32_t *slot_stamp = a.slot_stamp + (size_t)rh * S;
+    const float *sc = a.scores + (size_t)rh * a.NB_max;
+
+    // 1. predicted ids: keep those in range and strictly ascending (rows from
+    //    top-K are), compacted into pv in order
+    int npv;
+    {
+        const int per = (np + kThreads - 1) / kThreads;
+        const int lo = min(np, tid * per), hi = min(np, lo + per);
+        int c = 0;
+        for (int i = lo; i < hi; i++) {
+            const int p = P[i];
+            c += (p >= 0 && p < nb && (i == 0 || p > P[i - 1])) ? 1 : 0;
+        }
+        int pos = wg_exclusive_scan(c, tmp, &npv);
+        for (int i = lo; i < hi; i++) {
+            const int p = P[i];
+            if (p >= 0 && p < nb && (i == 0 || p > P[i - 1])) pv[pos++] = p;
+        }
+    }
+    for (int k = tid; k < npv; k += kThreads) res_of[k] = -1;
+    // 2. slot table; anything outside [0, nb) counts as free
+    for (int s = tid; s < S; s += kThreads) {
+        int b = slot_block[s];
+        if (b < 0 || b >= nb) b = -1;
+        sb[s] = b;
+        st[s] = b >= 0 ? slot_stamp[s] : -1;
+        in_p[s] = 0;
+        victim[s] = 0;
+    }
+    __syncthreads();
+    // 3. resident predicted blocks: binary search of each held block in pv
+    for (int s = tid; s < S; s += kThreads) {
+        const int b = sb[s];
+        if (b < 0) continue;
+        int lo = 0, hi = npv;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (pv[mid] < b) lo = mid + 1; else hi = mid;
+        }
+        if (lo < npv && pv[lo] == b) {
+            in_p[s] = 1;
+            res_of[lo] = s;
+            st[s] = a.step;
+        }
+    }
+    __syncthreads();
+    // 4. candidates for admission, counts
+    const int nc = wg_compact(npv, [&](int k) { return res_of[k] < 0; }, cand, tmp);
+    for (int i = tid; i < nc; i += kThreads) ckey[i] = rank_key(sc[pv[cand[i]]]);
+    int n_res, n_elig;
+    {
+        int c1 = 0, c2 = 0;
+        for (int s = tid; s < S; s += kThreads) {
+            c1 += sb[s] >= 0;
+            c2 += sb[s] >= 0 && !in_p[s];
+        }
+        int t;
+        wg_exclusive_scan(c1, tmp, &n_res);
+        wg_exclusive_scan(c2, tmp, &t);
+        n_elig = t;
+    }
+    // free slots before this step's evictions, ascending
+    const int nfree = wg_compact(S, [&](int s) { return sb[s] < 0; }, list_s, tmp);
+    const int free_cap = max(0, a.K_b - n_res);
+    int n_adm = min(a.C, nc);
+    n_adm = min(n_adm, nfree);
+    n_adm = min(n_adm, free_cap + n_elig);
+    n_adm = max(n_adm, 0);
+    const int need = max(0, n_adm - free_cap);
+
+    // 5. admission ranks: (score desc, id asc) among candidates
+    for (int i = tid; i < nc; i += kThreads) {
+        const uint32_t ki = ckey[i];
+        const int bi = pv[cand[i]];
+        int rank = 0;
+        for (int j = 0; j < nc; j++) {
+            const uint32_t kj = ckey[j];
+            rank += (kj > ki) || (kj == ki && pv[cand[j]] < bi);
+        }
+        if (rank < n_adm) adm[rank] = bi;
+    }
+    // 6. eviction ranks: (stamp asc, id asc) among resident, non-predicted
+    for (int s = tid; s < S; s += kThreads) {
+        const int b = sb[s];
+        if (b < 0 || in_p[s]) continue;
+        const int ts = st[s];
+        int rank = 0;
+        for (int u = 0; u < S; u++) {
+            const int bu = sb[u];
+            if (bu < 0 || in_p[u]) continue;
+            rank += (st[u] < ts) || (st[u] == ts && bu < b);
+        }
+        victim[s] = rank < need;
+    }
+    __syncthreads();
+    // 7. apply: evict, then place admits into the pre-step free slots
+    int32_t *plan = a.plan + (size_t)rh * plan_row(a.C);
+    for (int s = tid; s < S; s += kThreads) {
+        if (victim[s]) {
+            sb[s] = -1;
+            st[s] = -1;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < n_adm; i += kThreads) {
+        const int s = list_s[i];
+        sb[s] = adm[i];
+        st[s] = a.step;
+        plan[2 + 2 * i] = s;
+        plan[3 + 2 * i] = adm[i];
+    }
+    if (tid == 0) {
+        plan[0] = n_adm;
+        plan[1] = need;
+    }
+    __syncthreads();
+    for (int s = tid; s < S; s += kThreads) {
+        slot_block[s] = sb[s];
+        slot_stamp[s] = st[s];
+    }
+    // 8. next attention table: held slots, ascending
+    const int nheld = wg_compact(S, [&](int s) { return sb[s] >= 0; }, list_s, tmp);
+    const int nt = min(nheld, a.K_b);
+    int32_t *ts = a.tbl_slot + (size_t)rh * a.K_b;
+    int32_t *tb = a.tbl_block + (size_t)rh * a.K_b;
+    for (int i = tid; i < a.K_b; i += kThreads) {
+        ts[i] = i < nt ? list_s[i] : -1;
+        tb[i] = i < nt ? sb[list_s[i]] : -1;
+    }
+    if (tid == 0) a.tbl_n[rh] = nt;
+}
+
+__global__ __launch_bounds__(256) void stage_gather_kernel(
+    const int32_t *__restrict__ plan, int row, const uint4 *__restrict__ host_pool,
+    uint4 *__restrict__ ws_pool, int NB_max, int S) {
+    const int rh = blockIdx.x;
+    const int i = blockIdx.y;
+    const int32_t *p = plan + (size_t)rh * row;
+    if (i >= p[0]) return;
+    const int slot = p[2 + 2 * i], blk = p[3 + 2 * i];
+    if (slot < 0 || slot >= S || blk < 0 || blk >= NB_max) return;
+    constexpr int kVec = (int)(kBlockBytes / sizeof(uint4));  // 512
+    const uint4 *src = host_pool + ((size_t)rh * NB_max + blk) * kVec;
+    uint4 *dst = ws_pool + ((size_t)rh * S + slot) * kVec;
+    const uint4 a = src[threadIdx.x];
+    const uint4 b = src[threadIdx.x + 256];
+    dst[threadIdx.x] = a;
+    dst[threadIdx.x + 256] = b;
+}
+
+}  // namespace
+
+size_t stage_plan_lds_bytes(int S, int K_sel) {
+    return (size_t)(5 * S + 5 * K_sel) * sizeof(int);
+}
+
+hipError_t launch_stage_plan(const oasis_dims &d, const oasis_stage_args &a, hipStream_t s) {
+    PlanArgs p;
+    p.sel = a.sel;
+    p.n_sel = a.n_sel;
+    p.K_sel = a.K_sel;
+    p.scores = a.scores;
+    p.K_b = a.K_b;
+    p.C = a.C;
+    p.S = a.S;
+    p.step = a.step;
+    p.slot_block = a.slot_block;
+    p.slot_stamp = a.slot_stamp;
+    p.ctx_len = a.ctx_len;
+    p.tbl_slot = a.tbl_slot;
+    p.tbl_block = a.tbl_block;
+    p.tbl_n = a.tbl_n;
+    p.plan = a.plan;
+    p.H_kv = d.H_kv;
+    p.NB_max = d.NB_max;
+    hipLaunchKernelGGL(stage_plan_kernel, dim3((unsigned)(d.B * d.H_kv)), dim3(kThreads),
+                       stage_plan_lds_bytes(a.S, a.K_sel), s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage_gather(const oasis_dims &d, const oasis_stage_args &a,
+                               const void *host_pool_dev, hipStream_t s) {
+    if (a.C <= 0) return hipSuccess;
+    dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)a.C);
+    hipLaunchKernelGGL(stage_gather_kernel, grid, dim3(256), 0, s, a.plan, plan_row(a.C),
+                       reinterpret_cast<const uint4 *>(host_pool_dev),
+                       reinterpret_cast<uint4 *>(a.ws_pool), d.NB_max, a.S);
+    return hipGetLastError();
+}
+
+}  // namespace oasis

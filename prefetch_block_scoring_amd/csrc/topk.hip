@@ -1,0 +1,138 @@
+// Top-K block selection under the token budget.
+//
+// OasisKV (arXiv 2608.08097), paperlayer summary, sections 4 and 5: per KV
+// head and layer, the best-scoring blocks that fit the KV budget (2048 tokens
+// by default, K_b = budget / bs blocks) are predicted for the next step.
+// Order: fp32 score descending, equal scores by lower block id; ids are
+// written ascending.
+//
+// One workgroup per (request, KV head).  Scores are mapped to order-preserving
+// uint32 keys in LDS; a four-pass radix select (8-bit digits, most significant
+// first) finds the K_b-th largest key T and how many keys equal to T must be
+// taken; a compaction in index order then writes every key > T and the first
+// `need` keys == T, which is exactly the (score desc, id asc) prefix.  All
+// work is integer, so the result is bit-exact.
+#include "oasis_internal.h"
+
+namespace oasis {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// Exclusive scan of one uint32 per thread across the workgroup; returns the
+// exclusive prefix and writes the total to *total.  `tmp` holds kWaves words.
+__device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t *total) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    uint32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) tmp[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        const uint32_t t = tmp[w];
+        before += (w < wave) ? t : 0u;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - v;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ ctx_len, int H_kv,
+    int NB_max, int K_b, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel) {
+    extern __shared__ uint32_t keys[];  // NB_max
+    __shared__ uint32_t hist[kWaves][256];
+    __shared__ uint32_t tmp[kWaves];
+    __shared__ uint32_t s_digit, s_above;
+
+    const int rh = blockIdx.x;
+    const int r = rh / H_kv;
+    const int tid = threadIdx.x;
+    const int wave = tid / 64;
+    const int nb = n_blocks_of(ctx_len[r], NB_max);
+    int32_t *out = sel + (size_t)rh * K_b;
+
+    if (nb <= K_b) {
+        for (int i = tid; i < K_b; i += kThreads) out[i] = i < nb ? i : -1;
+        if (tid == 0) n_sel[rh] = nb;
+        return;
+    }
+
+    const float *row = scores + (size_t)rh * NB_max;
+    for (int b = tid; b < nb; b += kThreads) keys[b] = rank_key(row[b]);
+
+    // ---- radix select of the K_b-th largest key
+    uint32_t prefix = 0, mask = 0;
+    uint32_t k = (uint32_t)K_b;  // rank still to find among keys matching prefix
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
+        __syncthreads();
+        for (int b = tid; b < nb; b += kThreads) {
+            const uint32_t key = keys[b];
+            if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        // thread t looks at digit 255 - t: inclusive suffix count from the top
+        const uint32_t digit = 255u - (uint32_t)tid;
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) c += hist[w][digit];
+        uint32_t total;
+        const uint32_t above = wg_exclusive_scan(c, tmp, &total);  // keys with larger digits
+        if (above < k && above + c >= k) {
+            s_digit = digit;
+            s_above = above;
+        }
+        __syncthreads();
+        prefix |= s_digit << shift;
+        mask |= 255u << shift;
+        k -= s_above;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;  // K_b-th largest key
+    const uint32_t need = k;    // how many keys == T are taken (lowest ids first)
+
+    // ---- compaction in index order: thread t owns a contiguous id range
+    const int per = (nb + kThreads - 1) / kThreads;
+    const int lo = min(nb, tid * per), hi = min(nb, lo + per);
+    uint32_t gt = 0, eq = 0;
+    for (int b = lo; b < hi; b++) {
+        const uint32_t key = keys[b];
+        gt += key > T;
+        eq += key == T;
+    }
+    uint32_t tot;
+    const uint32_t eq_before = wg_exclusive_scan(eq, tmp, &tot);
+    const uint32_t take_eq = need > eq_before ? min(need - eq_before, eq) : 0u;
+    const uint32_t pos0 = wg_exclusive_scan(gt + take_eq, tmp, &tot);
+    uint32_t pos = pos0, eq_seen = 0;
+    for (int b = lo; b < hi; b++) {
+        const uint32_t key = keys[b];
+        bool take = key > T;
+        if (key == T) {
+            take = eq_seen < take_eq;
+            eq_seen++;
+        }
+        if (take && pos < (uint32_t)K_b) out[pos++] = b;
+    }
+    if (tid == 0) n_sel[rh] = K_b;
+}
+
+}  // namespace
+
+hipError_t launch_topk(const oasis_dims &d, const float *scores, const int32_t *ctx_len,
+                       int K_b, int32_t *sel, int32_t *n_sel, hipStream_t s) {
+    const size_t lds = (size_t)d.NB_max * sizeof(uint32_t);
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(d.B * d.H_kv)), dim3(kThreads), lds, s,
+                       scores, ctx_len, d.H_kv, d.NB_max, K_b, sel, n_sel);
+    return hipGetLastError();
+}
+
+}  // namespace oasis

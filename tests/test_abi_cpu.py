@@ -1,0 +1,149 @@
+"""The C ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host (no device work is enqueued, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import prefetch_block_scoring_amd as oa
+from prefetch_block_scoring_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oasis.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(oasis_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in binding._SIGNATURES, n
+
+
+def test_version_and_cap_mapping():
+    assert oa.oasis_version().startswith("oasis")
+    assert oa.oasis_fetch_cap_blocks(0.05, 128) == 6
+    assert oa.oasis_fetch_cap_blocks(0.01, 128) == 1
+    assert oa.oasis_fetch_cap_blocks(1.0, 128) == 128
+    assert oa.oasis_fetch_cap_blocks(0.0, 128) == 0
+    assert oa.oasis_fetch_cap_blocks(float("nan"), 128) == 0
+    assert oa.oasis_fetch_cap_blocks(0.5, 0) == -1
+
+
+def test_fetch_cap_matches_oracle_over_a_sweep():
+    import oracle
+    for K_b in (1, 7, 32, 128, 1000):
+        for cap in (0.0, 1e-6, 0.01, 0.05, 0.1, 0.333, 0.5, 0.99, 1.0, 2.0):
+            assert oa.oasis_fetch_cap_blocks(cap, K_b) == oracle.fetch_cap_blocks(cap, K_b)
+
+
+L = binding.library()
+NULL = None
+
+
+def d(**kw):
+    base = dict(B=2, H_q=8, H_kv=2, D=128, bs=16, NB_max=64)
+    base.update(kw)
+    return binding.oasis_dims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), oa.OASIS_EUNSUPPORTED),
+    (dict(bs=32), oa.OASIS_EUNSUPPORTED),
+    (dict(H_q=6, H_kv=4), oa.OASIS_EINVAL),
+    (dict(H_q=64, H_kv=2), oa.OASIS_EUNSUPPORTED),
+    (dict(NB_max=0), oa.OASIS_EINVAL),
+    (dict(NB_max=1 << 20), oa.OASIS_EUNSUPPORTED),
+    (dict(B=-1), oa.OASIS_EINVAL),
+])
+def test_bad_dims_rejected_by_every_call(kw, code):
+    dd = d(**kw)
+    p = ctypes.c_void_p(16)
+    assert L.oasis_build_summaries(ctypes.byref(dd), p, p, p, NULL) == code
+    assert L.oasis_score_blocks(ctypes.byref(dd), p, 1, p, p, p, NULL) == code
+    assert L.oasis_select_topk(ctypes.byref(dd), p, p, 8, p, p, NULL) == code
+    assert L.oasis_sparse_decode_attn(ctypes.byref(dd), p, p, 4, p, p, p, 4, p, 0.1, p, p, p, 1 << 30, 1,
+                                      NULL) == code
+    assert oa.oasis_last_error() != ""
+
+
+def test_null_pointers_and_bad_values():
+    dd = d()
+    p = ctypes.c_void_p(16)
+    assert L.oasis_score_blocks(None, p, 1, p, p, p, NULL) == oa.OASIS_EINVAL
+    assert L.oasis_score_blocks(ctypes.byref(dd), NULL, 1, p, p, p, NULL) == oa.OASIS_EINVAL
+    assert "q_look" in oa.oasis_last_error()
+    assert L.oasis_score_blocks(ctypes.byref(dd), p, 0, p, p, p, NULL) == oa.OASIS_EINVAL
+    assert L.oasis_select_topk(ctypes.byref(dd), p, p, 0, p, p, NULL) == oa.OASIS_EINVAL
+    assert L.oasis_select_topk(ctypes.byref(dd), p, NULL, 4, p, p, NULL) == oa.OASIS_EINVAL
+    assert L.oasis_build_summaries(ctypes.byref(dd), p, p, NULL, NULL) == oa.OASIS_EINVAL
+    # attention: P < 1, T < 0, n_split out of range, NaN scale, missing table
+    att = L.oasis_sparse_decode_attn
+    assert att(ctypes.byref(dd), p, p, 0, p, p, p, 4, p, 0.1, p, p, p, 0, 1, NULL) == oa.OASIS_EINVAL
+    assert att(ctypes.byref(dd), p, p, 4, p, p, p, -1, p, 0.1, p, p, p, 0, 1, NULL) == oa.OASIS_EINVAL
+    assert att(ctypes.byref(dd), p, p, 4, p, p, p, 4, p, 0.1, p, p, p, 0, 65, NULL) == oa.OASIS_EINVAL
+    assert att(ctypes.byref(dd), p, p, 4, p, p, p, 4, p, float("nan"), p, p, p, 0, 1, NULL) == oa.OASIS_EINVAL
+    assert att(ctypes.byref(dd), p, p, 4, NULL, p, p, 4, p, 0.1, p, p, p, 0, 1, NULL) == oa.OASIS_EINVAL
+    # workspace too small for an explicit split
+    need = L.oasis_attn_workspace_bytes(ctypes.byref(dd), 64, 4)
+    assert need == 2 * 8 * 4 * 130 * 4
+    assert att(ctypes.byref(dd), p, p, 64, p, p, p, 64, p, 0.1, p, p, p, need - 4, 4, NULL) == oa.OASIS_ENOSPACE
+    assert att(ctypes.byref(dd), p, p, 64, p, p, p, 64, p, 0.1, p, p, NULL, need, 4, NULL) == oa.OASIS_EINVAL
+
+
+def test_empty_batch_is_a_no_op():
+    dd = d(B=0)
+    assert L.oasis_score_blocks(ctypes.byref(dd), NULL, 1, NULL, NULL, NULL, NULL) == oa.OASIS_OK
+    assert L.oasis_select_topk(ctypes.byref(dd), NULL, NULL, 4, NULL, NULL, NULL) == oa.OASIS_OK
+    assert L.oasis_sparse_decode_attn(ctypes.byref(dd), NULL, NULL, 4, NULL, NULL, NULL, 4, NULL, 0.1,
+                                      NULL, NULL, NULL, 0, 1, NULL) == oa.OASIS_OK
+
+
+def stage_args(**kw):
+    a = binding.oasis_stage_args()
+    p = 16
+    for f in ("sel", "n_sel", "scores", "slot_block", "slot_stamp", "ctx_len", "host_pool", "ws_pool",
+              "tbl_slot", "tbl_block", "tbl_n", "plan"):
+        setattr(a, f, p)
+    a.K_sel, a.K_b, a.C, a.S, a.step = 8, 8, 2, 10, 0
+    a.plan_bytes = 1 << 20
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(C=-1), oa.OASIS_EINVAL),
+    (dict(C=9), oa.OASIS_EINVAL),
+    (dict(S=7), oa.OASIS_EINVAL),
+    (dict(K_b=0), oa.OASIS_EINVAL),
+    (dict(step=-1), oa.OASIS_EINVAL),
+    (dict(copy_mode=7), oa.OASIS_EINVAL),
+    (dict(S=5000), oa.OASIS_EUNSUPPORTED),
+    (dict(K_sel=2000), oa.OASIS_EUNSUPPORTED),
+    (dict(plan=None), oa.OASIS_EINVAL),
+    (dict(host_pool=None), oa.OASIS_EINVAL),
+    (dict(plan_bytes=4), oa.OASIS_ENOSPACE),
+    (dict(copy_mode=1, host_plan=None), oa.OASIS_EINVAL),
+    (dict(copy_mode=1, host_plan=16, host_plan_bytes=8), oa.OASIS_ENOSPACE),
+])
+def test_stage_argument_errors(kw, code):
+    dd = d()
+    a = stage_args(**kw)
+    assert L.oasis_stage_blocks(ctypes.byref(dd), ctypes.byref(a)) == code
+    assert oa.oasis_last_error() != ""
+
+
+def test_plan_sizes():
+    dd = d(B=3, H_kv=2)
+    assert L.oasis_stage_plan_bytes(ctypes.byref(dd), 6) == 4 * 3 * 2 * (2 + 12)
+    assert L.oasis_stage_plan_bytes(ctypes.byref(dd), 0) == 4 * 3 * 2 * 4
+    assert L.oasis_stage_host_plan_bytes(ctypes.byref(dd), 6) == 4 * 3 * 2 * (2 + 12)

@@ -1,0 +1,375 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Both sides receive the same seeded inputs from `workloads`; nothing the GPU
+computes is fed to the oracle.  Bars: integer work (summaries, selections on
+shared scores, staging state, copied bytes) bit-exact; scores within one fp32
+ulp (both round an fp64 sum of exact products); selections on each side's own
+scores equal except for swaps between blocks tied within 1e-6 relative;
+attention |out - ref| <= 2e-3 + 1e-2 |ref| against the fp64 oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from helpers import (assert_attn_close, assert_scores_close, assert_selection_matches,
+                     bf16_to_f64, n_blocks, u16)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def oa():
+    import prefetch_block_scoring_amd as m
+    return m
+
+
+def small_workloads():
+    W = wl.WORKLOADS
+    return [
+        W["parity_8q2kv_4k"],
+        W["qwen3_8b_16k_b32_hbm"].shrink(B=2),
+        W["reasoning_32k_b64_j4"].shrink(B=2, ctx=8192 + 5),
+        W["gqa32b_ragged_b16_staged"].shrink(B=3, ctx=(100, 5000), cap=None),
+        wl.Workload("odd_g3_ragged", B=4, H_q=12, H_kv=4, ctx=(1, 700), budget=160, J=2,
+                    structure="none", seed=77),
+        wl.Workload("g1_g16", B=2, H_q=16, H_kv=1, ctx=(17, 300), budget=64, J=1,
+                    structure="none", seed=78),
+    ]
+
+
+IDS = [w.name for w in small_workloads()]
+
+
+class Inputs:
+    def __init__(self, w):
+        self.w = w
+        self.ctx_cpu = wl.context_lengths(w)
+        self.kv_cpu = wl.kv_pool(w)
+        self.ql_cpu = wl.lookahead(w, 0)
+        self.q_cpu = wl.attention_query(w, 1)
+        self.ctx = self.ctx_cpu.to(DEV)
+        self.kv = self.kv_cpu.to(DEV)
+        self.ql = self.ql_cpu.to(DEV)
+        self.q = self.q_cpu.to(DEV)
+        self.ctx_np = self.ctx_cpu.numpy()
+        self.kv_np = u16(self.kv_cpu)
+        self.ql_np = u16(self.ql_cpu)
+        self.q_np = u16(self.q_cpu)
+
+
+_cache = {}
+
+
+def inputs(w):
+    if w.name not in _cache:
+        _cache[w.name] = Inputs(w)
+    return _cache[w.name]
+
+
+# ---------------------------------------------------------------- summaries / scores
+
+
+@pytest.mark.parametrize("w", small_workloads(), ids=IDS)
+def test_summaries_bit_exact(w):
+    x = inputs(w)
+    got = u16(oa().oasis_build_summaries(x.kv, x.ctx))
+    ref = oracle.build_summaries(x.kv_np, x.ctx_np, w.bs)
+    for r in range(w.B):
+        nb = n_blocks(x.ctx_np[r])
+        np.testing.assert_array_equal(bf16_to_f64(got[r, :, :nb]), bf16_to_f64(ref[r, :, :nb]))
+
+
+@pytest.mark.parametrize("w", small_workloads(), ids=IDS)
+def test_scores_within_one_ulp(w):
+    x = inputs(w)
+    summ = oa().oasis_build_summaries(x.kv, x.ctx)
+    got = oa().oasis_score_blocks(x.ql, summ, x.ctx).cpu().numpy()
+    ref = oracle.score(x.ql_np, oracle.build_summaries(x.kv_np, x.ctx_np, w.bs), x.ctx_np, w.bs, w.H_kv)
+    assert_scores_close(got, ref, x.ctx_np)
+
+
+def test_scores_from_host_pool_summaries():
+    """Summaries built straight from a pinned host pool match the oracle."""
+    w = small_workloads()[0]
+    x = inputs(w)
+    host = x.kv_cpu.pin_memory()
+    got = u16(oa().oasis_build_summaries(host, x.ctx))
+    ref = oracle.build_summaries(x.kv_np, x.ctx_np, w.bs)
+    np.testing.assert_array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- selection
+
+
+@pytest.mark.parametrize("ties", [0, 2, 50])
+@pytest.mark.parametrize("w", small_workloads(), ids=IDS)
+def test_select_bit_exact_on_shared_scores(w, ties):
+    x = inputs(w)
+    sc = wl.random_scores(w, tie_levels=ties)
+    sel, n = oa().oasis_select_topk(sc.to(DEV), x.ctx, w.K_b)
+    rsel, rn = oracle.select(sc.numpy(), x.ctx_np, w.bs, w.K_b)
+    np.testing.assert_array_equal(n.cpu().numpy(), rn)
+    np.testing.assert_array_equal(sel.cpu().numpy(), rsel)
+
+
+def test_select_special_values():
+    """NaN below -inf, -0 equal to +0 (ties by id), short rows take all."""
+    w = wl.Workload("sv", B=2, H_q=2, H_kv=2, ctx=(40, 40), budget=32, structure="none")
+    sc = torch.tensor([[[float("nan"), float("-inf"), 1.0], [-0.0, 0.0, -1.0]],
+                       [[2.0, float("nan"), float("nan")], [float("inf"), -2.0, float("inf")]]])
+    ctx = torch.tensor([40, 40], dtype=torch.int32)
+    sel, n = oa().oasis_select_topk(sc.to(DEV), ctx.to(DEV), 2)
+    rsel, rn = oracle.select(sc.numpy(), ctx.numpy(), 16, 2)
+    np.testing.assert_array_equal(sel.cpu().numpy(), rsel)
+    assert rsel.tolist() == [[[1, 2], [0, 1]], [[0, 1], [0, 2]]]
+
+
+@pytest.mark.parametrize("w", small_workloads(), ids=IDS)
+def test_selection_chain_matches_oracle(w):
+    x = inputs(w)
+    summ = oa().oasis_build_summaries(x.kv, x.ctx)
+    sc = oa().oasis_score_blocks(x.ql, summ, x.ctx)
+    sel, n = oa().oasis_select_topk(sc, x.ctx, w.K_b)
+    rsc = oracle.score(x.ql_np, oracle.build_summaries(x.kv_np, x.ctx_np, w.bs), x.ctx_np, w.bs, w.H_kv)
+    rsel, rn = oracle.select(rsc, x.ctx_np, w.bs, w.K_b)
+    assert_selection_matches(sel.cpu().numpy(), n.cpu().numpy(), rsel, rn, rsc)
+    if w.structure == "planted" and w.planted:
+        s = sel.cpu().numpy()
+        for r, heads in enumerate(wl.planted_blocks(w)):
+            for h, planted in enumerate(heads):
+                assert set(planted) <= set(s[r, h].tolist())
+
+
+# ---------------------------------------------------------------- attention
+
+
+def attn_ref(x, tbl, n, sm):
+    return oracle.attend(x.q_np, x.kv_np, x.ctx_np, tbl, n, sm)
+
+
+@pytest.mark.parametrize("n_split", [0, 1, 3])
+@pytest.mark.parametrize("T", [1, 7, 128])
+@pytest.mark.parametrize("w", small_workloads(), ids=IDS)
+def test_attention_full_pool(w, T, n_split):
+    x = inputs(w)
+    tbl, n = wl.random_table(w, T, seed_index=T)
+    sm = 1.0 / math.sqrt(w.D)
+    out, lse = oa().oasis_sparse_decode_attn(x.q, x.kv, tbl.to(DEV), tbl.to(DEV), n.to(DEV), x.ctx,
+                                             sm_scale=sm, n_split=n_split, want_lse=True)
+    ref, ref_lse = attn_ref(x, tbl.numpy(), n.numpy(), sm)
+    assert_attn_close(bf16_to_f64(u16(out)), ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-4)
+
+
+def test_attention_working_set_slots_and_invalid_entries():
+    """Blocks placed at shuffled slots of a smaller pool; entries with an
+    out-of-range slot or block id are skipped; an empty row gives zeros."""
+    w = small_workloads()[3]
+    x = inputs(w)
+    T = 40
+    tbl, n = wl.random_table(w, T, seed_index=5)
+    S = T + 3
+    g = torch.Generator().manual_seed(9)
+    ws = torch.zeros((w.B, w.H_kv, S, 2, w.bs, w.D), dtype=torch.bfloat16)
+    slots = torch.full_like(tbl, -1)
+    for r in range(w.B):
+        for h in range(w.H_kv):
+            perm = torch.randperm(S, generator=g)
+            for i in range(int(n[r, h])):
+                ws[r, h, perm[i]] = x.kv_cpu[r, h, tbl[r, h, i]]
+                slots[r, h, i] = perm[i]
+    ref_tbl = tbl.clone()
+    # corrupt entries: these must be skipped by the kernel and are dropped from the reference
+    bad_tbl, bad_slots, ref_n = tbl.clone(), slots.clone(), n.clone()
+    bad_slots[0, 0, 0] = S + 5            # slot out of range
+    bad_tbl[0, 1, 1] = 10 ** 6            # block out of range
+    ref_tbl[0, 0, 0] = -1
+    ref_tbl[0, 1, 1] = -1
+    n_zero = n.clone()
+    n_zero[1, 0] = 0                      # empty row
+    ref_n = n_zero
+    sm = 0.05
+    out, lse = oa().oasis_sparse_decode_attn(x.q, ws.to(DEV), bad_slots.to(DEV), bad_tbl.to(DEV),
+                                             n_zero.to(DEV), x.ctx, sm_scale=sm, want_lse=True)
+    ref, ref_lse = attn_ref(x, ref_tbl.numpy(), ref_n.numpy(), sm)
+    assert_attn_close(bf16_to_f64(u16(out)), ref)
+    o = out.cpu()
+    G = w.G
+    assert torch.all(o[1, 0:G] == 0)
+    assert torch.all(torch.isneginf(lse.cpu()[1, 0:G]))
+
+
+def test_attention_budget_equal_to_context_is_dense():
+    """Listing every block reproduces dense softmax attention (the oracle's
+    dense case is pinned against NumPy in the CPU suite)."""
+    w = small_workloads()[4]
+    x = inputs(w)
+    T = w.NB_max
+    tbl = torch.full((w.B, w.H_kv, T), -1, dtype=torch.int32)
+    n = torch.zeros((w.B, w.H_kv), dtype=torch.int32)
+    for r in range(w.B):
+        nb = n_blocks(x.ctx_np[r])
+        tbl[r, :, :nb] = torch.arange(nb, dtype=torch.int32)
+        n[r] = nb
+    sm = 1 / math.sqrt(128)
+    out = oa().oasis_sparse_decode_attn(x.q, x.kv, tbl.to(DEV), tbl.to(DEV), n.to(DEV), x.ctx, sm_scale=sm)
+    ref, _ = attn_ref(x, tbl.numpy(), n.numpy(), sm)
+    assert_attn_close(bf16_to_f64(u16(out)), ref)
+
+
+# ---------------------------------------------------------------- staging
+
+
+def gpu_stage_state(slot_block, slot_stamp, NB):
+    sb = slot_block.cpu().numpy()
+    st = slot_stamp.cpu().numpy()
+    B, H, S = sb.shape
+    stamp = np.full((B, H, NB), -1, dtype=np.int32)
+    for r in range(B):
+        for h in range(H):
+            held = sb[r, h][sb[r, h] >= 0]
+            assert len(set(held.tolist())) == len(held), "a block is held by two slots"
+            for s in range(S):
+                if sb[r, h, s] >= 0:
+                    stamp[r, h, sb[r, h, s]] = st[r, h, s]
+    return stamp
+
+
+@pytest.mark.parametrize("copy_mode", [0, 1])
+@pytest.mark.parametrize("C,turnover", [(1, 3), (6, 5), (6, 30)])
+def test_stage_matches_oracle(copy_mode, C, turnover):
+    w = wl.Workload("stage", B=3, H_q=8, H_kv=2, ctx=(1500, 3000), budget=512, J=1,
+                    structure="none", seed=31)
+    K_b, NB, steps = w.K_b, w.NB_max, 6
+    S = K_b + C
+    ctx_cpu = wl.context_lengths(w)
+    host = wl.kv_pool(w).pin_memory()
+    host_np = u16(host)
+    sels, nsels, scores = wl.predicted_set_sequence(w, steps, turnover)
+    dev = lambda t: t.to(DEV)
+    slot_block = torch.full((w.B, w.H_kv, S), -1, dtype=torch.int32, device=DEV)
+    slot_stamp = torch.full((w.B, w.H_kv, S), -1, dtype=torch.int32, device=DEV)
+    ws = torch.zeros((w.B, w.H_kv, S, 2, w.bs, w.D), dtype=torch.bfloat16, device=DEV)
+    tbl_slot = torch.empty((w.B, w.H_kv, K_b), dtype=torch.int32, device=DEV)
+    tbl_block = torch.empty_like(tbl_slot)
+    tbl_n = torch.empty((w.B, w.H_kv), dtype=torch.int32, device=DEV)
+    nbytes = oa().oasis_stage_plan_bytes(w.B, w.H_kv, K_b)
+    plan = torch.empty(nbytes // 4, dtype=torch.int32, device=DEV)
+    host_plan = torch.empty(nbytes // 4, dtype=torch.int32).pin_memory()
+    ctx = dev(ctx_cpu)
+    st = oracle.StageState(w.B, w.H_kv, NB)
+    for s in range(steps):
+        Cs = K_b if s == 0 else C
+        oa().oasis_stage_blocks(sel=dev(sels[s]), n_sel=dev(nsels[s]), scores=dev(scores[s]), ctx_len=ctx,
+                                K_b=K_b, C=Cs, step=s, slot_block=slot_block, slot_stamp=slot_stamp,
+                                host_pool=host, ws_pool=ws, tbl_slot=tbl_slot, tbl_block=tbl_block,
+                                tbl_n=tbl_n, plan=plan, host_plan=host_plan, copy_mode=copy_mode)
+        torch.cuda.synchronize()
+        adm, na, ev, ne = oracle.stage(st, sels[s].numpy(), nsels[s].numpy(), scores[s].numpy(),
+                                       ctx_cpu.numpy(), w.bs, K_b, Cs, s)
+        got = gpu_stage_state(slot_block, slot_stamp, NB)
+        np.testing.assert_array_equal(got, st.stamp, err_msg=f"step {s}")
+        p = plan.cpu().numpy()[: w.B * w.H_kv * (2 + 2 * Cs)].reshape(w.B, w.H_kv, 2 + 2 * Cs)
+        np.testing.assert_array_equal(p[:, :, 0], na)
+        np.testing.assert_array_equal(p[:, :, 1], ne)
+        for r in range(w.B):
+            for h in range(w.H_kv):
+                k = int(na[r, h])
+                assert p[r, h, 3:3 + 2 * k:2].tolist() == adm[r, h, :k].tolist()
+        # table lists exactly the held slots; every held slot holds its host block's bytes
+        wsn = u16(ws)
+        sb = slot_block.cpu().numpy()
+        tn, tsl, tbk = tbl_n.cpu().numpy(), tbl_slot.cpu().numpy(), tbl_block.cpu().numpy()
+        for r in range(w.B):
+            for h in range(w.H_kv):
+                held = [i for i in range(S) if sb[r, h, i] >= 0]
+                assert tn[r, h] == len(held)
+                assert tsl[r, h, :len(held)].tolist() == held
+                assert tbk[r, h, :len(held)].tolist() == [int(sb[r, h, i]) for i in held]
+                for i in held:
+                    assert np.array_equal(wsn[r, h, i], host_np[r, h, sb[r, h, i]]), (s, r, h, i)
+
+
+# ---------------------------------------------------------------- whole chain
+
+
+def run_chain_gpu(w, steps, C, copy_mode=0):
+    """score -> select -> stage -> attend for `steps` steps; returns per-step
+    (scores, sel, n_sel, stamps, out) on the CPU."""
+    m = oa()
+    ctx_cpu = wl.context_lengths(w)
+    ctx = ctx_cpu.to(DEV)
+    host = wl.kv_pool(w).pin_memory()
+    summ = m.oasis_build_summaries(host, ctx)
+    K_b, S = w.K_b, w.K_b + C
+    slot_block = torch.full((w.B, w.H_kv, S), -1, dtype=torch.int32, device=DEV)
+    slot_stamp = torch.full_like(slot_block, -1)
+    ws = torch.zeros((w.B, w.H_kv, S, 2, w.bs, w.D), dtype=torch.bfloat16, device=DEV)
+    tabs = [(torch.empty((w.B, w.H_kv, K_b), dtype=torch.int32, device=DEV),
+             torch.empty((w.B, w.H_kv, K_b), dtype=torch.int32, device=DEV),
+             torch.zeros((w.B, w.H_kv), dtype=torch.int32, device=DEV)) for _ in range(2)]
+    plan = torch.empty(m.oasis_stage_plan_bytes(w.B, w.H_kv, K_b) // 4, dtype=torch.int32, device=DEV)
+    host_plan = torch.empty(plan.numel(), dtype=torch.int32).pin_memory()
+    hist = []
+    for s in range(steps):
+        ql = wl.lookahead(w, s).to(DEV)
+        sc = m.oasis_score_blocks(ql, summ, ctx)
+        sel, n = m.oasis_select_topk(sc, ctx, K_b)
+        t = tabs[s % 2]
+        m.oasis_stage_blocks(sel=sel, n_sel=n, scores=sc, ctx_len=ctx, K_b=K_b, C=K_b if s == 0 else C,
+                             step=s, slot_block=slot_block, slot_stamp=slot_stamp, host_pool=host,
+                             ws_pool=ws, tbl_slot=t[0], tbl_block=t[1], tbl_n=t[2], plan=plan,
+                             host_plan=host_plan, copy_mode=copy_mode)
+        q = wl.attention_query(w, s + 1).to(DEV)
+        out = m.oasis_sparse_decode_attn(q, ws, t[0], t[1], t[2], ctx)
+        torch.cuda.synchronize()
+        hist.append((sc.cpu().numpy(), sel.cpu().numpy(), n.cpu().numpy(),
+                     gpu_stage_state(slot_block, slot_stamp, w.NB_max), u16(out)))
+    return hist
+
+
+def run_chain_oracle(w, steps, C):
+    ctx = wl.context_lengths(w).numpy()
+    kv = u16(wl.kv_pool(w))
+    summ = oracle.build_summaries(kv, ctx, w.bs)
+    st = oracle.StageState(w.B, w.H_kv, w.NB_max)
+    hist = []
+    for s in range(steps):
+        sc = oracle.score(u16(wl.lookahead(w, s)), summ, ctx, w.bs, w.H_kv)
+        sel, n = oracle.select(sc, ctx, w.bs, w.K_b)
+        oracle.stage(st, sel, n, sc, ctx, w.bs, w.K_b, w.K_b if s == 0 else C, s)
+        blocks = np.full((w.B, w.H_kv, w.K_b), -1, dtype=np.int32)
+        nblk = np.zeros((w.B, w.H_kv), dtype=np.int32)
+        for r in range(w.B):
+            for h in range(w.H_kv):
+                res = st.resident(r, h)
+                blocks[r, h, :len(res)] = res
+                nblk[r, h] = len(res)
+        out, _ = oracle.attend(u16(wl.attention_query(w, s + 1)), kv, ctx, blocks, nblk, 1 / math.sqrt(w.D))
+        hist.append((sc, sel, n, st.stamp.copy(), out))
+    return hist
+
+
+@pytest.mark.parametrize("name,B,ctx", [("qwen3_8b_16k_b128_staged", 2, 16384),
+                                        ("gqa32b_ragged_b16_staged", 2, (3000, 9000))])
+@pytest.mark.parametrize("copy_mode", [0, 1])
+def test_chain_end_to_end(name, B, ctx, copy_mode):
+    w = wl.WORKLOADS[name].shrink(B=B, ctx=ctx)
+    C = oracle.fetch_cap_blocks(w.cap, w.K_b)
+    steps = 5
+    g = run_chain_gpu(w, steps, C, copy_mode)
+    o = run_chain_oracle(w, steps, C)
+    ctx_np = wl.context_lengths(w).numpy()
+    for s in range(steps):
+        gs, gsel, gn, gst, gout = g[s]
+        os_, osel, on, ost, oout = o[s]
+        assert_scores_close(gs, os_, ctx_np)
+        assert_selection_matches(gsel, gn, osel, on, os_)
+        if np.array_equal(gsel, osel):
+            np.testing.assert_array_equal(gst, ost, err_msg=f"step {s}")
+            assert_attn_close(bf16_to_f64(gout), oout)
