@@ -171,7 +171,9 @@ int oasis_select_topk(const oasis_dims *dims, const float *scores,
  * plan kernel has finished, then enqueues one hipMemcpyAsync per admitted
  * block (adjacent blocks into adjacent slots are merged) on copy_stream.
  *
- * Calls that overlap on the same slot table race; keep them ordered. */
+ * The copies read the plan workspace after the call returns: the next
+ * step must use another plan buffer, or wait for `done_event` first.  Calls
+ * that overlap on the same slot table race; keep them ordered. */
 typedef struct oasis_stage_args {
     const int32_t *sel;     /* [B][H_kv][K_sel] device, ascending, -1 padded */
     const int32_t *n_sel;   /* [B][H_kv] device */

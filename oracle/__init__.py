@@ -40,6 +40,8 @@ def lib():
         L.oracle_fetch_cap_blocks.restype = I
         L.oracle_stage.argtypes = [I, I, I, I, P, P, P, I, P, I, I, I, P, P, P, P, P]
         L.oracle_attend.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, ctypes.c_double, P, P]
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = I
         for f in (L.oracle_build_summaries, L.oracle_score, L.oracle_select, L.oracle_stage,
                   L.oracle_attend):
             f.restype = None
@@ -59,6 +61,11 @@ def _c(a, dtype):
 
 def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(lib().oracle_num_threads())
 
 
 def build_summaries(kv, ctx_len, bs: int):

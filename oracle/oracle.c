@@ -375,3 +375,16 @@ void oracle_attend(int B, int H_q, int H_kv, int D, int NB_max, int bs,
         }
     }
 }
+
+/* Number of threads the OpenMP loops above use (for reporting). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
