@@ -1,24 +1,31 @@
 #!/usr/bin/env python3
 """Decode-layer benchmark of the lookahead block-scoring path on one MI355X.
 
-One step = one decode layer-step of the whole path over the batch: block
-scores from the lookahead queries, top-K under the KV budget, staging of the
-newly selected blocks (fetch-capped, from the pinned host pool into the HBM
-working set) and sparse GQA decode attention over the working set.  Staging of
-step s overlaps the attention of step s; the attention of step s + 1 waits only
-for that staging (the per-layer ordering of the OasisKV pages, arXiv
-2608.08097, paperlayer summary, section 4).
+One layer-step = one pass of the whole path over the batch for one layer:
+block scores from that layer's lookahead queries, top-K under the KV budget,
+staging of the newly selected blocks (fetch-capped, from the pinned host pool
+into the layer's HBM working set) and sparse GQA decode attention over the
+working set.  The OasisKV pages (arXiv 2608.08097, paperlayer summary,
+section 4) run the per-layer chain on background workers overlapped across
+layers and decode steps; the foreground waits only for the relevant layer's
+transfer before that layer's next-step attention.  The benchmark does the
+same with `--layers` layers in flight (default 4): each decode step runs the
+layers in order; a layer's staging overlaps the other layers' work and its
+attention at the next step waits only on its own staging.
 
-The default workload is the Qwen3-8B-shaped layer (32 query / 8 KV heads,
-head dim 128, 16-token blocks) at batch 128 and 16K context, 2048-token budget,
-fetch cap 0.05, K/V pool in pinned host memory.  Inputs are seeded synthetic
-data (workloads.py), generated on the GPU and resident before timing.
+Workload (default): the Qwen3-8B-shaped layer (32 query / 8 KV heads, head dim
+128, 16-token blocks) at batch 128 and 16K context, 2048-token budget, fetch
+cap 0.05, K/V pool in pinned host memory (one pool shared read-only by the
+layers, each layer with its own working set, slot table and lookahead phase).
+Inputs are seeded synthetic data (workloads.py), generated on the GPU and
+resident before timing.
 
 Prints one JSON line: tokens/s per layer-step (whole job), the attention
 kernel's HBM roofline (algorithmic bytes / measured launch time), the staging
 traffic against the PCIe link, and the CPU oracle timed on the host cores.
 """
 import argparse
+import concurrent.futures
 import json
 import math
 import os
@@ -37,12 +44,12 @@ PCIE_PEAK_GBS = 64.0         # PCIe Gen5 x16, nominal per direction
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=64)
+    p.add_argument("--steps", type=int, default=64, help="timed decode steps")
     p.add_argument("--warmup", type=int, default=4)
+    p.add_argument("--layers", type=int, default=4, help="layers in flight")
     p.add_argument("--workload", default="qwen3_8b_16k_b128_staged")
     p.add_argument("--copy-mode", choices=["kernel", "dma"], default="kernel")
-    p.add_argument("--same-stream-copies", action="store_true",
-                   help="run staging copies on the compute stream instead of a copy stream")
+    p.add_argument("--host-threads", type=int, default=8, help="packing threads of the DMA copy engine")
     p.add_argument("--n-split", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline")
@@ -72,128 +79,78 @@ def main():
     w = wl.WORKLOADS[args.workload]
     B, H_q, H_kv, D, bs, K_b, NB = w.B, w.H_q, w.H_kv, w.D, w.bs, w.K_b, w.NB_max
     staged = w.staged
+    L = max(1, args.layers)
     C = oa.oasis_fetch_cap_blocks(w.cap, K_b) if staged else 0
     S = K_b + C
     copy_mode = oa.OASIS_COPY_DMA if args.copy_mode == "dma" else oa.OASIS_COPY_KERNEL
-    total_steps = 1 + args.warmup + args.steps          # step 0 = initial fill
+    n_steps = 1 + args.warmup + args.steps              # step 0 = initial fill
     t_setup = time.perf_counter()
 
     ctx_cpu = wl.context_lengths(w)
     ctx = ctx_cpu.to(dev)
-    log(f"workload {w.name}: B={B} H_q={H_q} H_kv={H_kv} NB_max={NB} K_b={K_b} C={C} staged={staged}")
+    log(f"workload {w.name}: B={B} H_q={H_q} H_kv={H_kv} NB_max={NB} K_b={K_b} C={C} staged={staged} "
+        f"layers={L} copy={args.copy_mode}")
     if staged:
-        pool = torch.empty((B, H_kv, NB, 2, bs, D), dtype=torch.bfloat16, pin_memory=True)
+        pool = oa.oasis_host_empty((B, H_kv, NB, 2, bs, D), torch.bfloat16)
         wl.kv_pool(w, device=dev, out=pool)
     else:
         pool = wl.kv_pool(w, device=dev)
     summ = oa.oasis_build_summaries(pool, ctx)
-    q_look = [wl.lookahead(w, s, dev) for s in range(total_steps)]
-    q_attn = [q_look[max(s - 1, 0)][:, 0].contiguous() for s in range(total_steps)]
+    # layer l at step t uses the lookahead of drift step t + 3 l (its own phase)
+    n_look = n_steps + 3 * (L - 1)
+    q_look = [wl.lookahead(w, s, dev) for s in range(n_look)]
+    q_attn = [q_look[max(s - 1, 0)][:, 0].contiguous() for s in range(n_look)]
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t_setup:.1f}s")
 
-    main_s = torch.cuda.current_stream()
-    comp_s = torch.cuda.Stream()
-    copy_s = None if (args.same_stream_copies or not staged) else torch.cuda.Stream()
+    timers = {k: [] for k in ("attn", "score", "topk", "plan")}
+    timing = [False]
 
-    scores = torch.empty((B, H_kv, NB), dtype=torch.float32, device=dev)
-    sel = [torch.empty((B, H_kv, K_b), dtype=torch.int32, device=dev) for _ in range(2)]
-    n_sel = [torch.empty((B, H_kv), dtype=torch.int32, device=dev) for _ in range(2)]
-    out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=dev)
-    if staged:
-        ws_pool = torch.empty((B, H_kv, S, 2, bs, D), dtype=torch.bfloat16, device=dev)
-        slot_block = torch.full((B, H_kv, S), -1, dtype=torch.int32, device=dev)
-        slot_stamp = torch.full_like(slot_block, -1)
-        tbls = [(torch.empty((B, H_kv, K_b), dtype=torch.int32, device=dev),
-                 torch.empty((B, H_kv, K_b), dtype=torch.int32, device=dev),
-                 torch.zeros((B, H_kv), dtype=torch.int32, device=dev)) for _ in range(2)]
-        # two plans: the copies of step s still read theirs while step s + 1 plans
-        plans = [torch.empty(oa.oasis_stage_plan_bytes(B, H_kv, K_b) // 4, dtype=torch.int32, device=dev)
-                 for _ in range(2)]
-        host_plan = torch.empty(plans[0].numel(), dtype=torch.int32).pin_memory() if copy_mode else None
-        admitted = torch.zeros((), dtype=torch.int64, device=dev)
-        T, P = K_b, S
-        attn_pool = ws_pool
-    else:
-        T, P = K_b, NB
-        attn_pool = pool
-    splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
-    ws_bytes = oa.oasis_attn_workspace_bytes(B, H_q, H_kv, T, args.n_split)
-    attn_ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-
-    def ev(timing=False):
-        return torch.cuda.Event(enable_timing=timing)
-
-    attn_done = [ev() for _ in range(total_steps)]
-    stage_done = [ev() for _ in range(total_steps)]
-    sel_done = [ev() for _ in range(total_steps)]
-    timers = {k: [] for k in ("attn", "score", "topk", "stage")}
-
-    def timed(name, stream, fn, on):
-        if not on:
+    def timer(name, stream, fn):
+        if not timing[0]:
             fn()
             return
-        a, b = ev(True), ev(True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         fn()
         b.record(stream)
         timers[name].append((a, b))
 
-    def attend(s, on):
-        if staged:
-            t = tbls[s % 2]
-            main_s.wait_event(stage_done[s - 1])
-            timed("attn", main_s, lambda: oa.oasis_sparse_decode_attn(
-                q_attn[s], attn_pool, t[0], t[1], t[2], ctx, out=out, ws=attn_ws, n_split=args.n_split,
-                stream=main_s), on)
-        else:
-            j = (s - 1) % 2
-            main_s.wait_event(sel_done[s - 1])
-            timed("attn", main_s, lambda: oa.oasis_sparse_decode_attn(
-                q_attn[s], attn_pool, sel[j], sel[j], n_sel[j], ctx, out=out, ws=attn_ws,
-                n_split=args.n_split, stream=main_s), on)
-        attn_done[s].record(main_s)
+    from prefetch_block_scoring_amd.pipeline import LayerPipeline
+    pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=H_q, K_b=K_b, C=C, n_layers=L, staged=staged,
+                         copy_mode=copy_mode, host_threads=args.host_threads, n_split=args.n_split,
+                         timer=timer)
+    T = K_b
+    splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
+    admitted = torch.zeros((), dtype=torch.int64, device=dev)
 
-    def predict_and_stage(s, on):
-        j = s % 2
-        with torch.cuda.stream(comp_s):
-            timed("score", comp_s, lambda: oa.oasis_score_blocks(q_look[s], summ, ctx, scores=scores,
-                                                                 stream=comp_s), on)
-            if s >= 2:
-                # sel[j] / tables[(s+1)%2] were last read by the attention of step s-1
-                comp_s.wait_event(attn_done[s - 1])
-            timed("topk", comp_s, lambda: oa.oasis_select_topk(scores, ctx, K_b, sel=sel[j], n_sel=n_sel[j],
-                                                               stream=comp_s), on)
-            if staged:
-                t = tbls[(s + 1) % 2]
-                timed("stage", comp_s, lambda: oa.oasis_stage_blocks(
-                    sel=sel[j], n_sel=n_sel[j], scores=scores, ctx_len=ctx, K_b=K_b,
-                    C=K_b if s == 0 else C, step=s, slot_block=slot_block, slot_stamp=slot_stamp,
-                    host_pool=pool, ws_pool=ws_pool, tbl_slot=t[0], tbl_block=t[1], tbl_n=t[2],
-                    plan=plans[j], host_plan=host_plan, copy_mode=copy_mode, stream=comp_s,
-                    copy_stream=copy_s, done_event=stage_done[s]), on)
-                if on:
-                    row = 2 + 2 * max(C, 1)
-                    admitted.add_(plans[j][: B * H_kv * row].view(B * H_kv, row)[:, 0].sum())
-            else:
-                sel_done[s].record(comp_s)
+    def run(t0, t1, counting=False):
+        for t in range(t0, t1):
+            for l in range(L):
+                s = t + 3 * l
+                pipe.layer_step(l, t, q_look[s], q_attn[s])
+                if counting and staged and t >= 1:
+                    pipe.drain()
+                    with torch.cuda.stream(pipe.comp):
+                        admitted.add_(pipe.admitted(l, t))
 
-    def step(s, on):
-        if s >= 1:
-            attend(s, on)        # enqueue first: a blocking DMA-mode stage must not delay it
-        predict_and_stage(s, on)
-
-    # initial fill (step 0) and warm-up
-    for s in range(0, 1 + args.warmup):
-        step(s, False)
+    # initial fill (step 0) and warm-up; the warm-up steps also count the
+    # admitted blocks per layer-step (a property of the workload's drift), so
+    # that no counting work runs inside the timed steps
+    run(0, 1 + args.warmup, counting=True)
+    pipe.drain()
     torch.cuda.synchronize()
+    pipe.copy_host_s.clear()
+    timing[0] = True
     t0 = time.perf_counter()
-    for s in range(1 + args.warmup, total_steps):
-        step(s, True)
+    run(1 + args.warmup, n_steps)
+    pipe.drain()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    value = B * args.steps / elapsed
+    timing[0] = False
+    layer_steps = args.steps * L
+    ms_per_step = elapsed / layer_steps * 1e3
+    value = B * layer_steps / elapsed
 
     def avg_us(name):
         xs = timers[name]
@@ -201,9 +158,9 @@ def main():
 
     # algorithmic bytes per launch
     if staged:
-        tn = tbls[(total_steps - 1) % 2][2]
+        tn = pipe.table(0, n_steps - 1)[2]
     else:
-        tn = n_sel[(total_steps - 2) % 2]
+        tn = pipe.layers[0].n_sel[(n_steps - 2) % 2]
     n_entries = int(tn.sum())
     attn_bytes = (n_entries * 2 * bs * D * 2 + 2 * B * H_q * D * 2 + B * H_kv * T * 8 + B * H_kv * 4 + B * 4)
     n_blocks_total = int(sum(-(-int(c) // bs) for c in ctx_cpu)) * H_kv
@@ -216,16 +173,18 @@ def main():
                       "GBps": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None}
     h2d = None
     if staged:
-        kern["stage"] = {"avg_us": round(avg_us("stage"), 2),
-                         "note": "plan kernel" + (" and gather kernel" if copy_s is None and copy_mode == 0 else
-                                                  "; copies run on the copy engine / copy stream")}
-        adm = int(admitted) / args.steps
+        kern["plan"] = {"avg_us": round(avg_us("plan"), 2), "note": "plan and prefix kernels"}
+        kern["copy_host"] = {"avg_us": round(sum(pipe.copy_host_s) / max(len(pipe.copy_host_s), 1) * 1e6, 2),
+                              "note": ("host time of a staging call: plan read-back and packing up to the "
+                                       "copy's enqueue") if copy_mode == oa.OASIS_COPY_DMA
+                              else "host time of a staging call (enqueue only)"}
+        adm = int(admitted) / max(args.warmup * L, 1)
         h2d_bytes = adm * 2 * bs * D * 2
         # reference: one large pinned host -> device copy
-        big = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+        big = oa.oasis_host_empty((256 << 20,), torch.uint8)
         dst = torch.empty_like(big, device=dev)
         dst.copy_(big, non_blocking=True)
-        a, b = ev(True), ev(True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(4):
             dst.copy_(big, non_blocking=True)
@@ -233,8 +192,8 @@ def main():
         torch.cuda.synchronize()
         memcpy_gbs = 4 * big.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
         step_gbs = h2d_bytes / (ms_per_step * 1e-3) / 1e9
-        h2d = {"bytes_per_step": int(h2d_bytes), "blocks_per_step": round(adm, 1),
-               "GBps_over_step": round(step_gbs, 2), "pcie_nominal_GBps": PCIE_PEAK_GBS,
+        h2d = {"bytes_per_layer_step": int(h2d_bytes), "blocks_per_layer_step": round(adm, 1),
+               "GBps": round(step_gbs, 2), "pcie_nominal_GBps": PCIE_PEAK_GBS,
                "frac_of_nominal": round(step_gbs / PCIE_PEAK_GBS, 3),
                "pinned_memcpy_GBps": round(memcpy_gbs, 2),
                "frac_of_memcpy": round(step_gbs / memcpy_gbs, 3),
@@ -253,11 +212,12 @@ def main():
                                  "frac_of_peak": round(hbm_bytes / (hbm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
     if args.check:
-        check_against_oracle(w, pool, ctx_cpu, q_look, q_attn, out, tbls if staged else None, total_steps)
+        check_against_oracle(w, pool, ctx_cpu, q_attn, pipe, n_steps)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, pool, ctx_cpu, q_look, args.cpu_seconds, C)
+    pipe.close()
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -267,8 +227,11 @@ def main():
         "config": {"workload": w.name, "batch": B, "context": w.ctx, "heads_q": H_q, "heads_kv": H_kv,
                    "head_dim": D, "block_tokens": bs, "kv_budget_tokens": w.budget, "lookahead_queries": w.J,
                    "fetch_cap": w.cap, "fetch_cap_blocks": C, "slots": S if staged else None,
+                   "layers_in_flight": L, "step_unit": "layer-step",
                    "kv_location": "pinned host pool + HBM working set" if staged else "HBM",
-                   "copy_engine": args.copy_mode if staged else None, "attn_splits": splits},
+                   "copy_engine": args.copy_mode if staged else None,
+                   "host_threads": args.host_threads if staged and copy_mode == oa.OASIS_COPY_DMA else None,
+                   "attn_splits": splits},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "h2d": h2d,
@@ -278,10 +241,9 @@ def main():
 
 
 def cpu_baseline(w, pool, ctx_cpu, q_look, seconds, C):
-    """The CPU oracle, unchanged, on the same inputs: full-batch decode
-    layer-steps (score, select, staging bookkeeping, attention over the
-    selected resident blocks read from the host pool) until about `seconds`
-    of work are done."""
+    """The CPU oracle, unchanged, on the same inputs: full-batch layer-steps
+    (score, select, staging bookkeeping, attention over the resident blocks
+    read from the host pool) until about `seconds` of work are done."""
     import numpy as np
     import torch
     import oracle
@@ -317,9 +279,9 @@ def cpu_baseline(w, pool, ctx_cpu, q_look, seconds, C):
         n_steps += 1
         t_total += dt
         s += 1
-        log(f"cpu baseline: step {n_steps} took {dt:.2f}s")
         if t_total >= seconds or n_steps >= 64:
             break
+    log(f"cpu baseline: {n_steps} layer-steps in {t_total:.1f}s")
     return {"value": round(w.B * n_steps / t_total, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{n_steps} full-batch layer-steps (B={w.B}) of score+select+"
@@ -338,28 +300,42 @@ def _cpu_model():
     return None
 
 
-def check_against_oracle(w, pool, ctx_cpu, q_look, q_attn, out, tbls, total_steps):
-    """Sampled parity at full size: requests 0 and B-1 of the last step."""
+def check_against_oracle(w, pool, ctx_cpu, q_attn, pipe, n_steps):
+    """Sampled parity at full size: requests 0 and B-1 of every layer's last
+    step, against the oracle's attention over the same resident blocks (the
+    staging itself is checked against the oracle in the test suite)."""
     import numpy as np
     import torch
     import oracle
     log("check: comparing sampled requests against the oracle")
-    s = total_steps - 1
+    if not w.staged:
+        raise SystemExit("--check covers staged workloads")
+    t = n_steps - 1
     rs = sorted({0, w.B - 1})
-    u16 = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    u16 = lambda x: x.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
     kv = u16(pool[rs])
     ctx = ctx_cpu.numpy()[rs]
-    if tbls is not None:
-        t = tbls[s % 2]
-        blocks = t[1].cpu().numpy()[rs]
-        n = t[2].cpu().numpy()[rs]
-    else:
-        raise SystemExit("--check covers staged workloads")
-    ref, _ = oracle.attend(u16(q_attn[s][rs]), kv, ctx, blocks, n, 1 / math.sqrt(w.D))
-    got = (u16(out[rs]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    bad = np.abs(got - ref) > 2e-3 + 1e-2 * np.abs(ref)
-    log(f"check: {bad.sum()} of {bad.size} outputs out of tolerance")
-    if bad.any():
+    bad_total, n_total = 0, 0
+    for l in range(pipe.L):
+        tb = pipe.table(l, t)
+        blocks = tb[1].cpu().numpy()[rs]
+        n = tb[2].cpu().numpy()[rs]
+        ref, _ = oracle.attend(u16(q_attn[t + 3 * l][rs]), kv, ctx, blocks, n, 1 / math.sqrt(w.D))
+        got = (u16(pipe.layers[l].out[rs]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        bad = np.abs(got - ref) > 2e-3 + 1e-2 * np.abs(ref)
+        bad_total += int(bad.sum())
+        n_total += bad.size
+        # the resident blocks themselves: every slot holds its block's bytes
+        ly = pipe.layers[l]
+        ws = ly.ws_pool
+        for i, r in enumerate(rs):
+            slots = tb[0][r].cpu().numpy()
+            for h in range(w.H_kv):
+                for e in range(int(n[i, h])):
+                    if not torch.equal(ws[r, h, int(slots[h, e])].cpu(), pool[r, h, int(blocks[i, h, e])]):
+                        bad_total += 1
+    log(f"check: {bad_total} of {n_total} outputs (and resident blocks) out of tolerance")
+    if bad_total:
         raise SystemExit("check failed")
 
 

@@ -57,7 +57,7 @@ extern "C" {
 
 /* Copy engines for oasis_stage_blocks. */
 #define OASIS_COPY_KERNEL 0      /* device kernel reads the mapped pinned pool */
-#define OASIS_COPY_DMA 1         /* one hipMemcpyAsync per admitted block */
+#define OASIS_COPY_DMA 1         /* host packs, DMA engine copies, device scatters */
 
 typedef struct oasis_dims {
     int32_t B;       /* requests in the batch (0 = nothing to do) */
@@ -74,6 +74,17 @@ const char *oasis_version(void);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char *oasis_last_error(void);
+
+/* Pinned host memory for the KV pool and the staging buffers (hipHostMalloc,
+ * default flags), with every page mapped into the process before the call
+ * returns.  Pinned pages that only a device has written are otherwise
+ * mapped for the CPU on first touch, one fault per 4 KiB page; the DMA
+ * engine's packing threads visit fresh pages of the pool every step and would
+ * pay that each time.  On success *ptr holds `bytes` bytes (contents
+ * unspecified); release with oasis_host_free.  Returns OASIS_EINVAL for a
+ * NULL ptr or zero bytes, OASIS_EHIP if the runtime cannot pin the memory. */
+int oasis_host_alloc(size_t bytes, void **ptr);
+int oasis_host_free(void *ptr);
 
 /* Blocks per KV head per layer per step admitted under a fetch-cap fraction
  * (section 4 bounds the transfer to C blocks per KV head per layer; sections
@@ -156,20 +167,38 @@ int oasis_select_topk(const oasis_dims *dims, const float *scores,
  * The table for the next attention (tbl_slot / tbl_block / tbl_n, capacity
  * K_b entries per (r, h)) lists every resident slot after the step, in
  * ascending slot order.  It must not be a table that an attention still in
- * flight reads: alternate two tables.
+ * flight reads: rotate two tables when each stage call waits for the
+ * previous attention, three when stage calls may run one attention ahead.
  *
  * Ordering: the slot-table update and plan run on `stream`.  Copies run on
  * `copy_stream` (NULL = `stream`) after the plan and after `wait_event` (if
- * not NULL), which must mark the end of every attention that read the
- * table of the previous step.  `done_event` (if not NULL) is recorded on
- * `copy_stream` after the last copy: make the next attention wait on it.
+ * not NULL).  The copies of this call never touch a slot listed in the table
+ * written by the previous call, but may refill slots listed in the table
+ * written two calls earlier (blocks the previous call evicted): `wait_event`
+ * must mark the end of every attention that read that older table.
+ * `done_event` (if not NULL) is recorded on `copy_stream` after the last
+ * copy: make the next attention wait on it.
  *
- * Copy engines: OASIS_COPY_KERNEL enqueues a gather kernel that reads the
- * pinned pool through its device mapping; it never blocks the caller.
- * OASIS_COPY_DMA reads the plan back into `host_plan` (pinned host, at least
- * oasis_stage_host_plan_bytes() bytes), BLOCKS THE CALLING THREAD until the
- * plan kernel has finished, then enqueues one hipMemcpyAsync per admitted
- * block (adjacent blocks into adjacent slots are merged) on copy_stream.
+ * Copy engines:
+ *  - OASIS_COPY_DMA reads the plan back into `host_plan` (pinned host, at
+ *    least oasis_stage_plan_bytes()), BLOCKING THE CALLING THREAD until the
+ *    plan kernel has finished; `host_threads` worker threads (0 = 8) then pack
+ *    the admitted blocks into `stage_host` (pinned host), one hipMemcpyAsync on
+ *    copy_stream moves them into `stage_dev` (device), and a scatter kernel on
+ *    copy_stream places them into their slots.  The staging buffers hold
+ *    floor(bytes / 8 KiB) blocks each; more admits than that are moved in
+ *    rounds, the call waiting on the host for each round's copy before it
+ *    repacks.  The call returns once the last copy is enqueued.  A later call
+ *    that packs into the same `stage_host` first waits for this call's copy
+ *    (the library remembers the last few buffers per thread), so alternating
+ *    two staging buffers lets packing overlap the previous step's copy.  The
+ *    DMA engines leave the compute units and their memory path to the
+ *    HBM-bound kernels running meanwhile.
+ *  - OASIS_COPY_KERNEL enqueues a gather kernel on copy_stream that reads the
+ *    pinned pool through its device mapping; it never blocks the caller,
+ *    needs no staging buffers and no host CPU time.  It runs on a small
+ *    fixed grid: its PCIe reads slow concurrent HBM-bound kernels down, and a
+ *    small grid still keeps the link near its memcpy rate.
  *
  * The copies read the plan workspace after the call returns: the next
  * step must use another plan buffer, or wait for `done_event` first.  Calls
@@ -193,25 +222,49 @@ typedef struct oasis_stage_args {
     int32_t *tbl_n;         /* [B][H_kv] device, written */
     int32_t *plan;          /* device workspace, oasis_stage_plan_bytes() */
     size_t plan_bytes;
-    void *host_plan;        /* pinned host, OASIS_COPY_DMA only */
+    void *host_plan;        /* pinned host, oasis_stage_plan_bytes(); DMA only */
     size_t host_plan_bytes;
-    int32_t copy_mode;      /* OASIS_COPY_KERNEL or OASIS_COPY_DMA */
+    void *stage_host;       /* pinned host staging buffer; DMA only */
+    size_t stage_host_bytes;
+    void *stage_dev;        /* device staging buffer; DMA only */
+    size_t stage_dev_bytes;
+    int32_t host_threads;   /* packing threads, DMA only (0 = 8) */
+    int32_t copy_mode;      /* OASIS_COPY_DMA or OASIS_COPY_KERNEL */
     void *stream;
     void *copy_stream;
     void *wait_event;
     void *done_event;
+    void *plan_event;       /* optional: recorded after the plan kernels */
 } oasis_stage_args;
 
-/* Bytes of the device plan workspace and of the pinned host plan buffer:
- * 4 * B * H_kv * (2 + 2 * max(C, 1)). */
+/* Bytes of the device plan workspace (and of the pinned host plan buffer):
+ * 4 * (B * H_kv * (4 + 2 * max(C, 1)) + 4). */
 size_t oasis_stage_plan_bytes(const oasis_dims *dims, int32_t C);
-size_t oasis_stage_host_plan_bytes(const oasis_dims *dims, int32_t C);
 
-/* One staging step.  Once the plan kernel has run, the plan workspace holds
- * int32 [B][H_kv][2 + 2 * max(C, 1)]: per (r, h) the admit count, the evict
- * count, then the admitted (slot, block) pairs in admission order.  The
- * host plan (OASIS_COPY_DMA) receives the same array. */
+/* Bytes of a staging buffer (host or device) that holds n_blocks blocks. */
+size_t oasis_stage_buffer_bytes(const oasis_dims *dims, int32_t n_blocks);
+
+/* One staging step.  Once the plan kernels have run, the plan workspace holds
+ * int32 [B * H_kv][4 + 2 * max(C, 1)] followed by 4 int32: per (r, h) the
+ * admit count, the evict count, the packed position of its first admit (the
+ * running total of admits over the (r, h) before it), a reserved word, then
+ * the admitted (slot, block) pairs in admission order; after the rows the
+ * total number of admits.  The host plan (OASIS_COPY_DMA) receives a copy. */
 int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *args);
+
+/* The two halves of oasis_stage_blocks, for callers that overlap staging
+ * across layers: oasis_stage_plan enqueues the plan kernels (steps 1-4 and
+ * the table) on `stream`, records `plan_event` if given, and never blocks.
+ * oasis_stage_copy performs step 5 for the plan in `plan`: it orders the
+ * copies after `plan_event` if given, else after everything enqueued on
+ * `stream` so far, and otherwise behaves as the copy part of
+ * oasis_stage_blocks (it blocks the calling thread with OASIS_COPY_DMA).  It
+ * may run on another thread than the plan, as long as it is called after
+ * oasis_stage_plan of the same step has returned.  oasis_stage_copy reads only
+ * copy_mode, C, S, plan, host_pool, ws_pool, the staging buffers, the streams
+ * and the events; oasis_stage_plan reads everything else. */
+int oasis_stage_plan(const oasis_dims *dims, const oasis_stage_args *args);
+int oasis_stage_copy(const oasis_dims *dims, const oasis_stage_args *args);
 
 /* Sparse GQA decode attention over the listed blocks (sections 4 and 7:
  * attention runs over the HBM working set only).  For query head g of

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import weakref
 from typing import Optional
 
 import torch
@@ -47,8 +48,10 @@ class oasis_stage_args(ctypes.Structure):
         ("S", _I32), ("step", _I32), ("slot_block", _P), ("slot_stamp", _P), ("ctx_len", _P),
         ("host_pool", _P), ("ws_pool", _P), ("tbl_slot", _P), ("tbl_block", _P), ("tbl_n", _P),
         ("plan", _P), ("plan_bytes", ctypes.c_size_t), ("host_plan", _P),
-        ("host_plan_bytes", ctypes.c_size_t), ("copy_mode", _I32), ("stream", _P),
-        ("copy_stream", _P), ("wait_event", _P), ("done_event", _P)]
+        ("host_plan_bytes", ctypes.c_size_t), ("stage_host", _P), ("stage_host_bytes", ctypes.c_size_t),
+        ("stage_dev", _P), ("stage_dev_bytes", ctypes.c_size_t), ("host_threads", _I32),
+        ("copy_mode", _I32), ("stream", _P), ("copy_stream", _P), ("wait_event", _P),
+        ("done_event", _P), ("plan_event", _P)]
 
 
 # name -> (restype, argtypes)
@@ -56,12 +59,16 @@ _SIGNATURES = {
     "oasis_version": (ctypes.c_char_p, []),
     "oasis_last_error": (ctypes.c_char_p, []),
     "oasis_fetch_cap_blocks": (_I32, [ctypes.c_double, _I32]),
+    "oasis_host_alloc": (ctypes.c_int, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]),
+    "oasis_host_free": (ctypes.c_int, [_P]),
     "oasis_build_summaries": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _P, _P]),
     "oasis_score_blocks": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _I32, _P, _P, _P, _P]),
     "oasis_select_topk": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P]),
     "oasis_stage_plan_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32]),
-    "oasis_stage_host_plan_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32]),
+    "oasis_stage_buffer_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32]),
     "oasis_stage_blocks": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args)]),
+    "oasis_stage_plan": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args)]),
+    "oasis_stage_copy": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args)]),
     "oasis_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32, _I32]),
     "oasis_attn_num_splits": (_I32, [ctypes.POINTER(oasis_dims), _I32, _I32]),
     "oasis_sparse_decode_attn": (ctypes.c_int, [
@@ -143,6 +150,24 @@ def oasis_last_error() -> str:
     return _lib.oasis_last_error().decode()
 
 
+def oasis_host_empty(shape, dtype=torch.bfloat16) -> torch.Tensor:
+    """A CPU tensor over pinned host memory from oasis_host_alloc (freed
+    with the tensor's storage).  Unlike torch's pin_memory buffers this memory
+    is cacheable for the CPU, which the DMA engine's packing threads need."""
+    nbytes = max(1, math.prod(shape) * torch.empty((), dtype=dtype).element_size())
+    p = ctypes.c_void_p()
+    _check(_lib.oasis_host_alloc(nbytes, ctypes.byref(p)))
+    ptr = p.value
+    buf = (ctypes.c_uint8 * nbytes).from_address(ptr)
+    flat = torch.frombuffer(buf, dtype=torch.uint8)
+    # free the memory when the last view of it dies
+    weakref.finalize(buf, _lib.oasis_host_free, ctypes.c_void_p(ptr))
+    flat._oasis_host_buffer = buf  # keep the ctypes owner alive with the tensor
+    t = flat[: math.prod(shape) * torch.empty((), dtype=dtype).element_size()].view(dtype).view(shape)
+    t._oasis_host_buffer = buf
+    return t
+
+
 def oasis_fetch_cap_blocks(cap: float, K_b: int) -> int:
     return int(_lib.oasis_fetch_cap_blocks(float(cap), int(K_b)))
 
@@ -203,14 +228,14 @@ def oasis_stage_plan_bytes(B: int, H_kv: int, C: int) -> int:
     return int(_lib.oasis_stage_plan_bytes(ctypes.byref(d), int(C)))
 
 
-def oasis_stage_blocks(*, sel, n_sel, scores, ctx_len, K_b: int, C: int, step: int, slot_block,
-                       slot_stamp, host_pool, ws_pool, tbl_slot, tbl_block, tbl_n, plan,
-                       host_plan=None, copy_mode: int = OASIS_COPY_KERNEL, stream=None,
-                       copy_stream=None, wait_event=None, done_event=None):
-    """One staging step (include/oasis.h).  host_pool: pinned bf16
-    [B][H_kv][NB_max][2][bs][D]; ws_pool: device bf16 [B][H_kv][S][2][bs][D];
-    slot tables int32 [B][H_kv][S]; tables int32 [B][H_kv][K_b]; plan: device
-    int32 of oasis_stage_plan_bytes() bytes."""
+def oasis_stage_buffer_bytes(n_blocks: int, D: int = 128, bs: int = 16) -> int:
+    d = dims(1, 1, 1, 1, D, bs)
+    return int(_lib.oasis_stage_buffer_bytes(ctypes.byref(d), int(n_blocks)))
+
+
+def _stage_args(sel, n_sel, scores, ctx_len, K_b, C, step, slot_block, slot_stamp, host_pool, ws_pool,
+                tbl_slot, tbl_block, tbl_n, plan, host_plan, stage_host, stage_dev, host_threads, copy_mode,
+                stream, copy_stream, wait_event, done_event, plan_event):
     _need(sel, "sel", torch.int32, 3)
     _need(n_sel, "n_sel", torch.int32, 2)
     _need(scores, "scores", torch.float32, 3)
@@ -238,14 +263,54 @@ def oasis_stage_blocks(*, sel, n_sel, scores, ctx_len, K_b: int, C: int, step: i
     a.host_pool, a.ws_pool = host_pool.data_ptr(), ws_pool.data_ptr()
     a.tbl_slot, a.tbl_block, a.tbl_n = tbl_slot.data_ptr(), tbl_block.data_ptr(), tbl_n.data_ptr()
     a.plan, a.plan_bytes = plan.data_ptr(), plan.numel() * plan.element_size()
-    if host_plan is not None:
-        a.host_plan, a.host_plan_bytes = host_plan.data_ptr(), host_plan.numel() * host_plan.element_size()
+    for name, t in (("host_plan", host_plan), ("stage_host", stage_host), ("stage_dev", stage_dev)):
+        if t is not None:
+            setattr(a, name, t.data_ptr())
+            setattr(a, name + "_bytes", t.numel() * t.element_size())
+    a.host_threads = int(host_threads)
     a.copy_mode = int(copy_mode)
     a.stream = _stream(stream)
     a.copy_stream = _stream(copy_stream) if copy_stream is not None else None
     a.wait_event = _event(wait_event)
     a.done_event = _event(done_event)
+    a.plan_event = _event(plan_event)
+    return d, a
+
+
+def oasis_stage_blocks(*, sel, n_sel, scores, ctx_len, K_b: int, C: int, step: int, slot_block,
+                       slot_stamp, host_pool, ws_pool, tbl_slot, tbl_block, tbl_n, plan,
+                       host_plan=None, stage_host=None, stage_dev=None, host_threads: int = 0,
+                       copy_mode: int = OASIS_COPY_KERNEL, stream=None, copy_stream=None, wait_event=None,
+                       done_event=None, plan_event=None):
+    """One staging step (include/oasis.h).  host_pool: pinned bf16
+    [B][H_kv][NB_max][2][bs][D]; ws_pool: device bf16 [B][H_kv][S][2][bs][D];
+    slot tables int32 [B][H_kv][S]; tables int32 [B][H_kv][K_b]; plan: device
+    int32 of oasis_stage_plan_bytes() bytes.  The DMA engine also needs
+    host_plan (pinned, as large as plan) and the staging buffers stage_host
+    (pinned) and stage_dev (device)."""
+    d, a = _stage_args(sel, n_sel, scores, ctx_len, K_b, C, step, slot_block, slot_stamp, host_pool, ws_pool,
+                       tbl_slot, tbl_block, tbl_n, plan, host_plan, stage_host, stage_dev, host_threads,
+                       copy_mode, stream, copy_stream, wait_event, done_event, plan_event)
     _check(_lib.oasis_stage_blocks(ctypes.byref(d), ctypes.byref(a)))
+
+
+def oasis_stage_plan(**kw):
+    """The plan half of oasis_stage_blocks (same keyword arguments); never blocks."""
+    d, a = _stage_args(**_stage_kw(kw))
+    _check(_lib.oasis_stage_plan(ctypes.byref(d), ctypes.byref(a)))
+
+
+def oasis_stage_copy(**kw):
+    """The copy half of oasis_stage_blocks (same keyword arguments)."""
+    d, a = _stage_args(**_stage_kw(kw))
+    _check(_lib.oasis_stage_copy(ctypes.byref(d), ctypes.byref(a)))
+
+
+def _stage_kw(kw):
+    full = dict(host_plan=None, stage_host=None, stage_dev=None, host_threads=0, copy_mode=OASIS_COPY_KERNEL,
+                stream=None, copy_stream=None, wait_event=None, done_event=None, plan_event=None)
+    full.update(kw)
+    return full
 
 
 def oasis_attn_workspace_bytes(B: int, H_q: int, H_kv: int, T: int, n_split: int = 0) -> int:

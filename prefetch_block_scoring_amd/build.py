@@ -1,6 +1,8 @@
 """Build liboasis.so (HIP, gfx950) in-tree.
 
-    python -m prefetch_block_scoring_amd.build
+    python prefetch_block_scoring_amd/build.py
+
+(run it as a file: importing the package loads the library this builds)
 
 Every HIP source is compiled with packed-fp32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``): the kernels are written

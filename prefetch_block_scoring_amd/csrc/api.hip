@@ -19,8 +19,6 @@ struct DevInfo {
 std::mutex g_dev_mu;
 std::vector<DevInfo> g_dev;
 
-// Per-thread, per-device event that orders the copy stream after the plan.
-thread_local std::vector<hipEvent_t> t_plan_event;
 }  // namespace
 
 void set_error(const std::string &msg) { g_error = msg; }
@@ -73,15 +71,6 @@ int device_view(const void *p, const void **out, const char *name) {
     return OASIS_EINVAL;
 }
 
-static int plan_event(hipEvent_t *ev) {
-    int dev = 0;
-    OASIS_HIP(hipGetDevice(&dev));
-    if ((int)t_plan_event.size() <= dev) t_plan_event.resize(dev + 1, nullptr);
-    if (!t_plan_event[dev]) OASIS_HIP(hipEventCreateWithFlags(&t_plan_event[dev], hipEventDisableTiming));
-    *ev = t_plan_event[dev];
-    return OASIS_OK;
-}
-
 }  // namespace oasis
 
 using namespace oasis;
@@ -120,6 +109,23 @@ extern "C" {
 const char *oasis_version(void) { return "oasis 0.1.0 gfx950"; }
 
 const char *oasis_last_error(void) { return g_error.c_str(); }
+
+int oasis_host_alloc(size_t bytes, void **ptr) {
+    clear_error();
+    if (!ptr) FAIL(OASIS_EINVAL, "ptr is NULL");
+    *ptr = nullptr;
+    if (bytes == 0) FAIL(OASIS_EINVAL, "bytes = 0");
+    OASIS_HIP(hipHostMalloc(ptr, bytes, hipHostMallocDefault));
+    prefault_host(*ptr, bytes);
+    return OASIS_OK;
+}
+
+int oasis_host_free(void *ptr) {
+    clear_error();
+    if (!ptr) return OASIS_OK;
+    OASIS_HIP(hipHostFree(ptr));
+    return OASIS_OK;
+}
 
 int32_t oasis_fetch_cap_blocks(double cap, int32_t K_b) {
     if (K_b < 1) return -1;
@@ -178,13 +184,16 @@ int oasis_select_topk(const oasis_dims *dims, const float *scores, const int32_t
 
 size_t oasis_stage_plan_bytes(const oasis_dims *dims, int32_t C) {
     if (!dims || dims->B < 0 || dims->H_kv < 1) return 0;
-    return sizeof(int32_t) * (size_t)dims->B * dims->H_kv * plan_row(C);
+    return sizeof(int32_t) * plan_ints(dims->B * dims->H_kv, C);
 }
 
-size_t oasis_stage_host_plan_bytes(const oasis_dims *dims, int32_t C) { return oasis_stage_plan_bytes(dims, C); }
+size_t oasis_stage_buffer_bytes(const oasis_dims *dims, int32_t n_blocks) {
+    if (!dims || n_blocks < 0 || dims->bs < 1 || dims->D < 1) return 0;
+    return (size_t)n_blocks * 2 * dims->bs * dims->D * sizeof(uint16_t);
+}
 
-int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *a) {
-    clear_error();
+// Arguments of the plan phase.
+static int check_plan_args(const oasis_dims *dims, const oasis_stage_args *a) {
     int rc = check_dims(dims);
     if (rc) return rc;
     if (!a) FAIL(OASIS_EINVAL, "args is NULL");
@@ -195,8 +204,6 @@ int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *a) {
     if (a->S > 2048 || a->K_sel > 1024)
         FAIL(OASIS_EUNSUPPORTED, "S = %d, K_sel = %d (at most 2048, 1024)", a->S, a->K_sel);
     if (a->step < 0) FAIL(OASIS_EINVAL, "step = %d < 0", a->step);
-    if (a->copy_mode != OASIS_COPY_KERNEL && a->copy_mode != OASIS_COPY_DMA)
-        FAIL(OASIS_EINVAL, "copy_mode = %d", a->copy_mode);
     if (dims->B == 0) return OASIS_OK;
     NEED(a->sel);
     NEED(a->n_sel);
@@ -204,71 +211,107 @@ int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *a) {
     NEED(a->slot_block);
     NEED(a->slot_stamp);
     NEED(a->ctx_len);
-    NEED(a->host_pool);
-    NEED(a->ws_pool);
     NEED(a->tbl_slot);
     NEED(a->tbl_block);
     NEED(a->tbl_n);
     NEED(a->plan);
     const size_t need = oasis_stage_plan_bytes(dims, a->C);
     if (a->plan_bytes < need) FAIL(OASIS_ENOSPACE, "plan workspace %zu bytes < %zu", a->plan_bytes, need);
+    return OASIS_OK;
+}
+
+// Arguments of the copy phase (host checks only).
+static int check_copy_args(const oasis_dims *dims, const oasis_stage_args *a) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!a) FAIL(OASIS_EINVAL, "args is NULL");
+    if (a->C < 0 || a->C > 16384) FAIL(OASIS_EINVAL, "C = %d", a->C);
+    if (a->S < 1 || a->S > 2048) FAIL(a->S < 1 ? OASIS_EINVAL : OASIS_EUNSUPPORTED, "S = %d", a->S);
+    if (a->copy_mode != OASIS_COPY_KERNEL && a->copy_mode != OASIS_COPY_DMA)
+        FAIL(OASIS_EINVAL, "copy_mode = %d", a->copy_mode);
+    if (dims->B == 0) return OASIS_OK;
+    NEED(a->plan);
+    NEED(a->host_pool);
+    NEED(a->ws_pool);
+    const size_t need = oasis_stage_plan_bytes(dims, a->C);
+    if (a->plan_bytes < need) FAIL(OASIS_ENOSPACE, "plan workspace %zu bytes < %zu", a->plan_bytes, need);
     if (a->copy_mode == OASIS_COPY_DMA) {
         NEED(a->host_plan);
+        NEED(a->stage_host);
+        NEED(a->stage_dev);
         if (a->host_plan_bytes < need)
             FAIL(OASIS_ENOSPACE, "host plan %zu bytes < %zu", a->host_plan_bytes, need);
+        if (a->C > 0 && (a->stage_host_bytes < kBlockBytes || a->stage_dev_bytes < kBlockBytes))
+            FAIL(OASIS_ENOSPACE, "staging buffers (%zu, %zu bytes) hold no block", a->stage_host_bytes,
+                 a->stage_dev_bytes);
+        if (a->host_threads < 0 || a->host_threads > 256)
+            FAIL(OASIS_EINVAL, "host_threads = %d outside [0, 256]", a->host_threads);
     }
+    return OASIS_OK;
+}
+
+static int stage_plan_phase(const oasis_dims *dims, const oasis_stage_args *a) {
+    hipStream_t s = static_cast<hipStream_t>(a->stream);
+    OASIS_HIP(launch_stage_plan(*dims, *a, s));
+    OASIS_HIP(launch_stage_prefix(*dims, *a, s));
+    if (a->plan_event) OASIS_HIP(hipEventRecord(static_cast<hipEvent_t>(a->plan_event), s));
+    return OASIS_OK;
+}
+
+static int stage_copy_phase(const oasis_dims *dims, const oasis_stage_args *a) {
+    int rc;
     const void *pool_dev = nullptr;
     if ((rc = device_view(a->host_pool, &pool_dev, "host_pool"))) return rc;
     if (a->copy_mode == OASIS_COPY_DMA) {
-        hipPointerAttribute_t at;
-        if (hipPointerGetAttributes(&at, a->host_plan) != hipSuccess || at.type != hipMemoryTypeHost) {
-            (void)hipGetLastError();
-            FAIL(OASIS_EINVAL, "host_plan is not pinned host memory");
-        }
-    }
-
-    hipStream_t s = static_cast<hipStream_t>(a->stream);
-    hipStream_t cs = a->copy_stream ? static_cast<hipStream_t>(a->copy_stream) : s;
-    OASIS_HIP(launch_stage_plan(*dims, *a, s));
-
-    if (a->copy_mode == OASIS_COPY_KERNEL) {
-        if (cs != s) {
-            hipEvent_t ev;
-            if ((rc = plan_event(&ev))) return rc;
-            OASIS_HIP(hipEventRecord(ev, s));
-            OASIS_HIP(hipStreamWaitEvent(cs, ev, 0));
-        }
-        if (a->wait_event) OASIS_HIP(hipStreamWaitEvent(cs, static_cast<hipEvent_t>(a->wait_event), 0));
-        OASIS_HIP(launch_stage_gather(*dims, *a, pool_dev, cs));
-    } else {
-        OASIS_HIP(hipMemcpyAsync(a->host_plan, a->plan, need, hipMemcpyDeviceToHost, s));
-        OASIS_HIP(hipStreamSynchronize(s));
-        if (a->wait_event) OASIS_HIP(hipStreamWaitEvent(cs, static_cast<hipEvent_t>(a->wait_event), 0));
-        const int row = plan_row(a->C);
-        const int32_t *hp = static_cast<const int32_t *>(a->host_plan);
-        const char *src0 = static_cast<const char *>(a->host_pool);
-        char *dst0 = static_cast<char *>(a->ws_pool);
-        const int pairs = dims->B * dims->H_kv;
-        for (int rh = 0; rh < pairs; rh++) {
-            const int32_t *p = hp + (size_t)rh * row;
-            const int n = p[0] < a->C ? p[0] : a->C;
-            int i = 0;
-            while (i < n) {
-                const int slot = p[2 + 2 * i], blk = p[3 + 2 * i];
-                if (slot < 0 || slot >= a->S || blk < 0 || blk >= dims->NB_max) { i++; continue; }
-                int run = 1;  // merge admits that are adjacent in both pool and working set
-                while (i + run < n && p[2 + 2 * (i + run)] == slot + run && p[3 + 2 * (i + run)] == blk + run &&
-                       slot + run < a->S && blk + run < dims->NB_max)
-                    run++;
-                const char *src = src0 + ((size_t)rh * dims->NB_max + blk) * kBlockBytes;
-                char *dst = dst0 + ((size_t)rh * a->S + slot) * kBlockBytes;
-                OASIS_HIP(hipMemcpyAsync(dst, src, run * kBlockBytes, hipMemcpyHostToDevice, cs));
-                i += run;
+        for (const void *hb : {a->host_plan, a->stage_host}) {
+            hipPointerAttribute_t at;
+            if (hipPointerGetAttributes(&at, hb) != hipSuccess || at.type != hipMemoryTypeHost) {
+                (void)hipGetLastError();
+                FAIL(OASIS_EINVAL, "%s is not pinned host memory", hb == a->host_plan ? "host_plan" : "stage_host");
             }
         }
     }
+    hipStream_t s = static_cast<hipStream_t>(a->stream);
+    hipStream_t cs = a->copy_stream ? static_cast<hipStream_t>(a->copy_stream) : s;
+    // the plan this copy uses: `plan_event` if given, else everything on `stream` so far
+    hipEvent_t plan_ready = static_cast<hipEvent_t>(a->plan_event);
+    if (!plan_ready) {
+        if ((rc = ring_event(&plan_ready))) return rc;
+        OASIS_HIP(hipEventRecord(plan_ready, s));
+    }
+    if (a->copy_mode == OASIS_COPY_KERNEL) {
+        OASIS_HIP(hipStreamWaitEvent(cs, plan_ready, 0));
+        if (a->wait_event) OASIS_HIP(hipStreamWaitEvent(cs, static_cast<hipEvent_t>(a->wait_event), 0));
+        OASIS_HIP(launch_stage_gather(*dims, *a, pool_dev, cs));
+    } else {
+        if ((rc = stage_dma(*dims, *a, plan_ready, cs))) return rc;
+    }
     if (a->done_event) OASIS_HIP(hipEventRecord(static_cast<hipEvent_t>(a->done_event), cs));
     return OASIS_OK;
+}
+
+int oasis_stage_plan(const oasis_dims *dims, const oasis_stage_args *a) {
+    clear_error();
+    int rc = check_plan_args(dims, a);
+    if (rc || dims->B == 0) return rc;
+    return stage_plan_phase(dims, a);
+}
+
+int oasis_stage_copy(const oasis_dims *dims, const oasis_stage_args *a) {
+    clear_error();
+    int rc = check_copy_args(dims, a);
+    if (rc || dims->B == 0) return rc;
+    return stage_copy_phase(dims, a);
+}
+
+int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *a) {
+    clear_error();
+    int rc = check_plan_args(dims, a);
+    if (rc) return rc;
+    if ((rc = check_copy_args(dims, a))) return rc;
+    if (dims->B == 0) return OASIS_OK;
+    if ((rc = stage_plan_phase(dims, a))) return rc;
+    return stage_copy_phase(dims, a);
 }
 
 size_t oasis_attn_workspace_bytes(const oasis_dims *dims, int32_t T, int32_t n_split) {

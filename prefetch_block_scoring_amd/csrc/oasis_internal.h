@@ -72,8 +72,34 @@ hipError_t launch_attn(const oasis_dims &d, const uint16_t *q,
                        const int32_t *ctx_len, float sm_scale, uint16_t *out,
                        float *lse, float *ws, int n_split, hipStream_t s);
 
-// plan workspace row length in int32 per (r, h)
-__host__ __device__ inline int plan_row(int C) { return 2 + 2 * (C > 0 ? C : 1); }
+// Plan workspace: per (r, h) a row of int32
+//   [0] admits, [1] evictions, [2] packed position of the first admit (the
+//   exclusive prefix of admits over (r, h)), [3] reserved, then one
+//   (slot, block) pair per admit;
+// after the rows, kPlanTail int32: [0] total admits.
+constexpr int kPlanHead = 4;
+constexpr int kPlanTail = 4;
+__host__ __device__ inline int plan_row(int C) { return kPlanHead + 2 * (C > 0 ? C : 1); }
+inline size_t plan_ints(int pairs, int C) { return (size_t)pairs * plan_row(C) + kPlanTail; }
+
+hipError_t launch_stage_prefix(const oasis_dims &d, const oasis_stage_args &a, hipStream_t s);
+
+// Copy the admitted blocks of packed positions [lo, hi) from the device
+// staging buffer (position lo at its start) into their working-set slots.
+hipError_t launch_stage_scatter(const oasis_dims &d, const oasis_stage_args &a, int lo, int hi,
+                                hipStream_t s);
+
+// Host side of the DMA copy engine: read back the plan, pack the admitted
+// blocks on worker threads, one H2D copy per round, scatter on the device.
+int stage_dma(const oasis_dims &d, const oasis_stage_args &a, hipEvent_t plan_ready, hipStream_t cs);
+
+// per-thread ring of ordering events on the current device
+int ring_event(hipEvent_t *ev);
+
+// Map every page of a fresh pinned host allocation into the process (one
+// write per page, on the worker threads) so that later CPU accesses, such as
+// the DMA engine's packing, do not take a page fault per new page.
+void prefault_host(void *p, size_t bytes);
 
 }  // namespace oasis
 

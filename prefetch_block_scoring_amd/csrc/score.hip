@@ -15,88 +15,139 @@
 // Arithmetic: Qp / Qm are summed in fp64 (exact for bf16 inputs of ordinary
 // range), the 2 * D products and their sum in fp64, rounded once to fp32.
 //
-// Mapping: a workgroup owns one (request, KV head) and a chunk of 256 blocks.
-// Eight lanes share a block (512 bytes of summary); lane i of the eight holds
-// dims [8i, 8i + 8) and [64 + 8i, 64 + 8i + 8) of kmin and kmax, so each of the
-// four 16-byte loads per lane is one fully used 128-byte line per eight lanes.
-// The eight partial sums meet through three xor shuffles.
+// Mapping: the grid is persistent (compute units x resident workgroups); the
+// (request, KV head, 128-block chunk) items are split into equal contiguous
+// ranges, one per workgroup, so Qp / Qm are rebuilt only when a range crosses
+// into the next (request, KV head).  Eight lanes share a block (512 bytes of
+// summary); lane i of the eight holds dims [8i, 8i + 8) and [64 + 8i, 72 + 8i)
+// of kmin and kmax, so each 16-byte load fills whole 128-byte lines per eight
+// lanes.  Four 32-block groups are loaded before any is used (16 KiB in flight
+// per wave).  The eight partial sums meet through three DPP steps.
 #include "oasis_internal.h"
 
 namespace oasis {
 namespace {
 
-constexpr int kChunk = 256;        // blocks per workgroup
-constexpr int kLanesPerBlock = 8;  // lanes sharing one block
-constexpr int kBlocksPerIter = 256 / kLanesPerBlock;
+constexpr int kThreads = 256;
+constexpr int kLanesPerBlock = 8;                       // lanes sharing one block
+constexpr int kBlocksPerGroup = kThreads / kLanesPerBlock;  // 32
+constexpr int kUnroll = 4;
+constexpr int kItemBlocks = kBlocksPerGroup * kUnroll;  // 128 blocks per item
 
 __device__ __forceinline__ double bf16_d(uint32_t bits16) {
     return (double)__uint_as_float(bits16 << 16);
 }
 
-__global__ __launch_bounds__(256) void score_kernel(
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+    const long long v = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, 0xF, 0xF, true);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Sum over the eight lanes of an aligned octet; every lane gets the total.
+__device__ __forceinline__ double octet_sum(double x) {
+    x += dpp_d<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_d<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_d<0x141>(x);  // row_half_mirror: lane i <- lane 7 - i within 8
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads) void score_kernel(
     const uint16_t *__restrict__ q_look, int J, int H_q, int H_kv,
     const uint4 *__restrict__ kminmax, const int32_t *__restrict__ ctx_len,
-    float *__restrict__ scores, int NB_max) {
+    float *__restrict__ scores, int NB_max, int chunks, int n_items) {
     __shared__ double Qsh[2][kD];  // [0] = Qm (pairs with kmin), [1] = Qp (pairs with kmax)
-    const int rh = blockIdx.x;
-    const int r = rh / H_kv;
-    const int h = rh - r * H_kv;
     const int G = H_q / H_kv;
     const int tid = threadIdx.x;
-    if (tid < kD) {
-        double qp = 0.0, qm = 0.0;
-        for (int j = 0; j < J; j++) {
-            const uint16_t *qrow = q_look + (((size_t)r * J + j) * H_q + (size_t)h * G) * kD + tid;
-            for (int gi = 0; gi < G; gi++) {
-                const double v = bf16_d(qrow[(size_t)gi * kD]);
-                if (v > 0.0) qp += v; else qm += v;
+    const int li = tid % kLanesPerBlock;
+    const int per = (n_items + gridDim.x - 1) / gridDim.x;
+    const int it0 = blockIdx.x * per;
+    const int it1 = min(n_items, it0 + per);
+
+    int cur = -1, nb = 0;
+    double qm[16], qp[16];
+    for (int item = it0; item < it1; item++) {
+        const int rh = item / chunks;
+        const int chunk = item - rh * chunks;
+        if (rh != cur) {  // uniform across the workgroup
+            cur = rh;
+            const int r = rh / H_kv, h = rh - (rh / H_kv) * H_kv;
+            __syncthreads();
+            if (tid < kD) {
+                double sp = 0.0, sm = 0.0;
+                for (int j = 0; j < J; j++) {
+                    const uint16_t *qrow = q_look + (((size_t)r * J + j) * H_q + (size_t)h * G) * kD + tid;
+                    for (int gi = 0; gi < G; gi++) {
+                        const double v = bf16_d(qrow[(size_t)gi * kD]);
+                        if (v > 0.0) sp += v; else sm += v;
+                    }
+                }
+                Qsh[0][tid] = sm;
+                Qsh[1][tid] = sp;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                qm[e] = Qsh[0][li * 8 + e];
+                qm[8 + e] = Qsh[0][64 + li * 8 + e];
+                qp[e] = Qsh[1][li * 8 + e];
+                qp[8 + e] = Qsh[1][64 + li * 8 + e];
+            }
+            nb = n_blocks_of(ctx_len[r], NB_max);
+        }
+        float *out = scores + (size_t)rh * NB_max;
+        const uint4 *base = kminmax + (size_t)rh * NB_max * 32;  // 32 uint4 per block summary
+        const int b0 = chunk * kItemBlocks + tid / kLanesPerBlock;
+        uint4 mn0[kUnroll], mn1[kUnroll], mx0[kUnroll], mx1[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int b = b0 + u * kBlocksPerGroup;
+            if (b < nb) {
+                const uint4 *sb = base + (size_t)b * 32;
+                mn0[u] = sb[li];
+                mn1[u] = sb[8 + li];
+                mx0[u] = sb[16 + li];
+                mx1[u] = sb[24 + li];
             }
         }
-        Qsh[0][tid] = qm;
-        Qsh[1][tid] = qp;
-    }
-    __syncthreads();
-
-    const int li = tid % kLanesPerBlock;
-    double qm[16], qp[16];
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        qm[e] = Qsh[0][li * 8 + e];
-        qm[8 + e] = Qsh[0][64 + li * 8 + e];
-        qp[e] = Qsh[1][li * 8 + e];
-        qp[8 + e] = Qsh[1][64 + li * 8 + e];
-    }
-
-    const int nb = n_blocks_of(ctx_len[r], NB_max);
-    const int b_end = min(NB_max, (int)(blockIdx.y + 1) * kChunk);
-    float *out = scores + (size_t)rh * NB_max;
-    // summary of block b: [2][kD] bf16 = 32 uint4; kmin at 0..15, kmax at 16..31
-    const uint4 *base = kminmax + (size_t)rh * NB_max * 32;
-    for (int b0 = blockIdx.y * kChunk; b0 < b_end; b0 += kBlocksPerIter) {
-        const int b = b0 + tid / kLanesPerBlock;
-        if (b >= b_end) continue;            // whole group of eight skips together
-        if (b >= nb) {
-            if (li == 0) out[b] = -INFINITY;
-            continue;
-        }
-        const uint4 *sb = base + (size_t)b * 32;
-        const uint4 mn0 = sb[li], mn1 = sb[8 + li], mx0 = sb[16 + li], mx1 = sb[24 + li];
-        const uint32_t wmn[8] = {mn0.x, mn0.y, mn0.z, mn0.w, mn1.x, mn1.y, mn1.z, mn1.w};
-        const uint32_t wmx[8] = {mx0.x, mx0.y, mx0.z, mx0.w, mx1.x, mx1.y, mx1.z, mx1.w};
-        double acc = 0.0;
+        for (int u = 0; u < kUnroll; u++) {
+            const int b = b0 + u * kBlocksPerGroup;
+            if (b >= NB_max) continue;            // the octet skips together
+            if (b >= nb) {
+                if (li == 0) out[b] = -INFINITY;
+                continue;
+            }
+            const uint32_t wmn[8] = {mn0[u].x, mn0[u].y, mn0[u].z, mn0[u].w,
+                                     mn1[u].x, mn1[u].y, mn1[u].z, mn1[u].w};
+            const uint32_t wmx[8] = {mx0[u].x, mx0[u].y, mx0[u].z, mx0[u].w,
+                                     mx1[u].x, mx1[u].y, mx1[u].z, mx1[u].w};
+            double acc = 0.0;
 #pragma unroll
-        for (int w = 0; w < 8; w++) {
-            const int e = (w < 4) ? 2 * w : 8 + 2 * (w - 4);
-            acc = fma(qm[e], bf16_d(wmn[w] & 0xffffu), acc);
-            acc = fma(qm[e + 1], bf16_d(wmn[w] >> 16), acc);
-            acc = fma(qp[e], bf16_d(wmx[w] & 0xffffu), acc);
-            acc = fma(qp[e + 1], bf16_d(wmx[w] >> 16), acc);
+            for (int w = 0; w < 8; w++) {
+                const int e = (w < 4) ? 2 * w : 8 + 2 * (w - 4);
+                acc = fma(qm[e], bf16_d(wmn[w] & 0xffffu), acc);
+                acc = fma(qm[e + 1], bf16_d(wmn[w] >> 16), acc);
+                acc = fma(qp[e], bf16_d(wmx[w] & 0xffffu), acc);
+                acc = fma(qp[e + 1], bf16_d(wmx[w] >> 16), acc);
+            }
+            acc = octet_sum(acc);
+            if (li == 0) out[b] = (float)acc;
         }
-        acc += __shfl_xor(acc, 1, kLanesPerBlock);
-        acc += __shfl_xor(acc, 2, kLanesPerBlock);
-        acc += __shfl_xor(acc, 4, kLanesPerBlock);
-        if (li == 0) out[b] = (float)acc;
     }
+}
+
+int score_grid(int n_items) {
+    static int occ = 0;  // resident workgroups per compute unit
+    if (occ == 0) {
+        int o = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, score_kernel, kThreads, 0) != hipSuccess || o < 1) o = 2;
+        occ = o;
+    }
+    const long g = (long)device_cu_count() * occ;
+    return (int)(n_items < g ? n_items : g);
 }
 
 }  // namespace
@@ -104,9 +155,11 @@ __global__ __launch_bounds__(256) void score_kernel(
 hipError_t launch_score(const oasis_dims &d, const uint16_t *q_look, int J,
                         const uint16_t *kminmax, const int32_t *ctx_len,
                         float *scores, hipStream_t s) {
-    dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)((d.NB_max + kChunk - 1) / kChunk));
-    hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, s, q_look, J, d.H_q, d.H_kv,
-                       reinterpret_cast<const uint4 *>(kminmax), ctx_len, scores, d.NB_max);
+    const int chunks = (d.NB_max + kItemBlocks - 1) / kItemBlocks;
+    const int n_items = d.B * d.H_kv * chunks;
+    hipLaunchKernelGGL(score_kernel, dim3((unsigned)score_grid(n_items)), dim3(kThreads), 0, s, q_look, J,
+                       d.H_q, d.H_kv, reinterpret_cast<const uint4 *>(kminmax), ctx_len, scores, d.NB_max,
+                       chunks, n_items);
     return hipGetLastError();
 }
 

@@ -12,9 +12,17 @@
 //   were free before this step, never to a slot evicted in this step, so the
 //   attention that still reads the previous table is not raced; with
 //   S >= K_b + C slots there are always enough of them.
-// gather kernel: one workgroup per admitted block copies its 8 KiB from the
-//   pinned host pool, read through the pool's device mapping over PCIe, into
-//   its slot; many workgroups keep many PCIe reads in flight.
+// prefix kernel: packed positions of the admits (the order in which a copy
+//   engine stages them).
+// Copy engines (the pinned pool's blocks to their slots):
+//   DMA: the host reads the plan back, packs the admitted blocks into a
+//     pinned staging buffer on worker threads, and one hipMemcpyAsync moves
+//     them over PCIe; the scatter kernel then places them.  The DMA engines
+//     leave the compute units and their memory path to the HBM-bound kernels
+//     that run at the same time.
+//   kernel: a persistent gather kernel reads the pool through its device
+//     mapping.  No host work, but its PCIe reads hold the memory path and
+//     slow concurrent HBM-bound kernels down.
 #include "oasis_internal.h"
 
 namespace oasis {
@@ -22,6 +30,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+
+// Workgroups of the zero-copy gather.  Its PCIe reads wait microseconds and,
+// while they wait, slow the HBM-bound kernels that run beside them; 32
+// workgroups (256 KiB of reads in flight) still keep the link near its
+// pinned-memcpy rate, and measured over a pipelined decode step fewer or more
+// of them were slower overall.
+constexpr int kGatherWgs = 32;
 
 __device__ __forceinline__ int wg_exclusive_scan(int v, int *tmp, int *total) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
@@ -209,12 +224,14 @@ __global__ __launch_bounds__(kThreads) void stage_plan_kernel(PlanArgs a) {
         const int s = list_s[i];
         sb[s] = adm[i];
         st[s] = a.step;
-        plan[2 + 2 * i] = s;
-        plan[3 + 2 * i] = adm[i];
+        plan[kPlanHead + 2 * i] = s;
+        plan[kPlanHead + 2 * i + 1] = adm[i];
     }
     if (tid == 0) {
         plan[0] = n_adm;
         plan[1] = need;
+        plan[2] = 0;
+        plan[3] = 0;
     }
     __syncthreads();
     for (int s = tid; s < S; s += kThreads) {
@@ -233,22 +250,82 @@ __global__ __launch_bounds__(kThreads) void stage_plan_kernel(PlanArgs a) {
     if (tid == 0) a.tbl_n[rh] = nt;
 }
 
+// Exclusive prefix of the admit counts over (r, h), written to each row's
+// packed position, and the total after the rows: one workgroup.
+__global__ __launch_bounds__(1024) void stage_prefix_kernel(int32_t *__restrict__ plan, int row, int pairs) {
+    __shared__ int tmp[16];
+    __shared__ int carry;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < pairs; base += 1024) {
+        const int rh = base + tid;
+        const int v = rh < pairs ? plan[(size_t)rh * row] : 0;
+        int inc = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) tmp[wave] = inc;
+        __syncthreads();
+        int before = carry, all = carry;
+        for (int w = 0; w < 16; w++) {
+            before += (w < wave) ? tmp[w] : 0;
+            all += tmp[w];
+        }
+        if (rh < pairs) plan[(size_t)rh * row + 2] = before + inc - v;
+        __syncthreads();
+        if (tid == 0) carry = all;
+        __syncthreads();
+    }
+    if (tid == 0) plan[(size_t)pairs * row] = carry;
+}
+
+// Zero-copy engine.  Persistent: kGatherWgs workgroups walk the (pair, admit)
+// items; each thread keeps two 16-byte PCIe reads in flight per block.
 __global__ __launch_bounds__(256) void stage_gather_kernel(
-    const int32_t *__restrict__ plan, int row, const uint4 *__restrict__ host_pool,
+    const int32_t *__restrict__ plan, int row, int C, int n_items, const uint4 *__restrict__ host_pool,
     uint4 *__restrict__ ws_pool, int NB_max, int S) {
-    const int rh = blockIdx.x;
-    const int i = blockIdx.y;
-    const int32_t *p = plan + (size_t)rh * row;
-    if (i >= p[0]) return;
-    const int slot = p[2 + 2 * i], blk = p[3 + 2 * i];
-    if (slot < 0 || slot >= S || blk < 0 || blk >= NB_max) return;
     constexpr int kVec = (int)(kBlockBytes / sizeof(uint4));  // 512
-    const uint4 *src = host_pool + ((size_t)rh * NB_max + blk) * kVec;
-    uint4 *dst = ws_pool + ((size_t)rh * S + slot) * kVec;
-    const uint4 a = src[threadIdx.x];
-    const uint4 b = src[threadIdx.x + 256];
-    dst[threadIdx.x] = a;
-    dst[threadIdx.x + 256] = b;
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int rh = item / C;
+        const int i = item - rh * C;
+        const int32_t *p = plan + (size_t)rh * row;
+        if (i >= p[0]) continue;
+        const int slot = p[kPlanHead + 2 * i], blk = p[kPlanHead + 2 * i + 1];
+        if (slot < 0 || slot >= S || blk < 0 || blk >= NB_max) continue;
+        const uint4 *src = host_pool + ((size_t)rh * NB_max + blk) * kVec;
+        uint4 *dst = ws_pool + ((size_t)rh * S + slot) * kVec;
+        const uint4 a = src[threadIdx.x];
+        const uint4 b = src[threadIdx.x + 256];
+        dst[threadIdx.x] = a;
+        dst[threadIdx.x + 256] = b;
+    }
+}
+
+// DMA engine, device half: the packed blocks of positions [lo, hi) sit in
+// the device staging buffer in position order; copy each into its slot.
+__global__ __launch_bounds__(256) void stage_scatter_kernel(
+    const int32_t *__restrict__ plan, int row, int C, int n_items, const uint4 *__restrict__ staged,
+    int lo, int hi, uint4 *__restrict__ ws_pool, int S) {
+    constexpr int kVec = (int)(kBlockBytes / sizeof(uint4));
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int rh = item / C;
+        const int i = item - rh * C;
+        const int32_t *p = plan + (size_t)rh * row;
+        if (i >= p[0]) continue;
+        const int k = p[2] + i;
+        if (k < lo || k >= hi) continue;
+        const int slot = p[kPlanHead + 2 * i];
+        if (slot < 0 || slot >= S) continue;
+        const uint4 *src = staged + (size_t)(k - lo) * kVec;
+        uint4 *dst = ws_pool + ((size_t)rh * S + slot) * kVec;
+        const uint4 a = src[threadIdx.x];
+        const uint4 b = src[threadIdx.x + 256];
+        dst[threadIdx.x] = a;
+        dst[threadIdx.x + 256] = b;
+    }
 }
 
 }  // namespace
@@ -281,12 +358,29 @@ hipError_t launch_stage_plan(const oasis_dims &d, const oasis_stage_args &a, hip
     return hipGetLastError();
 }
 
+hipError_t launch_stage_prefix(const oasis_dims &d, const oasis_stage_args &a, hipStream_t s) {
+    hipLaunchKernelGGL(stage_prefix_kernel, dim3(1), dim3(1024), 0, s, a.plan, plan_row(a.C), d.B * d.H_kv);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage_scatter(const oasis_dims &d, const oasis_stage_args &a, int lo, int hi,
+                                hipStream_t s) {
+    if (a.C <= 0 || hi <= lo) return hipSuccess;
+    const int n_items = d.B * d.H_kv * a.C;
+    const int wgs = n_items < 4 * device_cu_count() ? n_items : 4 * device_cu_count();
+    hipLaunchKernelGGL(stage_scatter_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a.plan, plan_row(a.C), a.C,
+                       n_items, reinterpret_cast<const uint4 *>(a.stage_dev), lo, hi,
+                       reinterpret_cast<uint4 *>(a.ws_pool), a.S);
+    return hipGetLastError();
+}
+
 hipError_t launch_stage_gather(const oasis_dims &d, const oasis_stage_args &a,
                                const void *host_pool_dev, hipStream_t s) {
     if (a.C <= 0) return hipSuccess;
-    dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)a.C);
-    hipLaunchKernelGGL(stage_gather_kernel, grid, dim3(256), 0, s, a.plan, plan_row(a.C),
-                       reinterpret_cast<const uint4 *>(host_pool_dev),
+    const int n_items = d.B * d.H_kv * a.C;
+    const int wgs = n_items < kGatherWgs ? n_items : kGatherWgs;
+    hipLaunchKernelGGL(stage_gather_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a.plan, plan_row(a.C), a.C,
+                       n_items, reinterpret_cast<const uint4 *>(host_pool_dev),
                        reinterpret_cast<uint4 *>(a.ws_pool), d.NB_max, a.S);
     return hipGetLastError();
 }

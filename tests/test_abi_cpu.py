@@ -132,8 +132,14 @@ def stage_args(**kw):
     (dict(plan=None), oa.OASIS_EINVAL),
     (dict(host_pool=None), oa.OASIS_EINVAL),
     (dict(plan_bytes=4), oa.OASIS_ENOSPACE),
-    (dict(copy_mode=1, host_plan=None), oa.OASIS_EINVAL),
-    (dict(copy_mode=1, host_plan=16, host_plan_bytes=8), oa.OASIS_ENOSPACE),
+    (dict(copy_mode=1, host_plan=None, stage_host=16, stage_dev=16), oa.OASIS_EINVAL),
+    (dict(copy_mode=1, host_plan=16, stage_host=None, stage_dev=16), oa.OASIS_EINVAL),
+    (dict(copy_mode=1, host_plan=16, stage_host=16, stage_dev=16, host_plan_bytes=8,
+          stage_host_bytes=1 << 20, stage_dev_bytes=1 << 20), oa.OASIS_ENOSPACE),
+    (dict(copy_mode=1, host_plan=16, stage_host=16, stage_dev=16, host_plan_bytes=1 << 20,
+          stage_host_bytes=8191, stage_dev_bytes=1 << 20), oa.OASIS_ENOSPACE),
+    (dict(copy_mode=1, host_plan=16, stage_host=16, stage_dev=16, host_plan_bytes=1 << 20,
+          stage_host_bytes=1 << 20, stage_dev_bytes=1 << 20, host_threads=-1), oa.OASIS_EINVAL),
 ])
 def test_stage_argument_errors(kw, code):
     dd = d()
@@ -142,8 +148,9 @@ def test_stage_argument_errors(kw, code):
     assert oa.oasis_last_error() != ""
 
 
-def test_plan_sizes():
+def test_plan_and_staging_sizes():
     dd = d(B=3, H_kv=2)
-    assert L.oasis_stage_plan_bytes(ctypes.byref(dd), 6) == 4 * 3 * 2 * (2 + 12)
-    assert L.oasis_stage_plan_bytes(ctypes.byref(dd), 0) == 4 * 3 * 2 * 4
-    assert L.oasis_stage_host_plan_bytes(ctypes.byref(dd), 6) == 4 * 3 * 2 * (2 + 12)
+    assert L.oasis_stage_plan_bytes(ctypes.byref(dd), 6) == 4 * (3 * 2 * (4 + 12) + 4)
+    assert L.oasis_stage_plan_bytes(ctypes.byref(dd), 0) == 4 * (3 * 2 * 6 + 4)
+    assert L.oasis_stage_buffer_bytes(ctypes.byref(dd), 7) == 7 * 8192
+    assert oa.oasis_stage_buffer_bytes(3) == 3 * 8192

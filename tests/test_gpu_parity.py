@@ -240,15 +240,19 @@ def gpu_stage_state(slot_block, slot_stamp, NB):
     return stamp
 
 
-@pytest.mark.parametrize("copy_mode", [0, 1])
+@pytest.mark.parametrize("copy_mode,stage_blocks,split", [(0, 0, False), (1, 7, False), (1, 4096, False),
+                                                         (0, 0, True), (1, 64, True)])
 @pytest.mark.parametrize("C,turnover", [(1, 3), (6, 5), (6, 30)])
-def test_stage_matches_oracle(copy_mode, C, turnover):
+def test_stage_matches_oracle(copy_mode, stage_blocks, split, C, turnover):
+    """Both copy engines, through oasis_stage_blocks or its two halves; the
+    DMA engine with a 7-block staging buffer moves every step in rounds."""
     w = wl.Workload("stage", B=3, H_q=8, H_kv=2, ctx=(1500, 3000), budget=512, J=1,
                     structure="none", seed=31)
     K_b, NB, steps = w.K_b, w.NB_max, 6
     S = K_b + C
     ctx_cpu = wl.context_lengths(w)
-    host = wl.kv_pool(w).pin_memory()
+    host = oa().oasis_host_empty((w.B, w.H_kv, NB, 2, w.bs, w.D))
+    host.copy_(wl.kv_pool(w))
     host_np = u16(host)
     sels, nsels, scores = wl.predicted_set_sequence(w, steps, turnover)
     dev = lambda t: t.to(DEV)
@@ -261,26 +265,42 @@ def test_stage_matches_oracle(copy_mode, C, turnover):
     nbytes = oa().oasis_stage_plan_bytes(w.B, w.H_kv, K_b)
     plan = torch.empty(nbytes // 4, dtype=torch.int32, device=DEV)
     host_plan = torch.empty(nbytes // 4, dtype=torch.int32).pin_memory()
+    sbytes = oa().oasis_stage_buffer_bytes(max(stage_blocks, 1))
+    stage_host = [torch.empty(sbytes, dtype=torch.uint8).pin_memory() for _ in range(2)]
+    stage_dev = torch.empty(sbytes, dtype=torch.uint8, device=DEV)
     ctx = dev(ctx_cpu)
+    copy_stream = torch.cuda.Stream()
     st = oracle.StageState(w.B, w.H_kv, NB)
     for s in range(steps):
         Cs = K_b if s == 0 else C
-        oa().oasis_stage_blocks(sel=dev(sels[s]), n_sel=dev(nsels[s]), scores=dev(scores[s]), ctx_len=ctx,
-                                K_b=K_b, C=Cs, step=s, slot_block=slot_block, slot_stamp=slot_stamp,
-                                host_pool=host, ws_pool=ws, tbl_slot=tbl_slot, tbl_block=tbl_block,
-                                tbl_n=tbl_n, plan=plan, host_plan=host_plan, copy_mode=copy_mode)
+        kw = dict(sel=dev(sels[s]), n_sel=dev(nsels[s]), scores=dev(scores[s]), ctx_len=ctx,
+                  K_b=K_b, C=Cs, step=s, slot_block=slot_block, slot_stamp=slot_stamp,
+                  host_pool=host, ws_pool=ws, tbl_slot=tbl_slot, tbl_block=tbl_block,
+                  tbl_n=tbl_n, plan=plan, host_plan=host_plan, stage_host=stage_host[s % 2],
+                  stage_dev=stage_dev, copy_mode=copy_mode)
+        if split:
+            planned = torch.cuda.Event()
+            oa().oasis_stage_plan(plan_event=planned, **kw)
+            oa().oasis_stage_copy(plan_event=planned, copy_stream=copy_stream, **kw)
+        else:
+            oa().oasis_stage_blocks(**kw)
         torch.cuda.synchronize()
         adm, na, ev, ne = oracle.stage(st, sels[s].numpy(), nsels[s].numpy(), scores[s].numpy(),
                                        ctx_cpu.numpy(), w.bs, K_b, Cs, s)
         got = gpu_stage_state(slot_block, slot_stamp, NB)
         np.testing.assert_array_equal(got, st.stamp, err_msg=f"step {s}")
-        p = plan.cpu().numpy()[: w.B * w.H_kv * (2 + 2 * Cs)].reshape(w.B, w.H_kv, 2 + 2 * Cs)
+        row = 4 + 2 * max(Cs, 1)
+        flat = plan.cpu().numpy()
+        p = flat[: w.B * w.H_kv * row].reshape(w.B, w.H_kv, row)
         np.testing.assert_array_equal(p[:, :, 0], na)
         np.testing.assert_array_equal(p[:, :, 1], ne)
+        # packed positions: running total of admits in (r, h) order
+        np.testing.assert_array_equal(p[:, :, 2].ravel(), np.concatenate([[0], np.cumsum(na.ravel())[:-1]]))
+        assert flat[w.B * w.H_kv * row] == na.sum()
         for r in range(w.B):
             for h in range(w.H_kv):
                 k = int(na[r, h])
-                assert p[r, h, 3:3 + 2 * k:2].tolist() == adm[r, h, :k].tolist()
+                assert p[r, h, 5:5 + 2 * k:2].tolist() == adm[r, h, :k].tolist()
         # table lists exactly the held slots; every held slot holds its host block's bytes
         wsn = u16(ws)
         sb = slot_block.cpu().numpy()
@@ -315,6 +335,9 @@ def run_chain_gpu(w, steps, C, copy_mode=0):
              torch.zeros((w.B, w.H_kv), dtype=torch.int32, device=DEV)) for _ in range(2)]
     plan = torch.empty(m.oasis_stage_plan_bytes(w.B, w.H_kv, K_b) // 4, dtype=torch.int32, device=DEV)
     host_plan = torch.empty(plan.numel(), dtype=torch.int32).pin_memory()
+    sbytes = m.oasis_stage_buffer_bytes(w.B * w.H_kv * C)
+    stage_host = torch.empty(sbytes, dtype=torch.uint8).pin_memory()
+    stage_dev = torch.empty(sbytes, dtype=torch.uint8, device=DEV)
     hist = []
     for s in range(steps):
         ql = wl.lookahead(w, s).to(DEV)
@@ -324,7 +347,8 @@ def run_chain_gpu(w, steps, C, copy_mode=0):
         m.oasis_stage_blocks(sel=sel, n_sel=n, scores=sc, ctx_len=ctx, K_b=K_b, C=K_b if s == 0 else C,
                              step=s, slot_block=slot_block, slot_stamp=slot_stamp, host_pool=host,
                              ws_pool=ws, tbl_slot=t[0], tbl_block=t[1], tbl_n=t[2], plan=plan,
-                             host_plan=host_plan, copy_mode=copy_mode)
+                             host_plan=host_plan, stage_host=stage_host, stage_dev=stage_dev,
+                             copy_mode=copy_mode)
         q = wl.attention_query(w, s + 1).to(DEV)
         out = m.oasis_sparse_decode_attn(q, ws, t[0], t[1], t[2], ctx)
         torch.cuda.synchronize()
@@ -373,3 +397,60 @@ def test_chain_end_to_end(name, B, ctx, copy_mode):
         if np.array_equal(gsel, osel):
             np.testing.assert_array_equal(gst, ost, err_msg=f"step {s}")
             assert_attn_close(bf16_to_f64(gout), oout)
+
+
+# ---------------------------------------------------------------- pipelined layers
+
+
+@pytest.mark.parametrize("copy_mode", [0, 1])
+def test_layer_pipeline_matches_oracle(copy_mode):
+    """Three layers in flight on separate streams (the schedule the benchmark
+    times): every layer's attention output at every step equals the oracle
+    chain run serially for that layer."""
+    from prefetch_block_scoring_amd.pipeline import LayerPipeline
+    m = oa()
+    w = wl.WORKLOADS["qwen3_8b_16k_b128_staged"].shrink(B=2, ctx=(3000, 9000))
+    C = oracle.fetch_cap_blocks(w.cap, w.K_b)
+    L, steps = 3, 6
+    ctx_cpu = wl.context_lengths(w)
+    ctx = ctx_cpu.to(DEV)
+    host = m.oasis_host_empty((w.B, w.H_kv, w.NB_max, 2, w.bs, w.D))
+    host.copy_(wl.kv_pool(w))
+    summ = m.oasis_build_summaries(host, ctx)
+    looks = [wl.lookahead(w, s).to(DEV) for s in range(steps + 2 * L)]
+    attn_q = [looks[max(s - 1, 0)][:, 0].contiguous() for s in range(steps + 2 * L)]
+    pipe = LayerPipeline(pool=host, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=True,
+                         copy_mode=copy_mode, host_threads=4)
+    outs = {}
+    for t in range(steps):
+        for l in range(L):
+            s = t + 2 * l
+            pipe.layer_step(l, t, looks[s], attn_q[s])
+            if t >= 1:
+                # stream-ordered snapshot on the main stream: no host wait, so
+                # the compute and copy streams keep running ahead as they would
+                with torch.cuda.stream(pipe.main):
+                    outs[(l, t)] = pipe.layers[l].out.clone()
+    pipe.close()
+    torch.cuda.synchronize()
+    outs = {k: u16(v) for k, v in outs.items()}
+    # oracle: per layer, the serial chain with the same lookahead phase
+    ctx_np = ctx_cpu.numpy()
+    kv = u16(host)
+    summ_o = oracle.build_summaries(kv, ctx_np, w.bs)
+    for l in range(L):
+        st = oracle.StageState(w.B, w.H_kv, w.NB_max)
+        for t in range(steps - 1):
+            s = t + 2 * l
+            sc = oracle.score(u16(looks[s]), summ_o, ctx_np, w.bs, w.H_kv)
+            sel, n = oracle.select(sc, ctx_np, w.bs, w.K_b)
+            oracle.stage(st, sel, n, sc, ctx_np, w.bs, w.K_b, w.K_b if t == 0 else C, t)
+            blocks = np.full((w.B, w.H_kv, w.K_b), -1, dtype=np.int32)
+            nb = np.zeros((w.B, w.H_kv), dtype=np.int32)
+            for r in range(w.B):
+                for h in range(w.H_kv):
+                    res = st.resident(r, h)
+                    blocks[r, h, :len(res)] = res
+                    nb[r, h] = len(res)
+            ref, _ = oracle.attend(u16(attn_q[s + 1]), kv, ctx_np, blocks, nb, 1 / math.sqrt(w.D))
+            assert_attn_close(bf16_to_f64(outs[(l, t + 1)]), ref)
