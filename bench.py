@@ -56,6 +56,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--check", action="store_true",
                    help="after timing, compare sampled requests of the last step against the oracle")
+    p.add_argument("--summarize-profile", nargs="+", metavar="DIR",
+                   help="summarize rocprofv3 CSV output directories (kernel stats, FETCH_SIZE and "
+                        "WRITE_SIZE runs) instead of benchmarking")
+    p.add_argument("--command", default="", help="with --summarize-profile: the profiled command line")
     return p.parse_args()
 
 
@@ -63,8 +67,105 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = {"attn_kernel": "attn.hip", "score_kernel": "score.hip", "topk_kernel": "topk.hip",
+                  "stage_gather_kernel": "stage.hip", "stage_plan_kernel": "stage.hip"}
+CALIB_BYTES = 256 << 20
+
+
+def _source_hash(name):
+    import hashlib
+    path = os.path.join(ROOT, "prefetch_block_scoring_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _short(name):
+    import re
+    m = re.search(r"oasis::\(anonymous namespace\)::([A-Za-z_0-9]+(<[^>]*>)?)", name)
+    if m:
+        return m.group(1)
+    return name.split("(")[0][-60:]
+
+
+def summarize_profile(dirs, command):
+    """Reduce rocprofv3 CSV output to a short text summary: per-kernel call
+    counts and durations, and, from FETCH_SIZE / WRITE_SIZE runs, HBM bytes
+    per dispatch scaled by what the same counters read for the plain
+    CALIB_BYTES device copy that bench.py runs after its timed steps."""
+    import csv
+    import glob
+    import statistics
+    out = [f"command: {command}"] if command else []
+    machine = {}
+    for d in dirs:
+        for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+            rows = list(csv.DictReader(open(path)))
+            out.append(f"kernel stats ({os.path.basename(path)}):")
+            out.append(f"  {'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+            for r in rows:
+                n = _short(r["Name"])
+                if "oasis" not in r["Name"] and float(r.get("Percentage", 0) or 0) < 1.0:
+                    continue
+                out.append(f"  {n:40s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
+                           f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+                if "oasis" in r["Name"]:
+                    machine.setdefault(_short(r["Name"]), {})["avg_us"] = float(r["AverageNs"]) / 1e3
+        for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            rows = list(csv.DictReader(open(path)))
+            if not rows:
+                continue
+            counter = rows[0]["Counter_Name"]
+            per = {}
+            for r in rows:
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            copies = [(max(v), k) for k, v in per.items() if "copy" in k.lower()]
+            calib_kib = max(copies)[0] if copies else None
+            factor = calib_kib / (CALIB_BYTES / 1024) if calib_kib else None
+            out.append(f"{counter} ({os.path.basename(path)}): calibration copy of {CALIB_BYTES >> 20} MiB reads "
+                       f"{calib_kib} KiB -> scale {factor}")
+            for k, v in per.items():
+                if "oasis" not in k:
+                    continue
+                kib = statistics.mean(v)
+                byt = kib * 1024 / factor if factor else None
+                out.append(f"  {_short(k):40s} dispatches {len(v):4d} mean {kib:12.1f} KiB -> "
+                           f"{byt / 1e6 if byt else float('nan'):10.2f} MB per dispatch (calibrated)")
+                machine.setdefault(_short(k), {})[counter] = byt
+    for k, v in machine.items():
+        for src_key, fname in KERNEL_SOURCES.items():
+            if k.endswith(src_key) or src_key in k:
+                v["source"] = fname
+                v["source_sha256_16"] = _source_hash(fname)
+    out.append("machine-readable: " + json.dumps(machine, sort_keys=True))
+    print("\n".join(out))
+
+
+def profiled_traffic(kernel_key, profile_file):
+    """HBM bytes per dispatch of a kernel from a committed profile summary,
+    or None when the summary is missing or the kernel's source has changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", profile_file)
+    try:
+        for line in open(path):
+            if line.startswith("machine-readable: "):
+                data = json.loads(line[len("machine-readable: "):])
+                break
+        else:
+            return None
+    except OSError:
+        return None
+    for k, v in data.items():
+        if kernel_key in k and "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+            if v.get("source_sha256_16") != _source_hash(KERNEL_SOURCES[kernel_key]):
+                return None
+            return int(v["FETCH_SIZE"] + v["WRITE_SIZE"])
+    return None
+
+
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by request and KV head with no exchange, see DESIGN.md", file=sys.stderr)
@@ -203,13 +304,22 @@ def main():
     a_us = kern["attn"]["avg_us"]
     achieved = attn_bytes / (a_us * 1e-6) / 1e9
     roofline = {"kernel": "sparse_attn", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": profiled_traffic("attn_kernel", f"attn_traffic_{w.name}.txt"),
                 "bytes_per_launch": attn_bytes, "avg_launch_us": a_us}
     hbm_us = sum(kern[k]["avg_us"] for k in ("attn", "score", "topk"))
     hbm_bytes = attn_bytes + score_bytes + topk_bytes
     kern["hbm_kernels_total"] = {"avg_us": round(hbm_us, 2), "bytes": hbm_bytes,
                                  "GBps": round(hbm_bytes / (hbm_us * 1e-6) / 1e9, 1),
                                  "frac_of_peak": round(hbm_bytes / (hbm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # a plain 256 MiB device copy after the timed steps: the reference that
+    # hardware traffic counters of a profiled run are scaled by
+    calib_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     if args.check:
         check_against_oracle(w, pool, ctx_cpu, q_attn, pipe, n_steps)
