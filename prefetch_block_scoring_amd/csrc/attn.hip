@@ -56,9 +56,18 @@ struct AttnArgs {
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // GP: head slots compiled in (a power of two >= G); G = H_q / H_kv at run time.
+// Waves per SIMD the kernel is compiled for: four for up to four heads per
+// group (1024 workgroups of the 8-KV-head layers at batch 128 then fit the
+// 256 compute units in one round); the larger head counts need the registers.
 template <int GP>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+constexpr int attn_waves_per_simd() { return GP <= 4 ? 4 : (GP <= 8 ? 2 : 1); }
+
+template <int GP>
+__global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kernel(AttnArgs a) {
     __shared__ float p_lds[kWaves][17][16];  // per wave: p[token][head]; row 16 = rescale
+    // Q^T in the MFMA B layout, one 16-byte chunk per (head slot, 8 dims);
+    // rows padded by 16 bytes so the 16 head slots fall in distinct banks
+    __shared__ uint4 q_lds[16][17];
     __shared__ float m_lds[kWaves][16];
     __shared__ float l_lds[kWaves][16];
     __shared__ float o_lds[kWaves][GP][kD];
@@ -83,17 +92,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int i1 = min(n, i0 + per);
 
     // Q^T as the MFMA B operand: lane (col, grp) brings head `col`, dims
-    // kk * 32 + grp * 8 + [0, 8) for k-step kk.
-    bf16x8 qb[4];
-    if (col < G) {
-        const uint4 *qrow = reinterpret_cast<const uint4 *>(
-            a.q + ((size_t)r * a.H_q + (size_t)h * G + col) * kD);
-#pragma unroll
-        for (int kk = 0; kk < 4; kk++) qb[kk] = __builtin_bit_cast(bf16x8, qrow[kk * 4 + grp]);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; kk++) qb[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    // kk * 32 + grp * 8 + [0, 8) for k-step kk; staged once in LDS (head
+    // slots past G are zero) and read back per block, which keeps registers
+    // for the loads in flight.
+    {
+        const int hs = tid >> 4, chunk = tid & 15;  // 256 threads = 16 head slots x 16 chunks
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (hs < G)
+            v = reinterpret_cast<const uint4 *>(a.q + ((size_t)r * a.H_q + (size_t)h * G + hs) * kD)[chunk];
+        q_lds[hs][chunk] = v;
     }
+    __syncthreads();
 
     float acc[GP][8];
 #pragma unroll
@@ -149,7 +158,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; kk++)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[kk]), qb[kk], c,
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[kk]),
+                                                         __builtin_bit_cast(bf16x8, q_lds[col][kk * 4 + grp]), c,
                                                          0, 0, 0);
         const int valid = ctx - blk_c * kBs;
         float sv[4];
