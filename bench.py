@@ -305,7 +305,7 @@ def main():
     achieved = attn_bytes / (a_us * 1e-6) / 1e9
     roofline = {"kernel": "sparse_attn", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": profiled_traffic("attn_kernel", f"attn_traffic_{w.name}.txt"),
+                "traffic": profiled_traffic("attn_kernel", f"traffic_attn_score_{w.name}.txt"),
                 "bytes_per_launch": attn_bytes, "avg_launch_us": a_us}
     hbm_us = sum(kern[k]["avg_us"] for k in ("attn", "score", "topk"))
     hbm_bytes = attn_bytes + score_bytes + topk_bytes

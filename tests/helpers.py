@@ -55,3 +55,29 @@ def assert_attn_close(out_gpu: np.ndarray, ref: np.ndarray, atol=2e-3, rtol=1e-2
     lim = atol + rtol * np.abs(ref)
     bad = err > lim
     assert not bad.any(), f"{bad.sum()} of {bad.size} outputs out of tolerance; worst excess {np.max(err - lim):.3g}"
+
+
+def gpu_stage_state(slot_block, slot_stamp, NB):
+    """Per-block stamps (-1 = not resident) from the GPU's slot arrays, in the
+    oracle's layout; checks that no block is held by two slots."""
+    sb = slot_block.cpu().numpy() if isinstance(slot_block, torch.Tensor) else slot_block
+    st = slot_stamp.cpu().numpy() if isinstance(slot_stamp, torch.Tensor) else slot_stamp
+    B, H, S = sb.shape
+    stamp = np.full((B, H, NB), -1, dtype=np.int32)
+    for r in range(B):
+        for h in range(H):
+            held = sb[r, h][sb[r, h] >= 0]
+            assert len(set(held.tolist())) == len(held), "a block is held by two slots"
+            for s in range(S):
+                if sb[r, h, s] >= 0:
+                    stamp[r, h, sb[r, h, s]] = st[r, h, s]
+    return stamp
+
+
+def selection_equal_pairs(sel_g, n_g, sel_o, n_o):
+    """Boolean [B][H_kv]: the two selections are identical for that pair."""
+    out = np.zeros(n_o.shape, dtype=bool)
+    for idx in np.ndindex(*n_o.shape):
+        k = int(n_o[idx])
+        out[idx] = int(n_g[idx]) == k and np.array_equal(sel_g[idx][:k], sel_o[idx][:k])
+    return out

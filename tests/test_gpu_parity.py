@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads as wl
 from helpers import (assert_attn_close, assert_scores_close, assert_selection_matches,
-                     bf16_to_f64, n_blocks, u16)
+                     bf16_to_f64, gpu_stage_state, n_blocks, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -223,21 +223,6 @@ def test_attention_budget_equal_to_context_is_dense():
 
 
 # ---------------------------------------------------------------- staging
-
-
-def gpu_stage_state(slot_block, slot_stamp, NB):
-    sb = slot_block.cpu().numpy()
-    st = slot_stamp.cpu().numpy()
-    B, H, S = sb.shape
-    stamp = np.full((B, H, NB), -1, dtype=np.int32)
-    for r in range(B):
-        for h in range(H):
-            held = sb[r, h][sb[r, h] >= 0]
-            assert len(set(held.tolist())) == len(held), "a block is held by two slots"
-            for s in range(S):
-                if sb[r, h, s] >= 0:
-                    stamp[r, h, sb[r, h, s]] = st[r, h, s]
-    return stamp
 
 
 @pytest.mark.parametrize("copy_mode,stage_blocks,split", [(0, 0, False), (1, 7, False), (1, 4096, False),
