@@ -204,23 +204,9 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t_setup:.1f}s")
 
-    timers = {k: [] for k in ("attn", "score", "topk", "plan")}
-    timing = [False]
-
-    def timer(name, stream, fn):
-        if not timing[0]:
-            fn()
-            return
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        fn()
-        b.record(stream)
-        timers[name].append((a, b))
-
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
     pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=H_q, K_b=K_b, C=C, n_layers=L, staged=staged,
-                         copy_mode=copy_mode, host_threads=args.host_threads, n_split=args.n_split,
-                         timer=timer)
+                         copy_mode=copy_mode, host_threads=args.host_threads, n_split=args.n_split, J=w.J)
     T = K_b
     splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
     admitted = torch.zeros((), dtype=torch.int64, device=dev)
@@ -241,21 +227,23 @@ def main():
     run(0, 1 + args.warmup, counting=True)
     pipe.drain()
     torch.cuda.synchronize()
-    pipe.copy_host_s.clear()
-    timing[0] = True
+    # events around every launch of the timed steps, on the launch's stream
+    pipe.enable_timing(args.steps * L)
     t0 = time.perf_counter()
     run(1 + args.warmup, n_steps)
+    issued = time.perf_counter() - t0
     pipe.drain()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    timing[0] = False
     layer_steps = args.steps * L
     ms_per_step = elapsed / layer_steps * 1e3
     value = B * layer_steps / elapsed
 
     def avg_us(name):
-        xs = timers[name]
-        return sum(a.elapsed_time(b) for a, b in xs) / max(len(xs), 1) * 1e3
+        us, n = pipe.timing(name)
+        if n != args.steps * L:
+            raise SystemExit(f"timing of {name}: {n} launches recorded, {args.steps * L} expected")
+        return us
 
     # algorithmic bytes per launch
     if staged:
@@ -275,7 +263,8 @@ def main():
     h2d = None
     if staged:
         kern["plan"] = {"avg_us": round(avg_us("plan"), 2), "note": "plan and prefix kernels"}
-        kern["copy_host"] = {"avg_us": round(sum(pipe.copy_host_s) / max(len(pipe.copy_host_s), 1) * 1e6, 2),
+        copy_s, copy_n = pipe.copy_host_seconds()
+        kern["copy_host"] = {"avg_us": round(copy_s / max(copy_n, 1) * 1e6, 2),
                               "note": ("host time of a staging call: plan read-back and packing up to the "
                                        "copy's enqueue") if copy_mode == oa.OASIS_COPY_DMA
                               else "host time of a staging call (enqueue only)"}
@@ -346,6 +335,7 @@ def main():
         "cpu_baseline": cpu,
         "h2d": h2d,
         "kernels": kern,
+        "host_issue_ms_per_step": round(issued / layer_steps * 1e3, 4),
     }
     print(json.dumps(line), flush=True)
 

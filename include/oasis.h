@@ -304,6 +304,125 @@ int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q,
                              void *ws, size_t ws_bytes, int32_t n_split,
                              void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Layer pipeline: the per-layer decode chain, scheduled in native code.
+ *
+ * Section 4 of the paperlayer summary runs, per layer, a background chain of
+ * prediction (scores and top-K), selection (the staging plan) and transfer,
+ * overlapped across layers and decode steps; the foreground waits only for a
+ * layer's own transfer before that layer's next-step attention.  A pipeline
+ * enqueues one layer-step of that schedule per call, every launch, event
+ * record and stream wait made from native code:
+ *
+ *   main stream (the caller's)   attention of (l, t) over the working set
+ *                                staged at (l, t - 1)
+ *   compute stream (owned)       scores and top-K of (l, t), staging plan
+ *   copy stream (owned)          the copies of (l, t)
+ *
+ * Per layer the buffers rotate: the attention of step t reads table t % 3,
+ * the plan of step t writes table (t + 1) % 3 and uses selection and plan
+ * buffer t % 2.  So the plan of step t waits for the attention and the copies
+ * of step t - 2, and the copies of step t wait for the attention of step
+ * t - 1, whose slots they may refill.  Unstaged pipelines (K/V in HBM)
+ * attend at step t over the selection of step t - 1 in the full pool.  With
+ * OASIS_COPY_DMA the copy half, which blocks on host packing, runs on one
+ * worker thread owned by the pipeline, in submission order; with
+ * OASIS_COPY_KERNEL it is enqueued by the calling thread.  Streams are
+ * created at default priority; the pipeline allocates no device memory.
+ * --------------------------------------------------------------------------- */
+
+/* Caller-owned buffers of one layer; they must outlive the pipeline. */
+typedef struct oasis_layer_buffers {
+    float *scores;            /* [B][H_kv][NB_max] fp32, device */
+    int32_t *sel[2];          /* [B][H_kv][K_b] int32, device */
+    int32_t *n_sel[2];        /* [B][H_kv] int32, device */
+    void *attn_ws;            /* oasis_attn_workspace_bytes(dims, K_b, n_split) */
+    size_t attn_ws_bytes;
+    /* staged pipelines only (ignored otherwise) */
+    uint16_t *ws_pool;        /* [B][H_kv][K_b + C][2][bs][D] bf16, device */
+    int32_t *slot_block;      /* [B][H_kv][K_b + C] int32, device, all -1 */
+    int32_t *slot_stamp;      /* [B][H_kv][K_b + C] int32, device, all -1 */
+    int32_t *tbl_slot[3];     /* [B][H_kv][K_b] int32, device */
+    int32_t *tbl_block[3];    /* [B][H_kv][K_b] int32, device */
+    int32_t *tbl_n[3];        /* [B][H_kv] int32, device */
+    int32_t *plan[2];         /* device, plan_bytes each */
+    size_t plan_bytes;        /* >= oasis_stage_plan_bytes(dims, K_b) */
+    void *host_plan;          /* pinned host, plan_bytes; DMA only */
+    void *stage_host[2];      /* pinned host staging buffers; DMA only */
+    void *stage_dev;          /* device staging buffer; DMA only */
+    size_t stage_bytes;       /* bytes of each staging buffer; DMA only */
+} oasis_layer_buffers;
+
+typedef struct oasis_pipeline_desc {
+    int32_t n_layers;         /* 1 .. 1024 */
+    int32_t K_b;              /* budget in blocks per (r, h) */
+    int32_t C;                /* fetch cap in blocks per (r, h) per step
+                                 (staged; step 0 fills uncapped) */
+    int32_t J;                /* lookahead queries per request */
+    int32_t staged;           /* 1: pool is pinned host memory staged into
+                                 per-layer working sets; 0: pool in HBM */
+    int32_t copy_mode;        /* OASIS_COPY_KERNEL or OASIS_COPY_DMA */
+    int32_t host_threads;     /* DMA packing threads (0 = 8) */
+    int32_t n_split;          /* attention split count (0 = automatic) */
+    float sm_scale;           /* attention scale, e.g. 1 / sqrt(D) */
+    const uint16_t *pool;     /* [B][H_kv][NB_max][2][bs][D] bf16 */
+    const uint16_t *kminmax;  /* [B][H_kv][NB_max][2][D] summaries, device */
+    const int32_t *ctx_len;   /* [B] int32, device */
+    void *main_stream;        /* attention stream (hipStream_t; NULL = null
+                                 stream) */
+    const oasis_layer_buffers *layers;  /* n_layers entries, copied */
+} oasis_pipeline_desc;
+
+typedef struct oasis_pipeline oasis_pipeline;
+
+/* Checks the description, creates the compute and copy streams, the events
+ * and (DMA) the worker thread; *out receives the handle. */
+int oasis_pipeline_create(const oasis_dims *dims,
+                          const oasis_pipeline_desc *desc,
+                          oasis_pipeline **out);
+
+/* Enqueues layer `layer`'s work of decode step `step`: the attention of
+ * step t (query q_attn [B][H_q][D] bf16, device; output out [B][H_q][D] bf16
+ * and lse [B][H_q] fp32 (may be NULL), device; skipped at t = 0 where
+ * q_attn and out may be NULL) and the prediction and staging for step t + 1
+ * from q_look [B][J][H_q][D] bf16, device.  Steps of one layer must be
+ * issued in order 0, 1, 2, ... (OASIS_EINVAL otherwise); layers may
+ * interleave freely.  Inputs must stay valid until the work completes.
+ * Blocks the caller only while the DMA worker has not yet enqueued the
+ * copies of (layer, step - 1).  An error of the DMA worker is returned by
+ * the next call. */
+int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t layer, int32_t step,
+                              const uint16_t *q_look, const uint16_t *q_attn,
+                              uint16_t *out, float *lse);
+
+/* Waits until the DMA worker has enqueued every submitted copy (no device
+ * synchronisation). */
+int oasis_pipeline_drain(oasis_pipeline *p);
+
+/* The pipeline's streams: which = 0 main, 1 compute, 2 copy (NULL when
+ * unstaged). */
+int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
+
+/* Event timing of the steps: capacity > 0 (re)arms timing of up to
+ * `capacity` launches per kind and clears the totals; 0 disables it.
+ * Kinds: 0 attention (main stream), 1 scores, 2 top-K, 3 staging plan
+ * (compute stream); each interval starts once the stream's earlier waits are
+ * satisfied.  timing_read synchronises on the recorded events and returns
+ * their total milliseconds and count. */
+int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity);
+int oasis_pipeline_timing_read(oasis_pipeline *p, int32_t kind,
+                               double *total_ms, int32_t *count);
+
+/* Host seconds spent in the copy half of staging (plan read-back and packing
+ * with OASIS_COPY_DMA, the enqueue with OASIS_COPY_KERNEL) since timing was
+ * last armed, and the number of calls. */
+int oasis_pipeline_copy_host_seconds(oasis_pipeline *p, double *seconds,
+                                     int32_t *calls);
+
+/* Drains, synchronises the pipeline's streams and the main stream, and
+ * frees the streams, events and worker.  NULL is accepted. */
+int oasis_pipeline_destroy(oasis_pipeline *p);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,21 @@ class oasis_stage_args(ctypes.Structure):
         ("done_event", _P), ("plan_event", _P)]
 
 
+class oasis_layer_buffers(ctypes.Structure):
+    _fields_ = [
+        ("scores", _P), ("sel", _P * 2), ("n_sel", _P * 2), ("attn_ws", _P), ("attn_ws_bytes", ctypes.c_size_t),
+        ("ws_pool", _P), ("slot_block", _P), ("slot_stamp", _P), ("tbl_slot", _P * 3), ("tbl_block", _P * 3),
+        ("tbl_n", _P * 3), ("plan", _P * 2), ("plan_bytes", ctypes.c_size_t), ("host_plan", _P),
+        ("stage_host", _P * 2), ("stage_dev", _P), ("stage_bytes", ctypes.c_size_t)]
+
+
+class oasis_pipeline_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", _I32), ("K_b", _I32), ("C", _I32), ("J", _I32), ("staged", _I32), ("copy_mode", _I32),
+        ("host_threads", _I32), ("n_split", _I32), ("sm_scale", ctypes.c_float), ("pool", _P),
+        ("kminmax", _P), ("ctx_len", _P), ("main_stream", _P), ("layers", ctypes.POINTER(oasis_layer_buffers))]
+
+
 # name -> (restype, argtypes)
 _SIGNATURES = {
     "oasis_version": (ctypes.c_char_p, []),
@@ -74,6 +89,17 @@ _SIGNATURES = {
     "oasis_sparse_decode_attn": (ctypes.c_int, [
         ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
         ctypes.c_size_t, _I32, _P]),
+    "oasis_pipeline_create": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_pipeline_desc),
+                                             ctypes.POINTER(ctypes.c_void_p)]),
+    "oasis_pipeline_layer_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P]),
+    "oasis_pipeline_drain": (ctypes.c_int, [_P]),
+    "oasis_pipeline_stream": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_void_p)]),
+    "oasis_pipeline_timing": (ctypes.c_int, [_P, _I32]),
+    "oasis_pipeline_timing_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
+                                                  ctypes.POINTER(_I32)]),
+    "oasis_pipeline_copy_host_seconds": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_double),
+                                                        ctypes.POINTER(_I32)]),
+    "oasis_pipeline_destroy": (ctypes.c_int, [_P]),
 }
 
 
@@ -353,3 +379,59 @@ def oasis_sparse_decode_attn(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: t
         int(T), _ptr(ctx_len), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), int(n_split), _stream(stream)))
     return (out, lse) if want_lse or lse is not None else out
+
+
+# -------------------------------------------------------------------------- layer pipeline
+
+
+def oasis_pipeline_create(d: oasis_dims, desc: oasis_pipeline_desc) -> int:
+    """Creates a native layer pipeline (include/oasis.h); returns its handle."""
+    h = ctypes.c_void_p()
+    _check(_lib.oasis_pipeline_create(ctypes.byref(d), ctypes.byref(desc), ctypes.byref(h)))
+    return h.value
+
+
+def oasis_pipeline_layer_step(h: int, layer: int, step: int, q_look: torch.Tensor,
+                              q_attn: Optional[torch.Tensor], out: Optional[torch.Tensor],
+                              lse: Optional[torch.Tensor] = None):
+    """One layer-step: q_look bf16 [B][J][H_q][D], q_attn bf16 [B][H_q][D]
+    (unused at step 0), out bf16 [B][H_q][D], lse fp32 [B][H_q] or None."""
+    _need(q_look, "q_look", torch.bfloat16, 4)
+    if q_attn is not None:
+        _need(q_attn, "q_attn", torch.bfloat16, 3)
+    _check(_lib.oasis_pipeline_layer_step(h, int(layer), int(step), q_look.data_ptr(),
+                                          None if q_attn is None else q_attn.data_ptr(),
+                                          None if out is None else out.data_ptr(),
+                                          None if lse is None else lse.data_ptr()))
+
+
+def oasis_pipeline_drain(h: int):
+    _check(_lib.oasis_pipeline_drain(h))
+
+
+def oasis_pipeline_stream(h: int, which: int) -> Optional[int]:
+    s = ctypes.c_void_p()
+    _check(_lib.oasis_pipeline_stream(h, int(which), ctypes.byref(s)))
+    return s.value
+
+
+def oasis_pipeline_timing(h: int, capacity: int):
+    _check(_lib.oasis_pipeline_timing(h, int(capacity)))
+
+
+def oasis_pipeline_timing_read(h: int, kind: int):
+    """(total milliseconds, count) of the timed launches of one kind."""
+    ms, n = ctypes.c_double(), _I32()
+    _check(_lib.oasis_pipeline_timing_read(h, int(kind), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def oasis_pipeline_copy_host_seconds(h: int):
+    sec, n = ctypes.c_double(), _I32()
+    _check(_lib.oasis_pipeline_copy_host_seconds(h, ctypes.byref(sec), ctypes.byref(n)))
+    return sec.value, n.value
+
+
+def oasis_pipeline_destroy(h: Optional[int]):
+    if h:
+        _check(_lib.oasis_pipeline_destroy(h))

@@ -88,8 +88,8 @@ using namespace oasis;
         if ((ptr) == nullptr) FAIL(OASIS_EINVAL, "%s is NULL", #ptr);     \
     } while (0)
 
-// Common shape checks.  needs_nb: the call indexes [0, NB_max) arrays.
-static int check_dims(const oasis_dims *d) {
+// Common shape checks of every call.
+int oasis::check_dims(const oasis_dims *d) {
     if (!d) FAIL(OASIS_EINVAL, "dims is NULL");
     if (d->B < 0) FAIL(OASIS_EINVAL, "B = %d < 0", d->B);
     if (d->H_q < 1 || d->H_kv < 1) FAIL(OASIS_EINVAL, "H_q = %d, H_kv = %d must be >= 1", d->H_q, d->H_kv);

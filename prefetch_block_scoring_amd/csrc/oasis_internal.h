@@ -20,6 +20,9 @@ void clear_error();
 // is not hipSuccess.
 int hip_check(hipError_t e, const char *what);
 
+// Shape checks shared by every entry point (sets the error message).
+int check_dims(const oasis_dims *d);
+
 #define OASIS_HIP(call)                                   \
     do {                                                  \
         int _rc = ::oasis::hip_check((call), #call);      \

@@ -1,0 +1,456 @@
+// Native scheduler of the per-layer decode chain (oasis_pipeline_*).
+//
+// OasisKV (arXiv 2608.08097), paperlayer summary, section 4: per layer, a
+// background chain of top-K prediction, KV selection and KV transfer runs on
+// independent workers overlapped across layers and decode steps; the
+// foreground waits only for the relevant layer's transfer before that
+// layer's next-step attention.  One call here enqueues one layer-step of that
+// schedule through the library's own entry points, so a decode step costs a
+// few microseconds of host time per layer instead of a round of interpreter
+// calls per launch.  The dependency rules are stated in include/oasis.h.
+#include "oasis_internal.h"
+
+#include <chrono>
+#include <condition_variable>
+#include <cstdio>
+#include <deque>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+namespace oasis {
+namespace {
+
+enum EvKind { kEvAttn = 0, kEvSel, kEvPlan, kEvStage, kEvKinds };
+// Events of (kind, layer, step) are reused every kRing steps.  An event of
+// step t is waited on by work issued no later than step t + 2 (and, with the
+// DMA worker, before the caller moves on to step t + 2), so a ring of four
+// never re-records an event that a wait still has to be issued for.
+constexpr int kRing = 4;
+constexpr int kTimedKinds = 4;
+
+struct Job {
+    int layer = 0, step = 0;
+    oasis_stage_args args{};
+};
+
+}  // namespace
+}  // namespace oasis
+
+using namespace oasis;
+
+struct oasis_pipeline {
+    oasis_dims d{};
+    oasis_pipeline_desc desc{};
+    std::vector<oasis_layer_buffers> layers;
+    std::vector<int> next_step;  // per layer: the step the next call must issue
+    int device = 0;
+    int S = 0;
+    hipStream_t main = nullptr, comp = nullptr, copy = nullptr;
+    std::vector<hipEvent_t> ev;  // [kind][layer][kRing]
+
+    // timing
+    int t_cap = 0;
+    std::vector<hipEvent_t> t_ev[kTimedKinds];  // 2 * t_cap each
+    int t_n[kTimedKinds] = {0, 0, 0, 0};
+    double copy_host_s = 0.0;
+    int copy_calls = 0;
+    std::mutex t_mu;  // copy-host totals (written by the worker)
+
+    // DMA worker
+    std::thread worker;
+    std::mutex mu;
+    std::condition_variable cv_job, cv_done;
+    std::deque<Job> jobs;
+    std::vector<long> done;  // per layer: last step whose copies are enqueued
+    bool stop = false;
+    int err = OASIS_OK;
+    std::string err_msg;
+
+    hipEvent_t event(int kind, int l, int t) const {
+        return ev[((size_t)kind * desc.n_layers + l) * kRing + (t % kRing)];
+    }
+};
+
+namespace {
+
+#define PFAIL(code, ...)                                  \
+    do {                                                  \
+        char _buf[512];                                   \
+        snprintf(_buf, sizeof _buf, __VA_ARGS__);         \
+        set_error(_buf);                                  \
+        return (code);                                    \
+    } while (0)
+
+void timed_begin(oasis_pipeline *p, int kind, hipStream_t s) {
+    if (p->t_n[kind] < p->t_cap) (void)hipEventRecord(p->t_ev[kind][2 * p->t_n[kind]], s);
+}
+
+void timed_end(oasis_pipeline *p, int kind, hipStream_t s) {
+    if (p->t_n[kind] < p->t_cap) {
+        (void)hipEventRecord(p->t_ev[kind][2 * p->t_n[kind] + 1], s);
+        p->t_n[kind]++;
+    }
+}
+
+// The copy half of staging for one job; called by the calling thread
+// (kernel copies) or by the worker (DMA).
+int run_copy(oasis_pipeline *p, const Job &j) {
+    const auto h0 = std::chrono::steady_clock::now();
+    const int rc = oasis_stage_copy(&p->d, &j.args);
+    const double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - h0).count();
+    std::lock_guard<std::mutex> lk(p->t_mu);
+    p->copy_host_s += dt;
+    p->copy_calls++;
+    return rc;
+}
+
+void worker_loop(oasis_pipeline *p) {
+    (void)hipSetDevice(p->device);
+    for (;;) {
+        Job j;
+        {
+            std::unique_lock<std::mutex> lk(p->mu);
+            p->cv_job.wait(lk, [&] { return p->stop || !p->jobs.empty(); });
+            if (p->jobs.empty()) return;
+            j = p->jobs.front();
+        }
+        int rc = OASIS_OK;
+        std::string msg;
+        {
+            std::lock_guard<std::mutex> lk(p->mu);
+            rc = p->err;  // after an error, later copies are not issued
+        }
+        if (rc == OASIS_OK) {
+            rc = run_copy(p, j);
+            if (rc != OASIS_OK) msg = oasis_last_error();
+        }
+        {
+            std::lock_guard<std::mutex> lk(p->mu);
+            p->jobs.pop_front();
+            if (rc != OASIS_OK && p->err == OASIS_OK) {
+                p->err = rc;
+                p->err_msg = "staging copy of layer " + std::to_string(j.layer) + " step " +
+                             std::to_string(j.step) + ": " + msg;
+            }
+            p->done[j.layer] = j.step;
+        }
+        p->cv_done.notify_all();
+    }
+}
+
+int worker_error(oasis_pipeline *p) {
+    std::lock_guard<std::mutex> lk(p->mu);
+    if (p->err != OASIS_OK) set_error(p->err_msg);
+    return p->err;
+}
+
+int check_layer(const oasis_pipeline_desc &ds, const oasis_layer_buffers &b, int l, size_t plan_need,
+                size_t ws_need) {
+#define LNEED(ptr)                                                                   \
+    do {                                                                             \
+        if ((ptr) == nullptr) PFAIL(OASIS_EINVAL, "layer %d: %s is NULL", l, #ptr);  \
+    } while (0)
+    LNEED(b.scores);
+    for (int k = 0; k < 2; k++) {
+        LNEED(b.sel[k]);
+        LNEED(b.n_sel[k]);
+    }
+    if (ws_need > 0) {
+        LNEED(b.attn_ws);
+        if (b.attn_ws_bytes < ws_need)
+            PFAIL(OASIS_ENOSPACE, "layer %d: attention workspace %zu bytes < %zu", l, b.attn_ws_bytes, ws_need);
+    }
+    if (!ds.staged) return OASIS_OK;
+    LNEED(b.ws_pool);
+    LNEED(b.slot_block);
+    LNEED(b.slot_stamp);
+    for (int k = 0; k < 3; k++) {
+        LNEED(b.tbl_slot[k]);
+        LNEED(b.tbl_block[k]);
+        LNEED(b.tbl_n[k]);
+    }
+    for (int k = 0; k < 2; k++) LNEED(b.plan[k]);
+    if (b.plan_bytes < plan_need)
+        PFAIL(OASIS_ENOSPACE, "layer %d: plan buffers %zu bytes < %zu", l, b.plan_bytes, plan_need);
+    if (ds.copy_mode == OASIS_COPY_DMA) {
+        LNEED(b.host_plan);
+        LNEED(b.stage_host[0]);
+        LNEED(b.stage_host[1]);
+        LNEED(b.stage_dev);
+        if (b.stage_bytes < kBlockBytes)
+            PFAIL(OASIS_ENOSPACE, "layer %d: staging buffers of %zu bytes hold no block", l, b.stage_bytes);
+    }
+    return OASIS_OK;
+#undef LNEED
+}
+
+void release(oasis_pipeline *p) {
+    if (p->worker.joinable()) {
+        {
+            std::lock_guard<std::mutex> lk(p->mu);
+            p->stop = true;
+        }
+        p->cv_job.notify_all();
+        p->worker.join();
+    }
+    if (p->comp) (void)hipStreamSynchronize(p->comp);
+    if (p->copy) (void)hipStreamSynchronize(p->copy);
+    (void)hipStreamSynchronize(p->main);
+    for (hipEvent_t e : p->ev)
+        if (e) (void)hipEventDestroy(e);
+    for (auto &v : p->t_ev)
+        for (hipEvent_t e : v)
+            if (e) (void)hipEventDestroy(e);
+    if (p->comp) (void)hipStreamDestroy(p->comp);
+    if (p->copy) (void)hipStreamDestroy(p->copy);
+    delete p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *desc, oasis_pipeline **out) {
+    clear_error();
+    if (!out) PFAIL(OASIS_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!dims || !desc) PFAIL(OASIS_EINVAL, "dims or desc is NULL");
+    const oasis_pipeline_desc &ds = *desc;
+    if (ds.n_layers < 1 || ds.n_layers > 1024) PFAIL(OASIS_EINVAL, "n_layers = %d outside [1, 1024]", ds.n_layers);
+    if (ds.K_b < 1) PFAIL(OASIS_EINVAL, "K_b = %d < 1", ds.K_b);
+    if (ds.J < 1) PFAIL(OASIS_EINVAL, "J = %d < 1", ds.J);
+    if (ds.staged != 0 && ds.staged != 1) PFAIL(OASIS_EINVAL, "staged = %d", ds.staged);
+    if (ds.staged && (ds.C < 0 || ds.C > ds.K_b)) PFAIL(OASIS_EINVAL, "C = %d outside [0, K_b]", ds.C);
+    if (ds.copy_mode != OASIS_COPY_KERNEL && ds.copy_mode != OASIS_COPY_DMA)
+        PFAIL(OASIS_EINVAL, "copy_mode = %d", ds.copy_mode);
+    if (!ds.pool || !ds.kminmax || !ds.ctx_len || !ds.layers) PFAIL(OASIS_EINVAL, "pool, kminmax, ctx_len or layers is NULL");
+    if (ds.n_split < 0 || ds.n_split > 64) PFAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", ds.n_split);
+    int rc0 = check_dims(dims);
+    if (rc0) return rc0;
+    const size_t plan_need = oasis_stage_plan_bytes(dims, ds.K_b);
+    const size_t ws_need = oasis_attn_workspace_bytes(dims, ds.K_b, ds.n_split);
+    for (int l = 0; l < ds.n_layers; l++) {
+        int rc = check_layer(ds, ds.layers[l], l, plan_need, ws_need);
+        if (rc) return rc;
+    }
+    auto *p = new (std::nothrow) oasis_pipeline();
+    if (!p) PFAIL(OASIS_EINVAL, "out of host memory");
+    p->d = *dims;
+    p->desc = ds;
+    p->layers.assign(ds.layers, ds.layers + ds.n_layers);
+    p->desc.layers = nullptr;
+    p->next_step.assign(ds.n_layers, 0);
+    p->done.assign(ds.n_layers, -1);
+    p->S = ds.K_b + (ds.staged ? ds.C : 0);
+    p->main = static_cast<hipStream_t>(ds.main_stream);
+    auto fail = [&](hipError_t e, const char *what) {
+        hip_check(e, what);
+        release(p);
+        return OASIS_EHIP;
+    };
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) return fail(e, "hipGetDevice");
+    if ((e = hipStreamCreateWithFlags(&p->comp, hipStreamNonBlocking)) != hipSuccess)
+        return fail(e, "hipStreamCreateWithFlags");
+    if (ds.staged && (e = hipStreamCreateWithFlags(&p->copy, hipStreamNonBlocking)) != hipSuccess)
+        return fail(e, "hipStreamCreateWithFlags");
+    p->ev.assign((size_t)kEvKinds * ds.n_layers * kRing, nullptr);
+    for (auto &x : p->ev)
+        if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess)
+            return fail(e, "hipEventCreateWithFlags");
+    if (ds.staged && ds.copy_mode == OASIS_COPY_DMA) p->worker = std::thread(worker_loop, p);
+    *out = p;
+    return OASIS_OK;
+}
+
+int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uint16_t *q_look,
+                              const uint16_t *q_attn, uint16_t *out, float *lse) {
+    clear_error();
+    if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
+    const oasis_pipeline_desc &ds = p->desc;
+    if (l < 0 || l >= ds.n_layers) PFAIL(OASIS_EINVAL, "layer = %d outside [0, %d)", l, ds.n_layers);
+    if (t != p->next_step[l]) PFAIL(OASIS_EINVAL, "layer %d: step %d issued, step %d expected", l, t, p->next_step[l]);
+    if (!q_look) PFAIL(OASIS_EINVAL, "q_look is NULL");
+    if (t >= 1 && (!q_attn || !out)) PFAIL(OASIS_EINVAL, "q_attn or out is NULL at step %d", t);
+    int rc;
+    if ((rc = worker_error(p))) return rc;
+    const oasis_layer_buffers &b = p->layers[l];
+    const oasis_dims *d = &p->d;
+    const int K_b = ds.K_b;
+    const int j = t % 2;
+
+    // foreground: attention of step t
+    if (t >= 1) {
+        if (ds.staged) {
+            if (ds.copy_mode == OASIS_COPY_DMA) {
+                std::unique_lock<std::mutex> lk(p->mu);
+                p->cv_done.wait(lk, [&] { return p->done[l] >= t - 1 || p->err != OASIS_OK; });
+            }
+            if ((rc = worker_error(p))) return rc;
+            OASIS_HIP(hipStreamWaitEvent(p->main, p->event(kEvStage, l, t - 1), 0));
+            const int k = t % 3;
+            timed_begin(p, 0, p->main);
+            rc = oasis_sparse_decode_attn(d, q_attn, b.ws_pool, p->S, b.tbl_slot[k], b.tbl_block[k], b.tbl_n[k],
+                                          K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes,
+                                          ds.n_split, p->main);
+        } else {
+            const int jp = (t - 1) % 2;
+            OASIS_HIP(hipStreamWaitEvent(p->main, p->event(kEvSel, l, t - 1), 0));
+            timed_begin(p, 0, p->main);
+            rc = oasis_sparse_decode_attn(d, q_attn, ds.pool, d->NB_max, b.sel[jp], b.sel[jp], b.n_sel[jp], K_b,
+                                          ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes,
+                                          ds.n_split, p->main);
+        }
+        if (rc) return rc;
+        timed_end(p, 0, p->main);
+        OASIS_HIP(hipEventRecord(p->event(kEvAttn, l, t), p->main));
+    }
+
+    // background: prediction and staging plan for step t + 1
+    hipStream_t cs = p->comp;
+    timed_begin(p, 1, cs);
+    if ((rc = oasis_score_blocks(d, q_look, ds.J, ds.kminmax, ds.ctx_len, b.scores, cs))) return rc;
+    timed_end(p, 1, cs);
+    if (t >= 2) {
+        // sel[j] (unstaged: read by the attention of step t - 1) and table
+        // (t + 1) % 3 (staged: read by the attention of step t - 2)
+        OASIS_HIP(hipStreamWaitEvent(cs, p->event(kEvAttn, l, ds.staged ? t - 2 : t - 1), 0));
+    }
+    timed_begin(p, 2, cs);
+    if ((rc = oasis_select_topk(d, b.scores, ds.ctx_len, K_b, b.sel[j], b.n_sel[j], cs))) return rc;
+    timed_end(p, 2, cs);
+    if (!ds.staged) {
+        OASIS_HIP(hipEventRecord(p->event(kEvSel, l, t), cs));
+        p->next_step[l] = t + 1;
+        return OASIS_OK;
+    }
+    if (t >= 2) OASIS_HIP(hipStreamWaitEvent(cs, p->event(kEvStage, l, t - 2), 0));  // plan[j]'s last reader
+
+    Job job;
+    job.layer = l;
+    job.step = t;
+    oasis_stage_args &a = job.args;
+    const int k1 = (t + 1) % 3;
+    a.sel = b.sel[j];
+    a.n_sel = b.n_sel[j];
+    a.K_sel = K_b;
+    a.scores = b.scores;
+    a.K_b = K_b;
+    a.C = t == 0 ? K_b : ds.C;
+    a.S = p->S;
+    a.step = t;
+    a.slot_block = b.slot_block;
+    a.slot_stamp = b.slot_stamp;
+    a.ctx_len = ds.ctx_len;
+    a.host_pool = ds.pool;
+    a.ws_pool = b.ws_pool;
+    a.tbl_slot = b.tbl_slot[k1];
+    a.tbl_block = b.tbl_block[k1];
+    a.tbl_n = b.tbl_n[k1];
+    a.plan = b.plan[j];
+    a.plan_bytes = b.plan_bytes;
+    a.host_plan = b.host_plan;
+    a.host_plan_bytes = b.plan_bytes;
+    a.stage_host = b.stage_host[j];
+    a.stage_host_bytes = b.stage_bytes;
+    a.stage_dev = b.stage_dev;
+    a.stage_dev_bytes = b.stage_bytes;
+    a.host_threads = ds.host_threads;
+    a.copy_mode = ds.copy_mode;
+    a.stream = cs;
+    a.copy_stream = p->copy;
+    a.wait_event = t >= 1 ? p->event(kEvAttn, l, t - 1) : nullptr;
+    a.done_event = p->event(kEvStage, l, t);
+    a.plan_event = p->event(kEvPlan, l, t);
+    timed_begin(p, 3, cs);
+    if ((rc = oasis_stage_plan(d, &a))) return rc;
+    timed_end(p, 3, cs);
+    if (ds.copy_mode == OASIS_COPY_DMA) {
+        {
+            std::lock_guard<std::mutex> lk(p->mu);
+            p->jobs.push_back(job);
+        }
+        p->cv_job.notify_one();
+    } else if ((rc = run_copy(p, job))) {
+        return rc;
+    }
+    p->next_step[l] = t + 1;
+    return OASIS_OK;
+}
+
+int oasis_pipeline_drain(oasis_pipeline *p) {
+    clear_error();
+    if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
+    {
+        std::unique_lock<std::mutex> lk(p->mu);
+        p->cv_done.wait(lk, [&] { return p->jobs.empty(); });
+    }
+    return worker_error(p);
+}
+
+int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream) {
+    clear_error();
+    if (!p || !stream) PFAIL(OASIS_EINVAL, "pipeline or stream is NULL");
+    if (which < 0 || which > 2) PFAIL(OASIS_EINVAL, "which = %d outside [0, 2]", which);
+    *stream = which == 0 ? (void *)p->main : which == 1 ? (void *)p->comp : (void *)p->copy;
+    return OASIS_OK;
+}
+
+int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity) {
+    clear_error();
+    if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
+    if (capacity < 0 || capacity > (1 << 20)) PFAIL(OASIS_EINVAL, "capacity = %d", capacity);
+    int rc = oasis_pipeline_drain(p);
+    if (rc) return rc;
+    for (int k = 0; k < kTimedKinds; k++) {
+        auto &v = p->t_ev[k];
+        while ((int)v.size() < 2 * capacity) {
+            hipEvent_t e = nullptr;
+            OASIS_HIP(hipEventCreate(&e));
+            v.push_back(e);
+        }
+        p->t_n[k] = 0;
+    }
+    p->t_cap = capacity;
+    std::lock_guard<std::mutex> lk(p->t_mu);
+    p->copy_host_s = 0.0;
+    p->copy_calls = 0;
+    return OASIS_OK;
+}
+
+int oasis_pipeline_timing_read(oasis_pipeline *p, int32_t kind, double *total_ms, int32_t *count) {
+    clear_error();
+    if (!p || !total_ms || !count) PFAIL(OASIS_EINVAL, "pipeline, total_ms or count is NULL");
+    if (kind < 0 || kind >= kTimedKinds) PFAIL(OASIS_EINVAL, "kind = %d", kind);
+    int rc = oasis_pipeline_drain(p);
+    if (rc) return rc;
+    double sum = 0.0;
+    for (int i = 0; i < p->t_n[kind]; i++) {
+        OASIS_HIP(hipEventSynchronize(p->t_ev[kind][2 * i + 1]));
+        float ms = 0.f;
+        OASIS_HIP(hipEventElapsedTime(&ms, p->t_ev[kind][2 * i], p->t_ev[kind][2 * i + 1]));
+        sum += ms;
+    }
+    *total_ms = sum;
+    *count = p->t_n[kind];
+    return OASIS_OK;
+}
+
+int oasis_pipeline_copy_host_seconds(oasis_pipeline *p, double *seconds, int32_t *calls) {
+    clear_error();
+    if (!p || !seconds || !calls) PFAIL(OASIS_EINVAL, "pipeline, seconds or calls is NULL");
+    std::lock_guard<std::mutex> lk(p->t_mu);
+    *seconds = p->copy_host_s;
+    *calls = p->copy_calls;
+    return OASIS_OK;
+}
+
+int oasis_pipeline_destroy(oasis_pipeline *p) {
+    clear_error();
+    if (!p) return OASIS_OK;
+    release(p);
+    return OASIS_OK;
+}
+
+}  // extern "C"

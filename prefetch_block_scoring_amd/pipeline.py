@@ -4,48 +4,47 @@ The OasisKV pages (arXiv 2608.08097, paperlayer summary, section 4) run, per
 layer, a background chain of top-K prediction, KV selection and KV transfer,
 with independent workers overlapped across layers and decode steps; the
 foreground waits only for the relevant layer's transfer before that layer's
-next-step attention.  `LayerPipeline` schedules the library's calls that way
-on one GPU:
+next-step attention.  The library's native pipeline (oasis_pipeline_* in
+include/oasis.h) schedules that chain on one GPU:
 
   main stream     attention of (layer l, step t), after the transfer of
                   (l, t - 1) only
   compute stream  scores and top-K of (l, t), then the staging plan of (l, t)
-  copy stream     the copies of (l, t) (gather kernel, or DMA copy + scatter)
+  copy stream     the copies of (l, t) (gather kernel, or DMA copy + scatter
+                  on the pipeline's worker thread)
 
-Per layer the buffers rotate so that the compute stream can run ahead: three
-attention tables (step t attends table t % 3, the plan of step t writes
-(t + 1) % 3) and two plan workspaces.  The plan of step t therefore waits for
-the attention of step t - 2 (the last reader of its table) and for the copies
-of step t - 2 (the last reader of its plan), and the copies of step t wait
-for the attention of step t - 1 (whose slots they may refill).  The copy half
-of a staging step blocks its thread with the DMA engine, so it runs on one
-worker thread, in submission order.
+`LayerPipeline` allocates the per-layer buffers the native pipeline works in
+(three attention tables, two selections and two plan buffers per layer, the
+working sets) and issues one native call per layer-step.  Workloads without
+staging (K/V fully in HBM) run the same chain without the copy stream: the
+attention of step t reads the full pool through the selection of step t - 1.
 
-Workloads without staging (K/V fully in HBM) run the same chain without the
-copy stream: the attention of step t reads the full pool through the
-selection of step t - 1.
-
-Argument marshalling and scheduling only: every step runs in the library.
+Argument marshalling only: every step runs in the library.
 """
 from __future__ import annotations
 
-import concurrent.futures
-import time
-from typing import Callable, Optional
+import ctypes
+import math
+from typing import Optional
 
 import torch
 
 from . import binding as oa
 
+TIMING_KINDS = {"attn": 0, "score": 1, "topk": 2, "plan": 3}
+
 
 class _Layer:
-    def __init__(self, B, H_q, H_kv, NB, K_b, C, staged, copy_mode, dev, D=128, bs=16):
+    def __init__(self, B, H_q, H_kv, NB, K_b, C, staged, copy_mode, ws_bytes, dev, D=128, bs=16):
         i32 = torch.int32
         self.scores = torch.empty((B, H_kv, NB), dtype=torch.float32, device=dev)
         self.sel = [torch.empty((B, H_kv, K_b), dtype=i32, device=dev) for _ in range(2)]
         self.n_sel = [torch.empty((B, H_kv), dtype=i32, device=dev) for _ in range(2)]
         self.out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, H_q), dtype=torch.float32, device=dev)
+        self.attn_ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+        self.ws_pool = self.slot_block = self.slot_stamp = None
+        self.tbls, self.plans, self.host_plan, self.stage_host, self.stage_dev = [], [], None, [None, None], None
         if staged:
             S = K_b + C
             self.ws_pool = torch.empty((B, H_kv, S, 2, bs, D), dtype=torch.bfloat16, device=dev)
@@ -61,8 +60,27 @@ class _Layer:
                 sbytes = oa.oasis_stage_buffer_bytes(B * H_kv * max(C, 1))
                 self.stage_host = [oa.oasis_host_empty((sbytes,), torch.uint8) for _ in range(2)]
                 self.stage_dev = torch.empty(sbytes, dtype=torch.uint8, device=dev)
-            else:
-                self.host_plan, self.stage_host, self.stage_dev = None, [None, None], None
+
+    def buffers(self) -> oa.oasis_layer_buffers:
+        b = oa.oasis_layer_buffers()
+        p = lambda t: None if t is None else t.data_ptr()
+        b.scores = p(self.scores)
+        for k in range(2):
+            b.sel[k], b.n_sel[k] = p(self.sel[k]), p(self.n_sel[k])
+        b.attn_ws, b.attn_ws_bytes = p(self.attn_ws), self.attn_ws.numel()
+        if self.ws_pool is not None:
+            b.ws_pool, b.slot_block, b.slot_stamp = p(self.ws_pool), p(self.slot_block), p(self.slot_stamp)
+            for k in range(3):
+                b.tbl_slot[k], b.tbl_block[k], b.tbl_n[k] = (p(x) for x in self.tbls[k])
+            for k in range(2):
+                b.plan[k] = p(self.plans[k])
+            b.plan_bytes = self.plans[0].numel() * 4
+            if self.host_plan is not None:
+                b.host_plan, b.stage_dev = p(self.host_plan), p(self.stage_dev)
+                for k in range(2):
+                    b.stage_host[k] = p(self.stage_host[k])
+                b.stage_bytes = min(self.stage_dev.numel(), self.stage_host[0].numel())
+        return b
 
 
 class LayerPipeline:
@@ -72,62 +90,33 @@ class LayerPipeline:
            when staged, else device memory.
     summ:  the pool's block summaries (oasis_build_summaries), device.
     ctx:   int32 [B] context lengths, device.
-    Step 0 of every layer is the uncapped initial fill (staged workloads).
+    The attention runs on the stream current at construction (`main`); the
+    compute and copy streams belong to the native pipeline.  Step 0 of every
+    layer is the uncapped initial fill (staged workloads).  The caller keeps
+    the query tensors it passes alive until their work has completed.
     """
 
     def __init__(self, *, pool, summ, ctx, H_q: int, K_b: int, C: int, n_layers: int, staged: bool,
-                 copy_mode: int = oa.OASIS_COPY_KERNEL, host_threads: int = 8, n_split: int = 0,
-                 timer: Optional[Callable] = None):
+                 copy_mode: int = oa.OASIS_COPY_KERNEL, host_threads: int = 8, n_split: int = 0, J: int = 1):
         B, H_kv, NB, _, bs, D = pool.shape
         self.B, self.H_q, self.H_kv, self.NB, self.K_b, self.C = B, H_q, H_kv, NB, K_b, C
         self.pool, self.summ, self.ctx = pool, summ, ctx
-        self.staged, self.copy_mode, self.host_threads, self.n_split = staged, copy_mode, host_threads, n_split
-        self.L = n_layers
+        self.staged, self.copy_mode = staged, copy_mode
+        self.L, self.J = n_layers, J
         dev = ctx.device
-        self.layers = [_Layer(B, H_q, H_kv, NB, K_b, C, staged, copy_mode, dev, D, bs) for _ in range(n_layers)]
-        self.main = torch.cuda.current_stream()
-        self.comp = torch.cuda.Stream()
-        self.copy = torch.cuda.Stream() if staged else None
         ws = oa.oasis_attn_workspace_bytes(B, H_q, H_kv, K_b, n_split)
-        self.attn_ws = [torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev) for _ in range(n_layers)]
-        self.events = {}
-        self.pending = {}
-        self.stager = concurrent.futures.ThreadPoolExecutor(max_workers=1) if staged else None
-        self.timer = timer or (lambda name, stream, fn: fn())
-        self.copy_host_s = []
-
-    # ------------------------------------------------------------ helpers
-
-    def _ev(self, kind, l, t):
-        key = (kind, l, t)
-        e = self.events.get(key)
-        if e is None:
-            e = self.events[key] = torch.cuda.Event()
-        return e
-
-    def _forget(self, l, t):
-        for kind in ("attn", "stage", "plan", "sel"):
-            self.events.pop((kind, l, t), None)
-
-    def _stage_kw(self, l, t):
-        ly = self.layers[l]
-        j = t % 2
-        tb = ly.tbls[(t + 1) % 3]
-        return dict(
-            sel=ly.sel[j], n_sel=ly.n_sel[j], scores=ly.scores, ctx_len=self.ctx, K_b=self.K_b,
-            C=self.K_b if t == 0 else self.C, step=t, slot_block=ly.slot_block, slot_stamp=ly.slot_stamp,
-            host_pool=self.pool, ws_pool=ly.ws_pool, tbl_slot=tb[0], tbl_block=tb[1], tbl_n=tb[2],
-            plan=ly.plans[j], host_plan=ly.host_plan, stage_host=ly.stage_host[j], stage_dev=ly.stage_dev,
-            host_threads=self.host_threads, copy_mode=self.copy_mode, stream=self.comp,
-            copy_stream=self.copy, done_event=self._ev("stage", l, t), plan_event=self._ev("plan", l, t),
-            wait_event=self._ev("attn", l, t - 1) if t >= 2 else None)
-
-    def _copy(self, kw):
-        h0 = time.perf_counter()
-        oa.oasis_stage_copy(**kw)
-        self.copy_host_s.append(time.perf_counter() - h0)
-
-    # ------------------------------------------------------------ one layer-step
+        self.layers = [_Layer(B, H_q, H_kv, NB, K_b, C, staged, copy_mode, ws, dev, D, bs)
+                       for _ in range(n_layers)]
+        self.main = torch.cuda.current_stream()
+        bufs = (oa.oasis_layer_buffers * n_layers)(*[ly.buffers() for ly in self.layers])
+        desc = oa.oasis_pipeline_desc(
+            n_layers=n_layers, K_b=K_b, C=C if staged else 0, J=J, staged=int(staged), copy_mode=copy_mode,
+            host_threads=host_threads, n_split=n_split, sm_scale=1.0 / math.sqrt(D), pool=pool.data_ptr(),
+            kminmax=summ.data_ptr(), ctx_len=ctx.data_ptr(), main_stream=self.main.cuda_stream,
+            layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)))
+        self._h = oa.oasis_pipeline_create(oa.dims(B, H_q, H_kv, NB, D, bs), desc)
+        self.comp = torch.cuda.ExternalStream(oa.oasis_pipeline_stream(self._h, 1))
+        self.copy = torch.cuda.ExternalStream(oa.oasis_pipeline_stream(self._h, 2)) if staged else None
 
     def layer_step(self, l: int, t: int, q_look: torch.Tensor, q_attn: Optional[torch.Tensor]):
         """Enqueue layer l's work of decode step t: the attention of step t
@@ -135,44 +124,10 @@ class LayerPipeline:
         t = 0) and the prediction and staging for step t + 1 from the
         lookahead queries q_look.  The attention output lands in
         `self.layers[l].out` / `.lse` once the main stream reaches it."""
+        if tuple(q_look.shape) != (self.B, self.J, self.H_q, self.layers[l].out.shape[2]):
+            raise ValueError(f"q_look shape {tuple(q_look.shape)}: expected [B][J = {self.J}][H_q][D]")
         ly = self.layers[l]
-        main, comp = self.main, self.comp
-        j = t % 2
-        if t >= 1:
-            if self.staged:
-                self.pending.pop((l, t - 1)).result()        # its done event is recorded
-                tb = ly.tbls[t % 3]
-                main.wait_event(self._ev("stage", l, t - 1))
-                self.timer("attn", main, lambda: oa.oasis_sparse_decode_attn(
-                    q_attn, ly.ws_pool, tb[0], tb[1], tb[2], self.ctx, out=ly.out, lse=ly.lse,
-                    ws=self.attn_ws[l], n_split=self.n_split, stream=main))
-            else:
-                jp = (t - 1) % 2
-                main.wait_event(self._ev("sel", l, t - 1))
-                self.timer("attn", main, lambda: oa.oasis_sparse_decode_attn(
-                    q_attn, self.pool, ly.sel[jp], ly.sel[jp], ly.n_sel[jp], self.ctx, out=ly.out,
-                    lse=ly.lse, ws=self.attn_ws[l], n_split=self.n_split, stream=main))
-            self._ev("attn", l, t).record(main)
-        with torch.cuda.stream(comp):
-            self.timer("score", comp, lambda: oa.oasis_score_blocks(q_look, self.summ, self.ctx,
-                                                                    scores=ly.scores, stream=comp))
-            if t >= 2:
-                # sel[j] (no staging) and table (t + 1) % 3 were last read by
-                # the attention of step t - 2 ... t - 1
-                comp.wait_event(self._ev("attn", l, t - 1 if not self.staged else t - 2))
-            self.timer("topk", comp, lambda: oa.oasis_select_topk(ly.scores, self.ctx, self.K_b, sel=ly.sel[j],
-                                                                  n_sel=ly.n_sel[j], stream=comp))
-            if not self.staged:
-                self._ev("sel", l, t).record(comp)
-            else:
-                if t >= 2:
-                    comp.wait_event(self._ev("stage", l, t - 2))   # plan[j] was read by those copies
-                kw = self._stage_kw(l, t)
-                self.timer("plan", comp, lambda: oa.oasis_stage_plan(**kw))
-        if self.staged:
-            self.pending[(l, t)] = self.stager.submit(self._copy, kw)
-        if t >= 3:
-            self._forget(l, t - 3)
+        oa.oasis_pipeline_layer_step(self._h, l, t, q_look, q_attn if t >= 1 else None, ly.out, ly.lse)
 
     def admitted(self, l: int, t: int) -> torch.Tensor:
         """Device scalar: total admits of layer l's staging at step t (valid
@@ -185,11 +140,31 @@ class LayerPipeline:
         """(slot, block, n) tables that the attention of step t reads."""
         return self.layers[l].tbls[t % 3]
 
+    def enable_timing(self, capacity: int):
+        """Time up to `capacity` launches of each kind (attn, score, topk,
+        plan) with events on their own streams; clears earlier totals."""
+        oa.oasis_pipeline_timing(self._h, capacity)
+
+    def timing(self, kind: str):
+        """(average microseconds, count) of the timed launches of `kind`."""
+        ms, n = oa.oasis_pipeline_timing_read(self._h, TIMING_KINDS[kind])
+        return (ms * 1e3 / n if n else 0.0), n
+
+    def copy_host_seconds(self):
+        """(host seconds in the copy half of staging, calls) since timing
+        was last enabled."""
+        return oa.oasis_pipeline_copy_host_seconds(self._h)
+
     def drain(self):
-        for f in list(self.pending.values()):
-            f.result()
+        oa.oasis_pipeline_drain(self._h)
 
     def close(self):
-        self.drain()
-        if self.stager is not None:
-            self.stager.shutdown()
+        if self._h:
+            oa.oasis_pipeline_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -154,3 +154,66 @@ def test_plan_and_staging_sizes():
     assert L.oasis_stage_plan_bytes(ctypes.byref(dd), 0) == 4 * (3 * 2 * 6 + 4)
     assert L.oasis_stage_buffer_bytes(ctypes.byref(dd), 7) == 7 * 8192
     assert oa.oasis_stage_buffer_bytes(3) == 3 * 8192
+
+
+def _pipeline_desc(L=2, staged=1, copy_mode=0, **kw):
+    """A pipeline description whose buffers are fake non-NULL addresses:
+    every case below is rejected by the host checks before any pointer is
+    used or any device call is made."""
+    bufs = (binding.oasis_layer_buffers * L)()
+    fake = 0x1000
+    for b in bufs:
+        b.scores = fake
+        for k in range(2):
+            b.sel[k] = b.n_sel[k] = b.plan[k] = b.stage_host[k] = fake
+        for k in range(3):
+            b.tbl_slot[k] = b.tbl_block[k] = b.tbl_n[k] = fake
+        b.attn_ws, b.attn_ws_bytes = fake, 1 << 30
+        b.ws_pool = b.slot_block = b.slot_stamp = b.host_plan = b.stage_dev = fake
+        b.plan_bytes = 1 << 30
+        b.stage_bytes = 1 << 20
+    d = binding.oasis_pipeline_desc(n_layers=L, K_b=128, C=6, J=1, staged=staged, copy_mode=copy_mode,
+                                    host_threads=0, n_split=0, sm_scale=0.088, pool=fake, kminmax=fake,
+                                    ctx_len=fake, main_stream=None,
+                                    layers=ctypes.cast(bufs, ctypes.POINTER(binding.oasis_layer_buffers)))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d, bufs
+
+
+@pytest.mark.parametrize("change,code", [
+    ({"n_layers": 0}, oa.OASIS_EINVAL),
+    ({"K_b": 0}, oa.OASIS_EINVAL),
+    ({"J": 0}, oa.OASIS_EINVAL),
+    ({"C": 129}, oa.OASIS_EINVAL),
+    ({"copy_mode": 7}, oa.OASIS_EINVAL),
+    ({"staged": 2}, oa.OASIS_EINVAL),
+    ({"pool": None}, oa.OASIS_EINVAL),
+    ({"n_split": 65}, oa.OASIS_EINVAL),
+])
+def test_pipeline_create_rejects_bad_descriptions(change, code):
+    d, bufs = _pipeline_desc(**change)
+    with pytest.raises(oa.OasisError) as e:
+        oa.oasis_pipeline_create(oa.dims(4, 32, 8, 1024), d)
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("field,code", [("ws_pool", oa.OASIS_EINVAL), ("plan_bytes", oa.OASIS_ENOSPACE),
+                                        ("attn_ws_bytes", oa.OASIS_ENOSPACE), ("stage_dev", oa.OASIS_EINVAL)])
+def test_pipeline_create_rejects_bad_layer_buffers(field, code):
+    d, bufs = _pipeline_desc(copy_mode=oa.OASIS_COPY_DMA)
+    setattr(bufs[1], field, 0 if "bytes" in field else None)
+    with pytest.raises(oa.OasisError) as e:
+        # n_split = 4 needs an attention workspace, so its size is checked
+        d.n_split = 4
+        oa.oasis_pipeline_create(oa.dims(4, 32, 8, 1024), d)
+    assert e.value.code == code
+    assert "layer 1" in oa.oasis_last_error()
+
+
+def test_pipeline_calls_reject_null_handles():
+    lib = binding.library()
+    assert lib.oasis_pipeline_layer_step(None, 0, 0, None, None, None, None) == oa.OASIS_EINVAL
+    assert lib.oasis_pipeline_drain(None) == oa.OASIS_EINVAL
+    assert lib.oasis_pipeline_timing(None, 4) == oa.OASIS_EINVAL
+    assert lib.oasis_pipeline_destroy(None) == oa.OASIS_OK

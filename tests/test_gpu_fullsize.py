@@ -63,7 +63,7 @@ def run_gpu(w, copy_mode, rs):
     q_look = [wl.lookahead(w, s, DEV) for s in range(n_look)]
     q_attn = [q_look[max(s - 1, 0)][:, 0].contiguous() for s in range(n_look)]
     pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=LAYERS,
-                         staged=w.staged, copy_mode=copy_mode, host_threads=8)
+                         staged=w.staged, copy_mode=copy_mode, host_threads=8, J=w.J)
     idx = torch.tensor(rs, device=DEV)
     snaps = {}
     for t in range(STEPS):

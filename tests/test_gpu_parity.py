@@ -404,7 +404,7 @@ def test_layer_pipeline_matches_oracle(copy_mode):
     summ = m.oasis_build_summaries(host, ctx)
     looks = [wl.lookahead(w, s).to(DEV) for s in range(steps + 2 * L)]
     attn_q = [looks[max(s - 1, 0)][:, 0].contiguous() for s in range(steps + 2 * L)]
-    pipe = LayerPipeline(pool=host, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=True,
+    pipe = LayerPipeline(pool=host, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=True, J=w.J,
                          copy_mode=copy_mode, host_threads=4)
     outs = {}
     for t in range(steps):
