@@ -51,6 +51,10 @@ def parse():
     p.add_argument("--copy-mode", choices=["kernel", "dma"], default="kernel")
     p.add_argument("--host-threads", type=int, default=8, help="packing threads of the DMA copy engine")
     p.add_argument("--n-split", type=int, default=0)
+    p.add_argument("--cap", type=float, default=None,
+                   help="override the staged workload's fetch cap (fraction of the budget; >= 1 = fetch-all)")
+    p.add_argument("--drift", type=float, default=None,
+                   help="override the drift workload's per-step turnover (fraction of the budget)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -178,6 +182,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = wl.WORKLOADS[args.workload]
+    if args.cap is not None:
+        if not w.staged:
+            raise SystemExit(f"--cap: workload {w.name} keeps its K/V in HBM")
+        w = w.shrink(cap=args.cap)
+    if args.drift is not None:
+        if w.structure != "drift":
+            raise SystemExit(f"--drift: workload {w.name} has no drift structure")
+        w = w.shrink(drift=args.drift)
     B, H_q, H_kv, D, bs, K_b, NB = w.B, w.H_q, w.H_kv, w.D, w.bs, w.K_b, w.NB_max
     staged = w.staged
     L = max(1, args.layers)
@@ -326,6 +338,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "context": w.ctx, "heads_q": H_q, "heads_kv": H_kv,
                    "head_dim": D, "block_tokens": bs, "kv_budget_tokens": w.budget, "lookahead_queries": w.J,
                    "fetch_cap": w.cap, "fetch_cap_blocks": C, "slots": S if staged else None,
+                   "drift": w.drift if w.structure == "drift" else None,
                    "layers_in_flight": L, "step_unit": "layer-step",
                    "kv_location": "pinned host pool + HBM working set" if staged else "HBM",
                    "copy_engine": args.copy_mode if staged else None,

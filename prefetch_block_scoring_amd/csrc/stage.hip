@@ -20,7 +20,7 @@
 //     them over PCIe; the scatter kernel then places them.  The DMA engines
 //     leave the compute units and their memory path to the HBM-bound kernels
 //     that run at the same time.
-//   kernel: a persistent gather kernel reads the pool through its device
+//   kernel: a gather kernel of a few workgroups reads the pool through its device
 //     mapping.  No host work, but its PCIe reads hold the memory path and
 //     slow concurrent HBM-bound kernels down.
 #include "oasis_internal.h"
@@ -282,20 +282,55 @@ __global__ __launch_bounds__(1024) void stage_prefix_kernel(int32_t *__restrict_
     if (tid == 0) plan[(size_t)pairs * row] = carry;
 }
 
-// Zero-copy engine.  Persistent: kGatherWgs workgroups walk the (pair, admit)
-// items; each thread keeps two 16-byte PCIe reads in flight per block.
-__global__ __launch_bounds__(256) void stage_gather_kernel(
-    const int32_t *__restrict__ plan, int row, int C, int n_items, const uint4 *__restrict__ host_pool,
-    uint4 *__restrict__ ws_pool, int NB_max, int S) {
+// Packed positions: the admits of one step, numbered in (pair, admission)
+// order; row[2] of each pair holds the position of its first admit (the
+// exclusive prefix of the admit counts) and the total follows the rows.  A
+// workgroup of the copy kernels takes a contiguous range of positions, finds
+// the pair of its first position, and walks forward, so pairs with fewer
+// admits than C cost nothing.
+
+// The pair holding position k (0 <= k < total): the last pair whose first
+// position is <= k.  Every thread of the workgroup must call it.
+__device__ int pair_of_position(const int32_t *__restrict__ plan, int row, int pairs, int k) {
+    __shared__ int cnt;
+    if (threadIdx.x == 0) cnt = 0;
+    __syncthreads();
+    int c = 0;
+    for (int rh = threadIdx.x; rh < pairs; rh += blockDim.x) c += plan[(size_t)rh * row + 2] <= k ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    if ((threadIdx.x & 63) == 0 && c) atomicAdd(&cnt, c);
+    __syncthreads();
+    const int r = cnt - 1;
+    __syncthreads();  // cnt is rewritten by the next call
+    return r;
+}
+
+// Copy the blocks of positions [k0, k1): for each, the source returned by
+// src_of(k, rh, i) into slot `slot` of pair rh.  pairs' admit counts are
+// clamped to [0, C] and slots to [0, S); a pair index past the rows ends the
+// walk.
+template <class SrcOf>
+__device__ void copy_positions(const int32_t *__restrict__ plan, int row, int pairs, int C, int S, int k0,
+                               int k1, uint4 *__restrict__ ws_pool, SrcOf src_of) {
     constexpr int kVec = (int)(kBlockBytes / sizeof(uint4));  // 512
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int rh = item / C;
-        const int i = item - rh * C;
-        const int32_t *p = plan + (size_t)rh * row;
-        if (i >= p[0]) continue;
-        const int slot = p[kPlanHead + 2 * i], blk = p[kPlanHead + 2 * i + 1];
-        if (slot < 0 || slot >= S || blk < 0 || blk >= NB_max) continue;
-        const uint4 *src = host_pool + ((size_t)rh * NB_max + blk) * kVec;
+    if (k0 >= k1) return;
+    int rh = pair_of_position(plan, row, pairs, k0);
+    if (rh < 0) return;
+    const int32_t *p = plan + (size_t)rh * row;
+    int pos = p[2], n = min(max(p[0], 0), C);
+    for (int k = k0; k < k1; k++) {
+        while (k >= pos + n) {
+            if (++rh >= pairs) return;
+            p = plan + (size_t)rh * row;
+            pos = p[2];
+            n = min(max(p[0], 0), C);
+        }
+        const int i = k - pos;
+        if (i < 0) continue;  // inconsistent plan: skip, never index past it
+        const int slot = p[kPlanHead + 2 * i];
+        const uint4 *src = src_of(k, rh, p[kPlanHead + 2 * i + 1]);
+        if (slot < 0 || slot >= S || !src) continue;
         uint4 *dst = ws_pool + ((size_t)rh * S + slot) * kVec;
         const uint4 a = src[threadIdx.x];
         const uint4 b = src[threadIdx.x + 256];
@@ -304,28 +339,36 @@ __global__ __launch_bounds__(256) void stage_gather_kernel(
     }
 }
 
+// Zero-copy engine: kGatherWgs workgroups split the step's packed positions
+// into contiguous ranges; each thread keeps two 16-byte PCIe reads in flight
+// per block.
+__global__ __launch_bounds__(256) void stage_gather_kernel(
+    const int32_t *__restrict__ plan, int row, int pairs, int C, const uint4 *__restrict__ host_pool,
+    uint4 *__restrict__ ws_pool, int NB_max, int S) {
+    constexpr int kVec = (int)(kBlockBytes / sizeof(uint4));
+    const int total = (int)min((long)max(plan[(size_t)pairs * row], 0), (long)pairs * C);
+    const int per = (total + gridDim.x - 1) / gridDim.x;
+    const int k0 = min(total, (int)blockIdx.x * per), k1 = min(total, k0 + per);
+    copy_positions(plan, row, pairs, C, S, k0, k1, ws_pool, [&](int, int rh, int blk) -> const uint4 * {
+        if (blk < 0 || blk >= NB_max) return nullptr;
+        return host_pool + ((size_t)rh * NB_max + blk) * kVec;
+    });
+}
+
 // DMA engine, device half: the packed blocks of positions [lo, hi) sit in
 // the device staging buffer in position order; copy each into its slot.
 __global__ __launch_bounds__(256) void stage_scatter_kernel(
-    const int32_t *__restrict__ plan, int row, int C, int n_items, const uint4 *__restrict__ staged,
-    int lo, int hi, uint4 *__restrict__ ws_pool, int S) {
+    const int32_t *__restrict__ plan, int row, int pairs, int C, const uint4 *__restrict__ staged, int lo,
+    int hi, uint4 *__restrict__ ws_pool, int S) {
     constexpr int kVec = (int)(kBlockBytes / sizeof(uint4));
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int rh = item / C;
-        const int i = item - rh * C;
-        const int32_t *p = plan + (size_t)rh * row;
-        if (i >= p[0]) continue;
-        const int k = p[2] + i;
-        if (k < lo || k >= hi) continue;
-        const int slot = p[kPlanHead + 2 * i];
-        if (slot < 0 || slot >= S) continue;
-        const uint4 *src = staged + (size_t)(k - lo) * kVec;
-        uint4 *dst = ws_pool + ((size_t)rh * S + slot) * kVec;
-        const uint4 a = src[threadIdx.x];
-        const uint4 b = src[threadIdx.x + 256];
-        dst[threadIdx.x] = a;
-        dst[threadIdx.x + 256] = b;
-    }
+    const int total = (int)min((long)max(plan[(size_t)pairs * row], 0), (long)pairs * C);
+    hi = min(hi, total);
+    const int n = max(hi - lo, 0);
+    const int per = (n + gridDim.x - 1) / gridDim.x;
+    const int k0 = lo + min(n, (int)blockIdx.x * per), k1 = lo + min(n, (int)blockIdx.x * per + per);
+    copy_positions(plan, row, pairs, C, S, k0, k1, ws_pool, [&](int k, int, int) -> const uint4 * {
+        return staged + (size_t)(k - lo) * kVec;
+    });
 }
 
 }  // namespace
@@ -366,10 +409,10 @@ hipError_t launch_stage_prefix(const oasis_dims &d, const oasis_stage_args &a, h
 hipError_t launch_stage_scatter(const oasis_dims &d, const oasis_stage_args &a, int lo, int hi,
                                 hipStream_t s) {
     if (a.C <= 0 || hi <= lo) return hipSuccess;
-    const int n_items = d.B * d.H_kv * a.C;
-    const int wgs = n_items < 4 * device_cu_count() ? n_items : 4 * device_cu_count();
-    hipLaunchKernelGGL(stage_scatter_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a.plan, plan_row(a.C), a.C,
-                       n_items, reinterpret_cast<const uint4 *>(a.stage_dev), lo, hi,
+    const int cap = 4 * device_cu_count();
+    const int wgs = hi - lo < cap ? hi - lo : cap;
+    hipLaunchKernelGGL(stage_scatter_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a.plan, plan_row(a.C),
+                       d.B * d.H_kv, a.C, reinterpret_cast<const uint4 *>(a.stage_dev), lo, hi,
                        reinterpret_cast<uint4 *>(a.ws_pool), a.S);
     return hipGetLastError();
 }
@@ -377,10 +420,10 @@ hipError_t launch_stage_scatter(const oasis_dims &d, const oasis_stage_args &a, 
 hipError_t launch_stage_gather(const oasis_dims &d, const oasis_stage_args &a,
                                const void *host_pool_dev, hipStream_t s) {
     if (a.C <= 0) return hipSuccess;
-    const int n_items = d.B * d.H_kv * a.C;
-    const int wgs = n_items < kGatherWgs ? n_items : kGatherWgs;
-    hipLaunchKernelGGL(stage_gather_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a.plan, plan_row(a.C), a.C,
-                       n_items, reinterpret_cast<const uint4 *>(host_pool_dev),
+    const long most = (long)d.B * d.H_kv * a.C;  // admits of the step are at most this many
+    const int wgs = most < kGatherWgs ? (int)most : kGatherWgs;
+    hipLaunchKernelGGL(stage_gather_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a.plan, plan_row(a.C),
+                       d.B * d.H_kv, a.C, reinterpret_cast<const uint4 *>(host_pool_dev),
                        reinterpret_cast<uint4 *>(a.ws_pool), d.NB_max, a.S);
     return hipGetLastError();
 }
