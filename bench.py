@@ -302,6 +302,35 @@ def main():
                "copy_engine": args.copy_mode, "drift_frac": round(adm / (B * H_kv) / K_b, 4)}
         del big, dst
 
+    # the same attention launch alone on the GPU (nothing else in flight),
+    # over the last step's working set of layer 0: the kernel's own rate,
+    # beside its rate while sharing the GPU with the pipeline above
+    out_alone = torch.empty_like(pipe.layers[0].out)
+    if staged:
+        tb = pipe.table(0, n_steps - 1)
+        alone = lambda: oa.oasis_sparse_decode_attn(
+            q_attn[n_steps - 1], pipe.layers[0].ws_pool, tb[0], tb[1], tb[2], ctx, out=out_alone,
+            ws=pipe.layers[0].attn_ws, n_split=args.n_split)
+    else:
+        jp = (n_steps - 2) % 2
+        sel, ns = pipe.layers[0].sel[jp], pipe.layers[0].n_sel[jp]
+        alone = lambda: oa.oasis_sparse_decode_attn(
+            q_attn[n_steps - 1], pool, sel, sel, ns, ctx, out=out_alone, ws=pipe.layers[0].attn_ws,
+            n_split=args.n_split)
+    alone()
+    torch.cuda.synchronize()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for _ in range(20):
+        alone()
+    eb.record()
+    torch.cuda.synchronize()
+    alone_us = ea.elapsed_time(eb) / 20 * 1e3
+    kern["attn_alone"] = {"avg_us": round(alone_us, 2), "bytes": attn_bytes,
+                          "GBps": round(attn_bytes / (alone_us * 1e-6) / 1e9, 1),
+                          "frac_of_peak": round(attn_bytes / (alone_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "note": "same launch, alone on the GPU after the timed steps"}
+
     a_us = kern["attn"]["avg_us"]
     achieved = attn_bytes / (a_us * 1e-6) / 1e9
     roofline = {"kernel": "sparse_attn", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -317,7 +317,10 @@ int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q,
  *   main stream (the caller's)   attention of (l, t) over the working set
  *                                staged at (l, t - 1)
  *   compute stream (owned)       scores and top-K of (l, t), staging plan
- *   copy stream (owned)          the copies of (l, t)
+ *   copy streams (owned)         the copies of (l, t); the zero-copy engine
+ *                                alternates two by layer so that one
+ *                                layer's gather tail overlaps the next
+ *                                gather, the DMA engine uses one
  *
  * Per layer the buffers rotate: the attention of step t reads table t % 3,
  * the plan of step t writes table (t + 1) % 3 and uses selection and plan
@@ -399,8 +402,8 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t layer, int32_t step,
  * synchronisation). */
 int oasis_pipeline_drain(oasis_pipeline *p);
 
-/* The pipeline's streams: which = 0 main, 1 compute, 2 copy (NULL when
- * unstaged). */
+/* The pipeline's streams: which = 0 main, 1 compute, 2 and 3 the copy
+ * streams of even and odd layers (NULL where not used). */
 int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
 
 /* Event timing of the steps: capacity > 0 (re)arms timing of up to

@@ -46,7 +46,7 @@ struct oasis_pipeline {
     std::vector<int> next_step;  // per layer: the step the next call must issue
     int device = 0;
     int S = 0;
-    hipStream_t main = nullptr, comp = nullptr, copy = nullptr;
+    hipStream_t main = nullptr, comp = nullptr, copy[2] = {nullptr, nullptr};
     std::vector<hipEvent_t> ev;  // [kind][layer][kRing]
 
     // timing
@@ -195,7 +195,8 @@ void release(oasis_pipeline *p) {
         p->worker.join();
     }
     if (p->comp) (void)hipStreamSynchronize(p->comp);
-    if (p->copy) (void)hipStreamSynchronize(p->copy);
+    for (hipStream_t c : p->copy)
+        if (c) (void)hipStreamSynchronize(c);
     (void)hipStreamSynchronize(p->main);
     for (hipEvent_t e : p->ev)
         if (e) (void)hipEventDestroy(e);
@@ -203,7 +204,8 @@ void release(oasis_pipeline *p) {
         for (hipEvent_t e : v)
             if (e) (void)hipEventDestroy(e);
     if (p->comp) (void)hipStreamDestroy(p->comp);
-    if (p->copy) (void)hipStreamDestroy(p->copy);
+    for (hipStream_t c : p->copy)
+        if (c) (void)hipStreamDestroy(c);
     delete p;
 }
 
@@ -253,8 +255,13 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     if (e != hipSuccess) return fail(e, "hipGetDevice");
     if ((e = hipStreamCreateWithFlags(&p->comp, hipStreamNonBlocking)) != hipSuccess)
         return fail(e, "hipStreamCreateWithFlags");
-    if (ds.staged && (e = hipStreamCreateWithFlags(&p->copy, hipStreamNonBlocking)) != hipSuccess)
-        return fail(e, "hipStreamCreateWithFlags");
+    // copy streams: the zero-copy engine alternates two by layer, so that the
+    // tail of one layer's gather overlaps the start of the next one's; the
+    // DMA engine's copies all go through one (its packing is serial anyway)
+    const int n_copy = !ds.staged ? 0 : (ds.copy_mode == OASIS_COPY_KERNEL ? 2 : 1);
+    for (int c = 0; c < n_copy; c++)
+        if ((e = hipStreamCreateWithFlags(&p->copy[c], hipStreamNonBlocking)) != hipSuccess)
+            return fail(e, "hipStreamCreateWithFlags");
     p->ev.assign((size_t)kEvKinds * ds.n_layers * kRing, nullptr);
     for (auto &x : p->ev)
         if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess)
@@ -359,7 +366,7 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     a.host_threads = ds.host_threads;
     a.copy_mode = ds.copy_mode;
     a.stream = cs;
-    a.copy_stream = p->copy;
+    a.copy_stream = p->copy[p->copy[1] ? (l & 1) : 0];
     a.wait_event = t >= 1 ? p->event(kEvAttn, l, t - 1) : nullptr;
     a.done_event = p->event(kEvStage, l, t);
     a.plan_event = p->event(kEvPlan, l, t);
@@ -392,8 +399,8 @@ int oasis_pipeline_drain(oasis_pipeline *p) {
 int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream) {
     clear_error();
     if (!p || !stream) PFAIL(OASIS_EINVAL, "pipeline or stream is NULL");
-    if (which < 0 || which > 2) PFAIL(OASIS_EINVAL, "which = %d outside [0, 2]", which);
-    *stream = which == 0 ? (void *)p->main : which == 1 ? (void *)p->comp : (void *)p->copy;
+    if (which < 0 || which > 3) PFAIL(OASIS_EINVAL, "which = %d outside [0, 3]", which);
+    *stream = which == 0 ? (void *)p->main : which == 1 ? (void *)p->comp : (void *)p->copy[which - 2];
     return OASIS_OK;
 }
 

@@ -31,12 +31,13 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-// Workgroups of the zero-copy gather.  Its PCIe reads wait microseconds and,
-// while they wait, slow the HBM-bound kernels that run beside them; 32
-// workgroups (256 KiB of reads in flight) still keep the link near its
-// pinned-memcpy rate, and measured over a pipelined decode step fewer or more
-// of them were slower overall.
-constexpr int kGatherWgs = 32;
+// Workgroups of one zero-copy gather.  Its PCIe reads wait microseconds and,
+// while they wait, slow the HBM-bound kernels that run beside them.  The layer
+// pipeline runs the gathers of consecutive layers on two streams, so up to two
+// run at once; 24 workgroups each (up to 384 KiB of reads in flight) keep the
+// link at ~95% of the pinned-memcpy rate, and over a pipelined decode step
+// 16 to 32 measured the same while 48 was 20% slower.
+constexpr int kGatherWgs = 24;
 
 __device__ __forceinline__ int wg_exclusive_scan(int v, int *tmp, int *total) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
@@ -290,24 +291,22 @@ __global__ __launch_bounds__(1024) void stage_prefix_kernel(int32_t *__restrict_
 // admits than C cost nothing.
 
 // The pair holding position k (0 <= k < total): the last pair whose first
-// position is <= k.  Every thread of the workgroup must call it.
+// position is <= k, by binary search over the rows' positions (they are
+// non-decreasing); -1 if even the first row starts after k.  Uniform across
+// the workgroup.
 __device__ int pair_of_position(const int32_t *__restrict__ plan, int row, int pairs, int k) {
-    __shared__ int cnt;
-    if (threadIdx.x == 0) cnt = 0;
-    __syncthreads();
-    int c = 0;
-    for (int rh = threadIdx.x; rh < pairs; rh += blockDim.x) c += plan[(size_t)rh * row + 2] <= k ? 1 : 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-    if ((threadIdx.x & 63) == 0 && c) atomicAdd(&cnt, c);
-    __syncthreads();
-    const int r = cnt - 1;
-    __syncthreads();  // cnt is rewritten by the next call
-    return r;
+    if (plan[2] > k) return -1;
+    int lo = 0, hi = pairs - 1;
+    while (lo < hi) {
+        const int mid = lo + ((hi - lo + 1) >> 1);
+        if (plan[(size_t)mid * row + 2] <= k) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 // Copy the blocks of positions [k0, k1): for each, the source returned by
-// src_of(k, rh, i) into slot `slot` of pair rh.  pairs' admit counts are
+// src_of(k, rh, block) into the admit's slot of pair rh.  pairs' admit counts are
 // clamped to [0, C] and slots to [0, S); a pair index past the rows ends the
 // walk.
 template <class SrcOf>

@@ -10,8 +10,9 @@ include/oasis.h) schedules that chain on one GPU:
   main stream     attention of (layer l, step t), after the transfer of
                   (l, t - 1) only
   compute stream  scores and top-K of (l, t), then the staging plan of (l, t)
-  copy stream     the copies of (l, t) (gather kernel, or DMA copy + scatter
-                  on the pipeline's worker thread)
+  copy streams    the copies of (l, t) (gather kernels on two streams by
+                  layer parity, or DMA copy + scatter on the pipeline's worker
+                  thread)
 
 `LayerPipeline` allocates the per-layer buffers the native pipeline works in
 (three attention tables, two selections and two plan buffers per layer, the
@@ -116,7 +117,8 @@ class LayerPipeline:
             layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)))
         self._h = oa.oasis_pipeline_create(oa.dims(B, H_q, H_kv, NB, D, bs), desc)
         self.comp = torch.cuda.ExternalStream(oa.oasis_pipeline_stream(self._h, 1))
-        self.copy = torch.cuda.ExternalStream(oa.oasis_pipeline_stream(self._h, 2)) if staged else None
+        self.copy = [torch.cuda.ExternalStream(c) for c in
+                     (oa.oasis_pipeline_stream(self._h, k) for k in (2, 3)) if c]
 
     def layer_step(self, l: int, t: int, q_look: torch.Tensor, q_attn: Optional[torch.Tensor]):
         """Enqueue layer l's work of decode step t: the attention of step t
