@@ -304,6 +304,30 @@ int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q,
                              void *ws, size_t ws_bytes, int32_t n_split,
                              void *stream);
 
+/* Look-ahead attention (section 4: the normal query and the draft queries
+ * are computed together over the resident KV).  Exactly
+ * oasis_sparse_decode_attn applied to each of n_q query vectors per request
+ * over the same blocks, in one pass that reads each K / V block once for all
+ * of them:
+ *   q    [B][n_q][H_q][D] bf16, device (e.g. the normal query, then the J
+ *        draft queries)
+ *   out  [B][n_q][H_q][D] bf16, device, written
+ *   lse  [B][n_q][H_q] fp32, device, written; may be NULL
+ *   ws   oasis_lookahead_attn_workspace_bytes(dims, n_q, T, n_split) bytes
+ * The other arguments are those of oasis_sparse_decode_attn; n_q = 1 is that
+ * call.  Requires 1 <= n_q and n_q * H_q / H_kv <= 16 (the query rows of a KV
+ * group fill the 16 columns of one matrix-core tile); more return
+ * OASIS_EUNSUPPORTED. */
+size_t oasis_lookahead_attn_workspace_bytes(const oasis_dims *dims, int32_t n_q,
+                                            int32_t T, int32_t n_split);
+int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
+                         const uint16_t *kv_pool, int32_t P,
+                         const int32_t *tbl_slot, const int32_t *tbl_block,
+                         const int32_t *tbl_n, int32_t T,
+                         const int32_t *ctx_len, float sm_scale,
+                         uint16_t *out, float *lse, void *ws, size_t ws_bytes,
+                         int32_t n_split, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Layer pipeline: the per-layer decode chain, scheduled in native code.
  *

@@ -89,6 +89,10 @@ _SIGNATURES = {
     "oasis_sparse_decode_attn": (ctypes.c_int, [
         ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
         ctypes.c_size_t, _I32, _P]),
+    "oasis_lookahead_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32, _I32, _I32]),
+    "oasis_lookahead_attn": (ctypes.c_int, [
+        ctypes.POINTER(oasis_dims), _I32, _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
+        ctypes.c_size_t, _I32, _P]),
     "oasis_pipeline_create": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_pipeline_desc),
                                              ctypes.POINTER(ctypes.c_void_p)]),
     "oasis_pipeline_layer_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P]),
@@ -376,6 +380,43 @@ def oasis_sparse_decode_attn(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: t
         ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
     _check(_lib.oasis_sparse_decode_attn(
         ctypes.byref(d), _ptr(q), _ptr(kv_pool), int(P), _ptr(tbl_slot), _ptr(tbl_block), _ptr(tbl_n),
+        int(T), _ptr(ctx_len), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), int(n_split), _stream(stream)))
+    return (out, lse) if want_lse or lse is not None else out
+
+
+def oasis_lookahead_attn_workspace_bytes(B: int, H_q: int, H_kv: int, n_q: int, T: int, n_split: int = 0) -> int:
+    d = dims(B, H_q, H_kv, 1)
+    return int(_lib.oasis_lookahead_attn_workspace_bytes(ctypes.byref(d), int(n_q), int(T), int(n_split)))
+
+
+def oasis_lookahead_attn(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: torch.Tensor, tbl_block: torch.Tensor,
+                         tbl_n: torch.Tensor, ctx_len: torch.Tensor, sm_scale: Optional[float] = None, out=None,
+                         lse=None, ws=None, n_split: int = 0, want_lse: bool = False, stream=None):
+    """q bf16 [B][n_q][H_q][D] (the normal query and the drafts), kv_pool bf16
+    [B][H_kv][P][2][bs][D], tables int32 [B][H_kv][T] and [B][H_kv] ->
+    out bf16 [B][n_q][H_q][D] (and lse fp32 [B][n_q][H_q])."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 6)
+    _need(tbl_slot, "tbl_slot", torch.int32, 3)
+    _need(tbl_block, "tbl_block", torch.int32, 3)
+    _need(tbl_n, "tbl_n", torch.int32, 2)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    B, n_q, H_q, D = q.shape
+    _, H_kv, P, _, bs, _ = kv_pool.shape
+    T = tbl_slot.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, n_q, H_q, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n_q, H_q), dtype=torch.float32, device=q.device)
+    d = dims(B, H_q, H_kv, max(P, 1), D, bs)
+    need = int(_lib.oasis_lookahead_attn_workspace_bytes(ctypes.byref(d), int(n_q), T, int(n_split)))
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _check(_lib.oasis_lookahead_attn(
+        ctypes.byref(d), int(n_q), _ptr(q), _ptr(kv_pool), int(P), _ptr(tbl_slot), _ptr(tbl_block), _ptr(tbl_n),
         int(T), _ptr(ctx_len), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), int(n_split), _stream(stream)))
     return (out, lse) if want_lse or lse is not None else out

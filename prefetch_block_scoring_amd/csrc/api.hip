@@ -316,7 +316,12 @@ int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *a) {
 
 size_t oasis_attn_workspace_bytes(const oasis_dims *dims, int32_t T, int32_t n_split) {
     if (check_dims(dims) != OASIS_OK || T < 0 || n_split < 0) return 0;
-    return attn_ws_bytes(*dims, T, n_split);
+    return attn_ws_bytes(*dims, 1, T, n_split);
+}
+
+size_t oasis_lookahead_attn_workspace_bytes(const oasis_dims *dims, int32_t n_q, int32_t T, int32_t n_split) {
+    if (check_dims(dims) != OASIS_OK || n_q < 1 || T < 0 || n_split < 0) return 0;
+    return attn_ws_bytes(*dims, n_q, T, n_split);
 }
 
 int32_t oasis_attn_num_splits(const oasis_dims *dims, int32_t T, int32_t n_split) {
@@ -324,13 +329,17 @@ int32_t oasis_attn_num_splits(const oasis_dims *dims, int32_t T, int32_t n_split
     return attn_splits(*dims, T, n_split);
 }
 
-int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q, const uint16_t *kv_pool, int32_t P,
-                             const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n, int32_t T,
-                             const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,
-                             size_t ws_bytes, int32_t n_split, void *stream) {
+int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q, const uint16_t *kv_pool,
+                         int32_t P, const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n,
+                         int32_t T, const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,
+                         size_t ws_bytes, int32_t n_split, void *stream) {
     clear_error();
     int rc = check_dims(dims);
     if (rc) return rc;
+    if (n_q < 1) FAIL(OASIS_EINVAL, "n_q = %d < 1", n_q);
+    if ((int64_t)n_q * (dims->H_q / dims->H_kv) > kMaxG)
+        FAIL(OASIS_EUNSUPPORTED, "n_q * H_q / H_kv = %lld (at most %d)",
+             (long long)n_q * (dims->H_q / dims->H_kv), kMaxG);
     if (P < 1) FAIL(OASIS_EINVAL, "P = %d < 1", P);
     if (T < 0) FAIL(OASIS_EINVAL, "T = %d < 0", T);
     if (n_split < 0 || n_split > 64) FAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", n_split);
@@ -346,14 +355,22 @@ int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q, const ui
         NEED(tbl_block);
     }
     const int splits = attn_splits(*dims, T, n_split);
-    const size_t need = attn_ws_bytes(*dims, T, n_split);
+    const size_t need = attn_ws_bytes(*dims, n_q, T, n_split);
     if (need > 0) {
         NEED(ws);
         if (ws_bytes < need) FAIL(OASIS_ENOSPACE, "attention workspace %zu bytes < %zu", ws_bytes, need);
     }
-    OASIS_HIP(launch_attn(*dims, q, kv_pool, P, tbl_slot, tbl_block, tbl_n, T, ctx_len, sm_scale, out, lse,
+    OASIS_HIP(launch_attn(*dims, n_q, q, kv_pool, P, tbl_slot, tbl_block, tbl_n, T, ctx_len, sm_scale, out, lse,
                           static_cast<float *>(ws), splits, static_cast<hipStream_t>(stream)));
     return OASIS_OK;
+}
+
+int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q, const uint16_t *kv_pool, int32_t P,
+                             const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n, int32_t T,
+                             const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,
+                             size_t ws_bytes, int32_t n_split, void *stream) {
+    return oasis_lookahead_attn(dims, 1, q, kv_pool, P, tbl_slot, tbl_block, tbl_n, T, ctx_len, sm_scale, out, lse,
+                                ws, ws_bytes, n_split, stream);
 }
 
 }  // extern "C"

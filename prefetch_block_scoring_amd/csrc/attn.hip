@@ -4,6 +4,12 @@
 // attention runs only over the KV blocks held in the HBM working set.  For each
 // query head, softmax attention over the valid tokens of the listed blocks.
 //
+// Look-ahead attention (section 4: the normal and the draft queries are
+// computed together over the resident KV) is the same kernel with n_q query
+// vectors per request: the MFMA's 16 columns hold the n_q * G (query, head)
+// pairs of the KV group, column c = query (c / G), head (c % G), and every
+// K / V load serves all of them.  Plain decode attention is n_q = 1.
+//
 // Work split: a workgroup of four waves owns one (request, KV head) and one of
 // n_split contiguous ranges of its table; the waves take the range's entries
 // round-robin and keep private online-softmax states, merged in LDS at the end;
@@ -11,16 +17,26 @@
 //
 // Per 16-token block (8 KiB of K and V) a wave does:
 //   q . K   on the matrix cores: one v_mfma_f32_16x16x32_bf16 per 32 dims,
-//           A = K (16 tokens x 32 dims), B = Q^T (32 dims x 16 head slots, the
-//           group's G heads, the rest zero).  The G heads of a KV group share
-//           every K load, and the MFMA replaces G * 128 VALU FMAs per token.
+//           A = K (16 tokens x 32 dims), B = Q^T (32 dims x 16 columns, the
+//           group's n_q * G query rows, the rest zero).  The columns share
+//           every K load, and the MFMA replaces n_q * G * 128 VALU FMAs per
+//           token.
 //           Each lane loads 16 bytes of one key row per MFMA; since the sum
 //           over dims may be taken in any order, A and B only have to agree on
 //           which dims a lane brings.
 //   softmax fp32, base-2 online max / sum per head on the MFMA output.
-//   p . V   on the VALU: lane (c, q) owns dims [8c, 8c + 8) of tokens
-//           q, q + 4, q + 8, q + 12; each V load is a fully used 1 KiB row
-//           group; the four token groups are summed once at the end.
+//   p . V   up to 8 columns (attn_kernel): on the VALU; lane (c, q) owns
+//           dims [8c, 8c + 8) of tokens q, q + 4, q + 8, q + 12, each V load
+//           is a fully used 1 KiB row group, and the four token groups are
+//           summed once at the end.  VALU work and accumulator registers
+//           grow with the columns (8 per column per lane).
+//           9 to 16 columns (attn_pv_kernel): on the matrix cores,
+//           O^T[dims][columns] += V^T[dims][16 tokens] P[16 tokens][columns]
+//           with v_mfma_f32_16x16x16_bf16.  The logits' MFMA output already
+//           is P in the B-operand layout; V is transposed through a 5 KiB
+//           LDS tile per wave; p enters as two bf16 parts (hi + lo).  The
+//           accumulator is 32 registers for any column count, so 16 columns
+//           run at four waves per SIMD, at the cost of one column.
 // Loads of the next block are issued before the current block is computed.
 #include "oasis_internal.h"
 
@@ -47,7 +63,7 @@ struct AttnArgs {
     int T;
     const int32_t *ctx_len;
     float scale_log2;  // sm_scale * log2(e)
-    int H_q, H_kv, n_split;
+    int H_q, H_kv, n_q, n_split;
     uint16_t *out;
     float *lse;
     float *ws;
@@ -55,12 +71,13 @@ struct AttnArgs {
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// GP: head slots compiled in (a power of two >= G); G = H_q / H_kv at run time.
-// Waves per SIMD the kernel is compiled for: four for up to four heads per
-// group (1024 workgroups of the 8-KV-head layers at batch 128 then fit the
-// 256 compute units in one round); the larger head counts need the registers.
+// GP: columns compiled in (a power of two >= n_q * G, at most 8); G = H_q /
+// H_kv at run time.  Waves per SIMD the kernel is compiled for: four for up
+// to four columns (1024 workgroups of the 8-KV-head layers at batch 128 then
+// fit the 256 compute units in one round); eight columns need the registers
+// of two.  More columns run in attn_pv_kernel below.
 template <int GP>
-constexpr int attn_waves_per_simd() { return GP <= 4 ? 4 : (GP <= 8 ? 2 : 1); }
+constexpr int attn_waves_per_simd() { return GP <= 4 ? 4 : 2; }
 
 template <int GP>
 __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kernel(AttnArgs a) {
@@ -82,6 +99,7 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     const int col = lane & 15;  // MFMA row / column index
     const int grp = lane >> 4;  // lane group 0..3
     const int G = a.H_q / a.H_kv;
+    const int NC = a.n_q * G;  // columns in use
 
     const int ctx = a.ctx_len[r];
     const int nb = ctx <= 0 ? 0 : (ctx + kBs - 1) / kBs;
@@ -91,16 +109,19 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     const int i0 = split * per;
     const int i1 = min(n, i0 + per);
 
-    // Q^T as the MFMA B operand: lane (col, grp) brings head `col`, dims
-    // kk * 32 + grp * 8 + [0, 8) for k-step kk; staged once in LDS (head
-    // slots past G are zero) and read back per block, which keeps registers
+    // Q^T as the MFMA B operand: lane (col, grp) brings column `col`, dims
+    // kk * 32 + grp * 8 + [0, 8) for k-step kk; staged once in LDS (columns
+    // past n_q * G are zero) and read back per block, which keeps registers
     // for the loads in flight.
     {
-        const int hs = tid >> 4, chunk = tid & 15;  // 256 threads = 16 head slots x 16 chunks
+        const int c = tid >> 4, chunk = tid & 15;  // 256 threads = 16 columns x 16 chunks
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (hs < G)
-            v = reinterpret_cast<const uint4 *>(a.q + ((size_t)r * a.H_q + (size_t)h * G + hs) * kD)[chunk];
-        q_lds[hs][chunk] = v;
+        if (c < NC) {
+            const int qi = c / G, g = c - qi * G;
+            v = reinterpret_cast<const uint4 *>(
+                a.q + (((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + g) * kD)[chunk];
+        }
+        q_lds[c][chunk] = v;
     }
     __syncthreads();
 
@@ -154,7 +175,7 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
         uint4 kn[4], vn[4];
         if (src_n) load(src_n, kn, vn);
 
-        // logits of head `col` for tokens 4 * grp + [0, 4)
+        // logits of column `col` for tokens 4 * grp + [0, 4)
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; kk++)
@@ -253,9 +274,9 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     }
     __syncthreads();
 
-    // merge the waves; one thread per (head, dim)
-    for (int idx = tid; idx < G * kD; idx += kThreads) {
-        const int g = idx / kD, d = idx - g * kD;
+    // merge the waves; one thread per (column, dim)
+    for (int idx = tid; idx < NC * kD; idx += kThreads) {
+        const int g = idx / kD, d = idx - g * kD;  // g: column
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) M = fmaxf(M, m_lds[w][g]);
@@ -269,7 +290,247 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
                 L += f * l_lds[w][g];
             }
         }
-        const size_t row = (size_t)r * a.H_q + (size_t)h * G + g;
+        const int qi = g / G;
+        const size_t row = ((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + (g - qi * G);
+        if (a.n_split == 1) {
+            a.out[row * kD + d] = f32_to_bf16(L > 0.f ? o / L : 0.f);
+            if (d == 0 && a.lse)
+                a.lse[row] = (M == -INFINITY || !(L > 0.f)) ? -INFINITY : (M + __log2f(L)) * kLn2;
+        } else {
+            float *part = a.ws + (row * a.n_split + split) * (kD + 2);
+            part[d] = o;
+            if (d == 0) {
+                part[kD] = M;
+                part[kD + 1] = L;
+            }
+        }
+    }
+}
+
+// V^T tile of one block in LDS, per wave: [128 dims][16 tokens + 4 pad]
+// halfwords, so that a lane's four tokens of one dim are 8 aligned bytes.
+constexpr int kVtStride = 20;
+constexpr int kVtBytes = kD * kVtStride * 2;                 // 5 KiB per wave
+constexpr int kOBytes = 16 * kD * 4;                          // 8 KiB per wave
+constexpr int kScratchBytes = kWaves * (kVtBytes > kOBytes ? kVtBytes : kOBytes);
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
+    // Q^T in the MFMA B layout, one 16-byte chunk per (column, 8 dims); rows
+    // padded by 16 bytes so the 16 columns fall in distinct banks
+    __shared__ uint4 q_lds[16][17];
+    __shared__ float m_lds[kWaves][16];
+    __shared__ float l_lds[kWaves][16];
+    // per wave: V^T of the current block inside the loop, then the wave's
+    // unnormalised output [16 columns][128 dims] for the merge
+    __shared__ __attribute__((aligned(16))) unsigned char scratch[kScratchBytes];
+
+    const int rh = blockIdx.x;
+    const int split = blockIdx.y;
+    const int r = rh / a.H_kv;
+    const int h = rh - r * a.H_kv;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;  // MFMA row / column index
+    const int grp = lane >> 4;  // lane group 0..3
+    const int G = a.H_q / a.H_kv;
+    const int NC = a.n_q * G;  // columns in use
+
+    const int ctx = a.ctx_len[r];
+    const int nb = ctx <= 0 ? 0 : (ctx + kBs - 1) / kBs;
+    int n = a.tbl_n[rh];
+    n = n < 0 ? 0 : (n > a.T ? a.T : n);
+    const int per = (n + a.n_split - 1) / a.n_split;
+    const int i0 = split * per;
+    const int i1 = min(n, i0 + per);
+
+    // Q^T as the MFMA B operand: lane (col, grp) brings column `col`, dims
+    // kk * 32 + grp * 8 + [0, 8) for k-step kk; staged once in LDS (columns
+    // past n_q * G are zero) and read back per block, which keeps registers
+    // for the loads in flight.
+    {
+        const int c = tid >> 4, chunk = tid & 15;  // 256 threads = 16 columns x 16 chunks
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (c < NC) {
+            const int qi = c / G, g = c - qi * G;
+            v = reinterpret_cast<const uint4 *>(
+                a.q + (((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + g) * kD)[chunk];
+        }
+        q_lds[c][chunk] = v;
+    }
+    __syncthreads();
+
+    // output accumulator in the MFMA C layout: acc[tt][e] = O^T[dim tt * 16 +
+    // 4 * grp + e][column col], so every value of a lane belongs to its own
+    // column and the rescale needs no exchange
+    f32x4 acc[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; tt++) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int32_t *ts = a.tbl_slot + (size_t)rh * a.T;
+    const int32_t *tb = a.tbl_block + (size_t)rh * a.T;
+    const uint4 *pool = reinterpret_cast<const uint4 *>(a.kv) + (size_t)rh * a.P * kVecPerBlock;
+    uint16_t(*vt)[kVtStride] = reinterpret_cast<uint16_t(*)[kVtStride]>(scratch + wave * kVtBytes);
+
+    // next valid entry at or after i (wave-uniform); returns nullptr if none
+    auto next_valid = [&](int i, int &blk) -> const uint4 * {
+        for (; i < i1; i += kWaves) {
+            const int s = ts[i], b = tb[i];
+            if (s >= 0 && s < a.P && b >= 0 && b < nb) {
+                blk = b;
+                return pool + (size_t)s * kVecPerBlock;
+            }
+        }
+        return nullptr;
+    };
+    auto load = [&](const uint4 *src, uint4 (&kr)[4], uint4 (&vr)[4]) {
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) kr[kk] = src[col * 16 + kk * 4 + grp];
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) vr[qq] = src[256 + (qq * 4 + grp) * 16 + col];
+    };
+
+    int i = i0 + wave;
+    int blk_c = 0;
+    const uint4 *src_c = nullptr;
+    for (; i < i1; i += kWaves) {
+        const int s = ts[i], b = tb[i];
+        if (s >= 0 && s < a.P && b >= 0 && b < nb) {
+            blk_c = b;
+            src_c = pool + (size_t)s * kVecPerBlock;
+            break;
+        }
+    }
+    uint4 kc[4], vc[4];
+    if (src_c) load(src_c, kc, vc);
+
+    while (src_c) {
+        int blk_n = 0;
+        const uint4 *src_n = next_valid(i + kWaves, blk_n);
+        uint4 kn[4], vn[4];
+        if (src_n) load(src_n, kn, vn);
+
+        // V^T into this wave's LDS tile: lane (col, grp) holds token
+        // qq * 4 + grp, dims col * 8 + [0, 8) of vc[qq]
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) {
+            const uint32_t w[4] = {vc[qq].x, vc[qq].y, vc[qq].z, vc[qq].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                vt[col * 8 + 2 * e][qq * 4 + grp] = (uint16_t)(w[e] & 0xffffu);
+                vt[col * 8 + 2 * e + 1][qq * 4 + grp] = (uint16_t)(w[e] >> 16);
+            }
+        }
+
+        // logits of column `col` for tokens 4 * grp + [0, 4)
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[kk]),
+                                                         __builtin_bit_cast(bf16x8, q_lds[col][kk * 4 + grp]), c,
+                                                         0, 0, 0);
+        const int valid = ctx - blk_c * kBs;
+        float sv[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) sv[t] = (4 * grp + t < valid) ? c[t] * a.scale_log2 : -INFINITY;
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_(m_run - m_use);
+        // p goes to the matrix cores as two bf16 parts, p = hi + lo with
+        // hi = bf16(p) and lo = bf16(p - hi), so the weights keep ~17
+        // significant bits (one bf16 alone, 2^-9, is too coarse for outputs
+        // near zero) and each bf16 x bf16 product is exact in the fp32
+        // accumulator
+        s16x4 pb_hi, pb_lo;
+        float psum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const float p = exp2_(sv[t] - m_use);
+            const uint16_t hi = f32_to_bf16(p);
+            pb_hi[t] = (short)hi;
+            pb_lo[t] = (short)f32_to_bf16(p - __uint_as_float((uint32_t)hi << 16));
+            psum += p;
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // p . V on the matrix cores: O^T[dims][columns] += V^T[dims][tokens]
+        // P[tokens][columns]; A = the V^T tile rows tt * 16 + col, tokens
+        // 4 * grp + [0, 4); B = P (hi, then lo), already in the B layout
+        // (the logits' output layout)
+#pragma unroll
+        for (int tt = 0; tt < 8; tt++) {
+            const uint2 av = *reinterpret_cast<const uint2 *>(&vt[tt * 16 + col][4 * grp]);
+            const s16x4 va = __builtin_bit_cast(s16x4, av);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi, acc[tt] * alpha, 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo, acc[tt], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        if (!src_n) break;
+        // advance: the entry just prefetched becomes current
+        {
+            int j = i + kWaves;
+            for (; j < i1; j += kWaves) {
+                const int s = ts[j], b = tb[j];
+                if (s >= 0 && s < a.P && b >= 0 && b < nb) break;
+            }
+            i = j;
+        }
+        src_c = src_n;
+        blk_c = blk_n;
+#pragma unroll
+        for (int x = 0; x < 4; x++) {
+            kc[x] = kn[x];
+            vc[x] = vn[x];
+        }
+    }
+
+    // the denominator: sum the four token groups of the column
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    __syncthreads();  // every wave is done with its V^T tile
+    float(*o_lds)[kD] = reinterpret_cast<float(*)[kD]>(scratch + wave * kOBytes);
+#pragma unroll
+    for (int tt = 0; tt < 8; tt++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) o_lds[col][tt * 16 + 4 * grp + e] = acc[tt][e];
+    if (grp == 0) {
+        m_lds[wave][col] = m_run;
+        l_lds[wave][col] = l_run;
+    }
+    __syncthreads();
+
+    // merge the waves; one thread per (column, dim)
+    for (int idx = tid; idx < NC * kD; idx += kThreads) {
+        const int g = idx / kD, d = idx - g * kD;  // g: column
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) M = fmaxf(M, m_lds[w][g]);
+        float o = 0.f, L = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) {
+                const float mw = m_lds[w][g];
+                const float f = (mw == -INFINITY) ? 0.f : exp2_(mw - M);
+                o += f * reinterpret_cast<const float(*)[kD]>(scratch + w * kOBytes)[g][d];
+                L += f * l_lds[w][g];
+            }
+        }
+        const int qi = g / G;
+        const size_t row = ((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + (g - qi * G);
         if (a.n_split == 1) {
             a.out[row * kD + d] = f32_to_bf16(L > 0.f ? o / L : 0.f);
             if (d == 0 && a.lse)
@@ -330,13 +591,13 @@ int attn_splits(const oasis_dims &d, int T, int n_split) {
     return (int)s;
 }
 
-size_t attn_ws_bytes(const oasis_dims &d, int T, int n_split) {
+size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split) {
     const int s = attn_splits(d, T, n_split);
     if (s <= 1) return 0;
-    return (size_t)d.B * d.H_q * s * (kD + 2) * sizeof(float);
+    return (size_t)d.B * n_q * d.H_q * s * (kD + 2) * sizeof(float);
 }
 
-hipError_t launch_attn(const oasis_dims &d, const uint16_t *q, const uint16_t *kv_pool, int P,
+hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q, const uint16_t *kv_pool, int P,
                        const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n,
                        int T, const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse,
                        float *ws, int n_split, hipStream_t s) {
@@ -352,19 +613,24 @@ hipError_t launch_attn(const oasis_dims &d, const uint16_t *q, const uint16_t *k
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     a.H_q = d.H_q;
     a.H_kv = d.H_kv;
+    a.n_q = n_q;
     a.n_split = n_split;
     a.out = out;
     a.lse = lse;
     a.ws = ws;
-    const int G = d.H_q / d.H_kv;
+    const int NC = n_q * (d.H_q / d.H_kv);
     hipError_t e;
-    if (G <= 1) e = launch_g<1>(d, a, s);
-    else if (G <= 2) e = launch_g<2>(d, a, s);
-    else if (G <= 4) e = launch_g<4>(d, a, s);
-    else if (G <= 8) e = launch_g<8>(d, a, s);
-    else e = launch_g<16>(d, a, s);
+    if (NC <= 1) e = launch_g<1>(d, a, s);
+    else if (NC <= 2) e = launch_g<2>(d, a, s);
+    else if (NC <= 4) e = launch_g<4>(d, a, s);
+    else if (NC <= 8) e = launch_g<8>(d, a, s);
+    else {
+        dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)n_split);
+        hipLaunchKernelGGL(attn_pv_kernel, grid, dim3(kThreads), 0, s, a);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess || n_split <= 1) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(d.B * d.H_q)), dim3(kD), 0, s, ws,
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(d.B * n_q * d.H_q)), dim3(kD), 0, s, ws,
                        n_split, out, lse);
     return hipGetLastError();
 }

@@ -67,9 +67,11 @@ hipError_t launch_stage_gather(const oasis_dims &d, const oasis_stage_args &a,
                                const void *host_pool_dev, hipStream_t s);
 
 int attn_splits(const oasis_dims &d, int T, int n_split);
-size_t attn_ws_bytes(const oasis_dims &d, int T, int n_split);
+// split-K workspace for n_q queries per request
+size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split);
 
-hipError_t launch_attn(const oasis_dims &d, const uint16_t *q,
+// n_q queries per request, q / out [B][n_q][H_q][D]; n_q * G <= kMaxG
+hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q,
                        const uint16_t *kv_pool, int P, const int32_t *tbl_slot,
                        const int32_t *tbl_block, const int32_t *tbl_n, int T,
                        const int32_t *ctx_len, float sm_scale, uint16_t *out,

@@ -217,3 +217,17 @@ def test_pipeline_calls_reject_null_handles():
     assert lib.oasis_pipeline_drain(None) == oa.OASIS_EINVAL
     assert lib.oasis_pipeline_timing(None, 4) == oa.OASIS_EINVAL
     assert lib.oasis_pipeline_destroy(None) == oa.OASIS_OK
+
+
+def test_lookahead_attention_argument_errors():
+    lib = binding.library()
+    d = oa.dims(2, 32, 8, 64)     # G = 4
+    call = lambda n_q, n_split=0: lib.oasis_lookahead_attn(ctypes.byref(d), n_q, None, None, 8, None, None, None, 4,
+                                                           None, 0.1, None, None, None, 0, n_split, None)
+    assert call(0) == oa.OASIS_EINVAL
+    assert call(5) == oa.OASIS_EUNSUPPORTED      # 5 * 4 = 20 columns > 16
+    assert call(4, n_split=65) == oa.OASIS_EINVAL
+    assert call(4) == oa.OASIS_EINVAL            # then the NULL pointers
+    assert oa.oasis_lookahead_attn_workspace_bytes(2, 32, 8, 3, 128, 3) == 2 * 3 * 32 * 3 * 130 * 4
+    assert oa.oasis_lookahead_attn_workspace_bytes(2, 32, 8, 1, 128, 3) == oa.oasis_attn_workspace_bytes(
+        2, 32, 8, 128, 3)
