@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--copy-mode", choices=["kernel", "dma"], default="kernel")
     p.add_argument("--host-threads", type=int, default=8, help="packing threads of the DMA copy engine")
     p.add_argument("--n-split", type=int, default=0)
+    p.add_argument("--joint", action="store_true",
+                   help="look-ahead attention: the normal query and the step's J draft queries attend together")
     p.add_argument("--cap", type=float, default=None,
                    help="override the staged workload's fetch cap (fraction of the budget; >= 1 = fetch-all)")
     p.add_argument("--drift", type=float, default=None,
@@ -213,12 +215,17 @@ def main():
     n_look = n_steps + 3 * (L - 1)
     q_look = [wl.lookahead(w, s, dev) for s in range(n_look)]
     q_attn = [q_look[max(s - 1, 0)][:, 0].contiguous() for s in range(n_look)]
+    n_q = 1 + w.J if args.joint else 1
+    if args.joint:
+        # the normal query, then the draft queries that score this step's blocks
+        q_attn = [torch.cat([q_attn[s][:, None], q_look[s]], dim=1).contiguous() for s in range(n_look)]
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t_setup:.1f}s")
 
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
     pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=H_q, K_b=K_b, C=C, n_layers=L, staged=staged,
-                         copy_mode=copy_mode, host_threads=args.host_threads, n_split=args.n_split, J=w.J)
+                         copy_mode=copy_mode, host_threads=args.host_threads, n_split=args.n_split, J=w.J,
+                         n_q=n_q)
     T = K_b
     splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
     admitted = torch.zeros((), dtype=torch.int64, device=dev)
@@ -263,7 +270,8 @@ def main():
     else:
         tn = pipe.layers[0].n_sel[(n_steps - 2) % 2]
     n_entries = int(tn.sum())
-    attn_bytes = (n_entries * 2 * bs * D * 2 + 2 * B * H_q * D * 2 + B * H_kv * T * 8 + B * H_kv * 4 + B * 4)
+    attn_bytes = (n_entries * 2 * bs * D * 2 + 2 * n_q * B * H_q * D * 2 + B * H_kv * T * 8 + B * H_kv * 4
+                  + B * 4)
     n_blocks_total = int(sum(-(-int(c) // bs) for c in ctx_cpu)) * H_kv
     score_bytes = n_blocks_total * 2 * D * 2 + B * H_kv * NB * 4 + q_look[0].numel() * 2 + B * 4
     topk_bytes = n_blocks_total * 4 + B * H_kv * (K_b + 1) * 4 + B * 4
@@ -305,18 +313,18 @@ def main():
     # the same attention launch alone on the GPU (nothing else in flight),
     # over the last step's working set of layer 0: the kernel's own rate,
     # beside its rate while sharing the GPU with the pipeline above
-    out_alone = torch.empty_like(pipe.layers[0].out)
+    q4 = q_attn[n_steps - 1].view(B, n_q, H_q, D)
+    out_alone = torch.empty_like(q4)
     if staged:
         tb = pipe.table(0, n_steps - 1)
-        alone = lambda: oa.oasis_sparse_decode_attn(
-            q_attn[n_steps - 1], pipe.layers[0].ws_pool, tb[0], tb[1], tb[2], ctx, out=out_alone,
-            ws=pipe.layers[0].attn_ws, n_split=args.n_split)
+        alone = lambda: oa.oasis_lookahead_attn(
+            q4, pipe.layers[0].ws_pool, tb[0], tb[1], tb[2], ctx, out=out_alone, ws=pipe.layers[0].attn_ws,
+            n_split=args.n_split)
     else:
         jp = (n_steps - 2) % 2
         sel, ns = pipe.layers[0].sel[jp], pipe.layers[0].n_sel[jp]
-        alone = lambda: oa.oasis_sparse_decode_attn(
-            q_attn[n_steps - 1], pool, sel, sel, ns, ctx, out=out_alone, ws=pipe.layers[0].attn_ws,
-            n_split=args.n_split)
+        alone = lambda: oa.oasis_lookahead_attn(
+            q4, pool, sel, sel, ns, ctx, out=out_alone, ws=pipe.layers[0].attn_ws, n_split=args.n_split)
     alone()
     torch.cuda.synchronize()
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -368,6 +376,7 @@ def main():
                    "head_dim": D, "block_tokens": bs, "kv_budget_tokens": w.budget, "lookahead_queries": w.J,
                    "fetch_cap": w.cap, "fetch_cap_blocks": C, "slots": S if staged else None,
                    "drift": w.drift if w.structure == "drift" else None,
+                   "attention_queries": n_q,
                    "layers_in_flight": L, "step_unit": "layer-step",
                    "kv_location": "pinned host pool + HBM working set" if staged else "HBM",
                    "copy_engine": args.copy_mode if staged else None,
@@ -444,8 +453,9 @@ def _cpu_model():
 
 def check_against_oracle(w, pool, ctx_cpu, q_attn, pipe, n_steps):
     """Sampled parity at full size: requests 0 and B-1 of every layer's last
-    step, against the oracle's attention over the same resident blocks (the
-    staging itself is checked against the oracle in the test suite)."""
+    step, against the oracle's attention over the same resident blocks, each
+    attention query on its own (the staging itself is checked against the
+    oracle in the test suite)."""
     import numpy as np
     import torch
     import oracle
@@ -462,11 +472,15 @@ def check_against_oracle(w, pool, ctx_cpu, q_attn, pipe, n_steps):
         tb = pipe.table(l, t)
         blocks = tb[1].cpu().numpy()[rs]
         n = tb[2].cpu().numpy()[rs]
-        ref, _ = oracle.attend(u16(q_attn[t + 3 * l][rs]), kv, ctx, blocks, n, 1 / math.sqrt(w.D))
+        qa = q_attn[t + 3 * l][rs]
         got = (u16(pipe.layers[l].out[rs]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        bad = np.abs(got - ref) > 2e-3 + 1e-2 * np.abs(ref)
-        bad_total += int(bad.sum())
-        n_total += bad.size
+        if qa.dim() == 3:          # one query per request
+            qa, got = qa[:, None], got[:, None]
+        for qi in range(qa.shape[1]):  # look-ahead attention: each query on its own
+            ref, _ = oracle.attend(u16(qa[:, qi]), kv, ctx, blocks, n, 1 / math.sqrt(w.D))
+            bad = np.abs(got[:, qi] - ref) > 2e-3 + 1e-2 * np.abs(ref)
+            bad_total += int(bad.sum())
+            n_total += bad.size
         # the resident blocks themselves: every slot holds its block's bytes
         ly = pipe.layers[l]
         ws = ly.ws_pool

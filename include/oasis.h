@@ -363,7 +363,8 @@ typedef struct oasis_layer_buffers {
     float *scores;            /* [B][H_kv][NB_max] fp32, device */
     int32_t *sel[2];          /* [B][H_kv][K_b] int32, device */
     int32_t *n_sel[2];        /* [B][H_kv] int32, device */
-    void *attn_ws;            /* oasis_attn_workspace_bytes(dims, K_b, n_split) */
+    void *attn_ws;            /* oasis_lookahead_attn_workspace_bytes(dims,
+                                 n_q, K_b, n_split) bytes */
     size_t attn_ws_bytes;
     /* staged pipelines only (ignored otherwise) */
     uint16_t *ws_pool;        /* [B][H_kv][K_b + C][2][bs][D] bf16, device */
@@ -386,6 +387,11 @@ typedef struct oasis_pipeline_desc {
     int32_t C;                /* fetch cap in blocks per (r, h) per step
                                  (staged; step 0 fills uncapped) */
     int32_t J;                /* lookahead queries per request */
+    int32_t n_q;              /* attention queries per request: 1 = decode
+                                 attention; 1 + J = look-ahead attention of
+                                 the normal and the draft queries
+                                 (oasis_lookahead_attn; n_q * H_q / H_kv
+                                 <= 16) */
     int32_t staged;           /* 1: pool is pinned host memory staged into
                                  per-layer working sets; 0: pool in HBM */
     int32_t copy_mode;        /* OASIS_COPY_KERNEL or OASIS_COPY_DMA */
@@ -409,10 +415,10 @@ int oasis_pipeline_create(const oasis_dims *dims,
                           oasis_pipeline **out);
 
 /* Enqueues layer `layer`'s work of decode step `step`: the attention of
- * step t (query q_attn [B][H_q][D] bf16, device; output out [B][H_q][D] bf16
- * and lse [B][H_q] fp32 (may be NULL), device; skipped at t = 0 where
- * q_attn and out may be NULL) and the prediction and staging for step t + 1
- * from q_look [B][J][H_q][D] bf16, device.  Steps of one layer must be
+ * step t (queries q_attn [B][n_q][H_q][D] bf16, device; output out
+ * [B][n_q][H_q][D] bf16 and lse [B][n_q][H_q] fp32 (may be NULL), device;
+ * skipped at t = 0 where q_attn and out may be NULL) and the prediction and
+ * staging for step t + 1 from q_look [B][J][H_q][D] bf16, device.  Steps of one layer must be
  * issued in order 0, 1, 2, ... (OASIS_EINVAL otherwise); layers may
  * interleave freely.  Inputs must stay valid until the work completes.
  * Blocks the caller only while the DMA worker has not yet enqueued the

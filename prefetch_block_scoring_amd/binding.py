@@ -64,7 +64,8 @@ class oasis_layer_buffers(ctypes.Structure):
 
 class oasis_pipeline_desc(ctypes.Structure):
     _fields_ = [
-        ("n_layers", _I32), ("K_b", _I32), ("C", _I32), ("J", _I32), ("staged", _I32), ("copy_mode", _I32),
+        ("n_layers", _I32), ("K_b", _I32), ("C", _I32), ("J", _I32), ("n_q", _I32), ("staged", _I32),
+        ("copy_mode", _I32),
         ("host_threads", _I32), ("n_split", _I32), ("sm_scale", ctypes.c_float), ("pool", _P),
         ("kminmax", _P), ("ctx_len", _P), ("main_stream", _P), ("layers", ctypes.POINTER(oasis_layer_buffers))]
 
@@ -435,11 +436,12 @@ def oasis_pipeline_create(d: oasis_dims, desc: oasis_pipeline_desc) -> int:
 def oasis_pipeline_layer_step(h: int, layer: int, step: int, q_look: torch.Tensor,
                               q_attn: Optional[torch.Tensor], out: Optional[torch.Tensor],
                               lse: Optional[torch.Tensor] = None):
-    """One layer-step: q_look bf16 [B][J][H_q][D], q_attn bf16 [B][H_q][D]
-    (unused at step 0), out bf16 [B][H_q][D], lse fp32 [B][H_q] or None."""
+    """One layer-step: q_look bf16 [B][J][H_q][D], q_attn bf16 [B][n_q][H_q][D]
+    (or [B][H_q][D] when n_q = 1; unused at step 0), out bf16 of q_attn's
+    shape, lse fp32 [B][n_q][H_q] or None."""
     _need(q_look, "q_look", torch.bfloat16, 4)
     if q_attn is not None:
-        _need(q_attn, "q_attn", torch.bfloat16, 3)
+        _need(q_attn, "q_attn", torch.bfloat16, q_attn.dim())
     _check(_lib.oasis_pipeline_layer_step(h, int(layer), int(step), q_look.data_ptr(),
                                           None if q_attn is None else q_attn.data_ptr(),
                                           None if out is None else out.data_ptr(),

@@ -222,6 +222,7 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     if (ds.n_layers < 1 || ds.n_layers > 1024) PFAIL(OASIS_EINVAL, "n_layers = %d outside [1, 1024]", ds.n_layers);
     if (ds.K_b < 1) PFAIL(OASIS_EINVAL, "K_b = %d < 1", ds.K_b);
     if (ds.J < 1) PFAIL(OASIS_EINVAL, "J = %d < 1", ds.J);
+    if (ds.n_q < 1) PFAIL(OASIS_EINVAL, "n_q = %d < 1", ds.n_q);
     if (ds.staged != 0 && ds.staged != 1) PFAIL(OASIS_EINVAL, "staged = %d", ds.staged);
     if (ds.staged && (ds.C < 0 || ds.C > ds.K_b)) PFAIL(OASIS_EINVAL, "C = %d outside [0, K_b]", ds.C);
     if (ds.copy_mode != OASIS_COPY_KERNEL && ds.copy_mode != OASIS_COPY_DMA)
@@ -230,8 +231,11 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     if (ds.n_split < 0 || ds.n_split > 64) PFAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", ds.n_split);
     int rc0 = check_dims(dims);
     if (rc0) return rc0;
+    if ((int64_t)ds.n_q * (dims->H_q / dims->H_kv) > kMaxG)
+        PFAIL(OASIS_EUNSUPPORTED, "n_q * H_q / H_kv = %lld (at most %d)",
+              (long long)ds.n_q * (dims->H_q / dims->H_kv), kMaxG);
     const size_t plan_need = oasis_stage_plan_bytes(dims, ds.K_b);
-    const size_t ws_need = oasis_attn_workspace_bytes(dims, ds.K_b, ds.n_split);
+    const size_t ws_need = oasis_lookahead_attn_workspace_bytes(dims, ds.n_q, ds.K_b, ds.n_split);
     for (int l = 0; l < ds.n_layers; l++) {
         int rc = check_layer(ds, ds.layers[l], l, plan_need, ws_need);
         if (rc) return rc;
@@ -298,16 +302,16 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
             OASIS_HIP(hipStreamWaitEvent(p->main, p->event(kEvStage, l, t - 1), 0));
             const int k = t % 3;
             timed_begin(p, 0, p->main);
-            rc = oasis_sparse_decode_attn(d, q_attn, b.ws_pool, p->S, b.tbl_slot[k], b.tbl_block[k], b.tbl_n[k],
-                                          K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes,
-                                          ds.n_split, p->main);
+            rc = oasis_lookahead_attn(d, ds.n_q, q_attn, b.ws_pool, p->S, b.tbl_slot[k], b.tbl_block[k],
+                                      b.tbl_n[k], K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws,
+                                      b.attn_ws_bytes, ds.n_split, p->main);
         } else {
             const int jp = (t - 1) % 2;
             OASIS_HIP(hipStreamWaitEvent(p->main, p->event(kEvSel, l, t - 1), 0));
             timed_begin(p, 0, p->main);
-            rc = oasis_sparse_decode_attn(d, q_attn, ds.pool, d->NB_max, b.sel[jp], b.sel[jp], b.n_sel[jp], K_b,
-                                          ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes,
-                                          ds.n_split, p->main);
+            rc = oasis_lookahead_attn(d, ds.n_q, q_attn, ds.pool, d->NB_max, b.sel[jp], b.sel[jp], b.n_sel[jp],
+                                      K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes,
+                                      ds.n_split, p->main);
         }
         if (rc) return rc;
         timed_end(p, 0, p->main);

@@ -36,13 +36,15 @@ TIMING_KINDS = {"attn": 0, "score": 1, "topk": 2, "plan": 3}
 
 
 class _Layer:
-    def __init__(self, B, H_q, H_kv, NB, K_b, C, staged, copy_mode, ws_bytes, dev, D=128, bs=16):
+    def __init__(self, B, H_q, H_kv, NB, K_b, C, staged, copy_mode, ws_bytes, dev, D=128, bs=16, n_q=1):
         i32 = torch.int32
         self.scores = torch.empty((B, H_kv, NB), dtype=torch.float32, device=dev)
         self.sel = [torch.empty((B, H_kv, K_b), dtype=i32, device=dev) for _ in range(2)]
         self.n_sel = [torch.empty((B, H_kv), dtype=i32, device=dev) for _ in range(2)]
-        self.out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty((B, H_q), dtype=torch.float32, device=dev)
+        # attention output: [B][H_q][D], or [B][n_q][H_q][D] for look-ahead attention
+        qs = (B, H_q) if n_q == 1 else (B, n_q, H_q)
+        self.out = torch.empty(qs + (D,), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(qs, dtype=torch.float32, device=dev)
         self.attn_ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
         self.ws_pool = self.slot_block = self.slot_stamp = None
         self.tbls, self.plans, self.host_plan, self.stage_host, self.stage_dev = [], [], None, [None, None], None
@@ -91,6 +93,8 @@ class LayerPipeline:
            when staged, else device memory.
     summ:  the pool's block summaries (oasis_build_summaries), device.
     ctx:   int32 [B] context lengths, device.
+    n_q:   attention queries per request; 1 + J runs look-ahead attention of
+           the normal and the draft queries (q_attn [B][n_q][H_q][D]).
     The attention runs on the stream current at construction (`main`); the
     compute and copy streams belong to the native pipeline.  Step 0 of every
     layer is the uncapped initial fill (staged workloads).  The caller keeps
@@ -98,20 +102,22 @@ class LayerPipeline:
     """
 
     def __init__(self, *, pool, summ, ctx, H_q: int, K_b: int, C: int, n_layers: int, staged: bool,
-                 copy_mode: int = oa.OASIS_COPY_KERNEL, host_threads: int = 8, n_split: int = 0, J: int = 1):
+                 copy_mode: int = oa.OASIS_COPY_KERNEL, host_threads: int = 8, n_split: int = 0, J: int = 1,
+                 n_q: int = 1):
         B, H_kv, NB, _, bs, D = pool.shape
         self.B, self.H_q, self.H_kv, self.NB, self.K_b, self.C = B, H_q, H_kv, NB, K_b, C
         self.pool, self.summ, self.ctx = pool, summ, ctx
         self.staged, self.copy_mode = staged, copy_mode
-        self.L, self.J = n_layers, J
+        self.L, self.J, self.n_q = n_layers, J, n_q
         dev = ctx.device
-        ws = oa.oasis_attn_workspace_bytes(B, H_q, H_kv, K_b, n_split)
-        self.layers = [_Layer(B, H_q, H_kv, NB, K_b, C, staged, copy_mode, ws, dev, D, bs)
+        ws = oa.oasis_lookahead_attn_workspace_bytes(B, H_q, H_kv, n_q, K_b, n_split)
+        self.layers = [_Layer(B, H_q, H_kv, NB, K_b, C, staged, copy_mode, ws, dev, D, bs, n_q)
                        for _ in range(n_layers)]
         self.main = torch.cuda.current_stream()
         bufs = (oa.oasis_layer_buffers * n_layers)(*[ly.buffers() for ly in self.layers])
         desc = oa.oasis_pipeline_desc(
-            n_layers=n_layers, K_b=K_b, C=C if staged else 0, J=J, staged=int(staged), copy_mode=copy_mode,
+            n_layers=n_layers, K_b=K_b, C=C if staged else 0, J=J, n_q=n_q, staged=int(staged),
+            copy_mode=copy_mode,
             host_threads=host_threads, n_split=n_split, sm_scale=1.0 / math.sqrt(D), pool=pool.data_ptr(),
             kminmax=summ.data_ptr(), ctx_len=ctx.data_ptr(), main_stream=self.main.cuda_stream,
             layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)))
@@ -126,8 +132,11 @@ class LayerPipeline:
         t = 0) and the prediction and staging for step t + 1 from the
         lookahead queries q_look.  The attention output lands in
         `self.layers[l].out` / `.lse` once the main stream reaches it."""
-        if tuple(q_look.shape) != (self.B, self.J, self.H_q, self.layers[l].out.shape[2]):
+        D = self.layers[l].out.shape[-1]
+        if tuple(q_look.shape) != (self.B, self.J, self.H_q, D):
             raise ValueError(f"q_look shape {tuple(q_look.shape)}: expected [B][J = {self.J}][H_q][D]")
+        if t >= 1 and q_attn.numel() != self.B * self.n_q * self.H_q * D:
+            raise ValueError(f"q_attn shape {tuple(q_attn.shape)}: expected [B][n_q = {self.n_q}][H_q][D]")
         ly = self.layers[l]
         oa.oasis_pipeline_layer_step(self._h, l, t, q_look, q_attn if t >= 1 else None, ly.out, ly.lse)
 

@@ -172,7 +172,7 @@ def _pipeline_desc(L=2, staged=1, copy_mode=0, **kw):
         b.ws_pool = b.slot_block = b.slot_stamp = b.host_plan = b.stage_dev = fake
         b.plan_bytes = 1 << 30
         b.stage_bytes = 1 << 20
-    d = binding.oasis_pipeline_desc(n_layers=L, K_b=128, C=6, J=1, staged=staged, copy_mode=copy_mode,
+    d = binding.oasis_pipeline_desc(n_layers=L, K_b=128, C=6, J=1, n_q=1, staged=staged, copy_mode=copy_mode,
                                     host_threads=0, n_split=0, sm_scale=0.088, pool=fake, kminmax=fake,
                                     ctx_len=fake, main_stream=None,
                                     layers=ctypes.cast(bufs, ctypes.POINTER(binding.oasis_layer_buffers)))
@@ -190,6 +190,8 @@ def _pipeline_desc(L=2, staged=1, copy_mode=0, **kw):
     ({"staged": 2}, oa.OASIS_EINVAL),
     ({"pool": None}, oa.OASIS_EINVAL),
     ({"n_split": 65}, oa.OASIS_EINVAL),
+    ({"n_q": 0}, oa.OASIS_EINVAL),
+    ({"n_q": 5}, oa.OASIS_EUNSUPPORTED),     # 5 queries x 4 heads > 16 columns
 ])
 def test_pipeline_create_rejects_bad_descriptions(change, code):
     d, bufs = _pipeline_desc(**change)

@@ -387,11 +387,13 @@ def test_chain_end_to_end(name, B, ctx, copy_mode):
 # ---------------------------------------------------------------- pipelined layers
 
 
-@pytest.mark.parametrize("copy_mode", [0, 1])
-def test_layer_pipeline_matches_oracle(copy_mode):
+@pytest.mark.parametrize("copy_mode,joint", [(0, False), (1, False), (0, True)])
+def test_layer_pipeline_matches_oracle(copy_mode, joint):
     """Three layers in flight on separate streams (the schedule the benchmark
     times): every layer's attention output at every step equals the oracle
-    chain run serially for that layer."""
+    chain run serially for that layer.  joint: look-ahead attention of the
+    normal query and the step's draft queries (n_q = 1 + J), each query
+    against the oracle's attention for it alone."""
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
     m = oa()
     w = wl.WORKLOADS["qwen3_8b_16k_b128_staged"].shrink(B=2, ctx=(3000, 9000))
@@ -404,8 +406,11 @@ def test_layer_pipeline_matches_oracle(copy_mode):
     summ = m.oasis_build_summaries(host, ctx)
     looks = [wl.lookahead(w, s).to(DEV) for s in range(steps + 2 * L)]
     attn_q = [looks[max(s - 1, 0)][:, 0].contiguous() for s in range(steps + 2 * L)]
+    if joint:
+        attn_q = [torch.cat([attn_q[s][:, None], looks[s]], dim=1).contiguous() for s in range(steps + 2 * L)]
+    n_q = 1 + w.J if joint else 1
     pipe = LayerPipeline(pool=host, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=True, J=w.J,
-                         copy_mode=copy_mode, host_threads=4)
+                         copy_mode=copy_mode, host_threads=4, n_q=n_q)
     outs = {}
     for t in range(steps):
         for l in range(L):
@@ -437,5 +442,11 @@ def test_layer_pipeline_matches_oracle(copy_mode):
                     res = st.resident(r, h)
                     blocks[r, h, :len(res)] = res
                     nb[r, h] = len(res)
-            ref, _ = oracle.attend(u16(attn_q[s + 1]), kv, ctx_np, blocks, nb, 1 / math.sqrt(w.D))
-            assert_attn_close(bf16_to_f64(outs[(l, t + 1)]), ref)
+            got = bf16_to_f64(outs[(l, t + 1)])
+            if not joint:
+                ref, _ = oracle.attend(u16(attn_q[s + 1]), kv, ctx_np, blocks, nb, 1 / math.sqrt(w.D))
+                assert_attn_close(got, ref)
+                continue
+            for qi in range(n_q):
+                ref, _ = oracle.attend(u16(attn_q[s + 1][:, qi]), kv, ctx_np, blocks, nb, 1 / math.sqrt(w.D))
+                assert_attn_close(got[:, qi], ref)
