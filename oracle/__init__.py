@@ -40,6 +40,8 @@ def lib():
         L.oracle_fetch_cap_blocks.restype = I
         L.oracle_stage.argtypes = [I, I, I, I, P, P, P, I, P, I, I, I, P, P, P, P, P]
         L.oracle_attend.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, ctypes.c_double, P, P]
+        L.oracle_append.argtypes = [I, I, I, I, I, P, P, P, P, P]
+        L.oracle_append.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = I
         for f in (L.oracle_build_summaries, L.oracle_score, L.oracle_select, L.oracle_stage,
@@ -162,3 +164,21 @@ def attend(q, kv, ctx_len, blocks, n_blocks, sm_scale: float):
     lib().oracle_attend(B, H_q, H_kv, D, NB, bs, _p(q), _p(kv), _p(ctx), _p(blk), _p(nb), T,
                         float(sm_scale), _p(out), _p(lse))
     return out, lse
+
+
+def append(k_new, v_new, ctx_len, kv, kminmax, bs: int):
+    """One decoded token per request (section 4: full KV off-GPU, block
+    summaries in HBM): K / V written at position ctx_len[r] of every KV head,
+    the block's min / max summary updated, ctx_len incremented.  Returns the
+    updated copies (ctx_len, kv, kminmax); the inputs are not modified.
+    k_new, v_new uint16 [B][H_kv][D]."""
+    k = _c(k_new, _u16)
+    v = _c(v_new, _u16)
+    ctx = _c(ctx_len, _i32).copy()
+    kv = _c(kv, _u16).copy()
+    s = _c(kminmax, _u16).copy()
+    B, H_kv, NB, two, bs_, D = kv.shape
+    assert two == 2 and bs_ == bs and k.shape == (B, H_kv, D) and v.shape == (B, H_kv, D)
+    assert s.shape == (B, H_kv, NB, 2, D) and ctx.shape == (B,)
+    lib().oracle_append(B, H_kv, NB, bs, D, _p(k), _p(v), _p(ctx), _p(kv), _p(s))
+    return ctx, kv, s

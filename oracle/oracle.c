@@ -376,6 +376,47 @@ void oracle_attend(int B, int H_q, int H_kv, int D, int NB_max, int bs,
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Appending one decoded token per request.                                   */
+/* Section 4: the full KV lives off-GPU while HBM keeps the per-block key     */
+/* summaries.  When request r's next token (position c = ctx_len[r]) gets its */
+/* K and V, they are written at block c / bs, row c % bs of every KV head in  */
+/* the pool, that block's summary becomes the min / max over its valid keys   */
+/* including the new one, and ctx_len[r] becomes c + 1.  Reading: the summary */
+/* of a block is its valid keys' coordinate-wise min and max (as built above:  */
+/* the first of equal extreme values in position order is kept), so the new    */
+/* key replaces a bound only when strictly below the min or above the max,    */
+/* and a fresh block (c % bs == 0) starts from the new key.  A request whose  */
+/* pool is full (c >= NB_max * bs), or with c < 0, is left unchanged.        */
+/* k_new, v_new [B][H_kv][D]; kv and kminmax as above, updated in place.      */
+/* ------------------------------------------------------------------------ */
+void oracle_append(int B, int H_kv, int NB_max, int bs, int D,
+                   const uint16_t *k_new, const uint16_t *v_new, int32_t *ctx_len,
+                   uint16_t *kv, uint16_t *kminmax)
+{
+    for (int r = 0; r < B; r++) {
+        const int32_t c = ctx_len[r];
+        if (c < 0 || (int64_t)c >= (int64_t)NB_max * bs) continue;
+        const int b = c / bs, row = c % bs;
+        for (int h = 0; h < H_kv; h++) {
+            const size_t rh = (size_t)r * H_kv + h;
+            const uint16_t *k = k_new + rh * D;
+            const uint16_t *v = v_new + rh * D;
+            uint16_t *K = kv + ((rh * NB_max + b) * 2 + 0) * bs * D;
+            uint16_t *V = K + (size_t)bs * D;
+            uint16_t *smin = kminmax + ((rh * NB_max + b) * 2 + 0) * D;
+            uint16_t *smax = smin + D;
+            for (int d = 0; d < D; d++) {
+                K[(size_t)row * D + d] = k[d];
+                V[(size_t)row * D + d] = v[d];
+                if (row == 0 || bf16_value(k[d]) < bf16_value(smin[d])) smin[d] = k[d];
+                if (row == 0 || bf16_value(k[d]) > bf16_value(smax[d])) smax[d] = k[d];
+            }
+        }
+        ctx_len[r] = c + 1;
+    }
+}
+
 /* Number of threads the OpenMP loops above use (for reporting). */
 #ifdef _OPENMP
 #include <omp.h>

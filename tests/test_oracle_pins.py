@@ -407,3 +407,87 @@ def test_attend_closed_forms():
     n0 = np.zeros_like(n)
     out, lse = oracle.attend(q, kv, ctx, tbl, n0, 0.3)
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# --------------------------------------------------------------------------
+# append: one decoded token per request
+
+
+def np_first_extreme_bits(kv, r, h, b, valid):
+    """bf16 bits of the coordinate-wise min and max over the first `valid`
+    keys of a block, the first of equal values in position order (NumPy's
+    argmin / argmax return the first occurrence)."""
+    K = kv[r, h, b, 0, :valid]
+    vals = f64(K)
+    cols = np.arange(K.shape[1])
+    return K[vals.argmin(axis=0), cols], K[vals.argmax(axis=0), cols]
+
+
+def test_append_matches_numpy_rebuild_token_by_token():
+    """Appending tokens one at a time, across block boundaries and up to the
+    pool's capacity: every block summary equals NumPy's min / max over the
+    updated pool's valid keys, the K / V rows land at the context position,
+    nothing else in the pool changes, and a full request stays unchanged."""
+    w = tiny(ctx=(14, 40))                     # NB_max = 3 blocks = 48 tokens
+    ctx, kv, _ = inputs(w)
+    summ = oracle.build_summaries(kv, ctx, w.bs)
+    cap = w.NB_max * w.bs
+    g = torch.Generator().manual_seed(11)
+    for step in range(cap - int(ctx.min()) + 2):      # until every request is full, then two more
+        k = u16(torch.randn((w.B, w.H_kv, w.D), generator=g).to(torch.bfloat16))
+        v = u16(torch.randn((w.B, w.H_kv, w.D), generator=g).to(torch.bfloat16))
+        ctx2, kv2, summ2 = oracle.append(k, v, ctx, kv, summ, w.bs)
+        for r in range(w.B):
+            c = int(ctx[r])
+            if c >= cap:
+                assert ctx2[r] == c
+                np.testing.assert_array_equal(kv2[r], kv[r])
+                np.testing.assert_array_equal(summ2[r], summ[r])
+                continue
+            assert ctx2[r] == c + 1
+            b, row = divmod(c, w.bs)
+            np.testing.assert_array_equal(kv2[r, :, b, 0, row], k[r])
+            np.testing.assert_array_equal(kv2[r, :, b, 1, row], v[r])
+            changed = np.zeros(kv.shape[1:], dtype=bool)
+            changed[:, b, :, row] = True
+            np.testing.assert_array_equal(kv2[r][~changed], kv[r][~changed])
+            for h in range(w.H_kv):
+                for bb in range(-(-(c + 1) // w.bs)):
+                    valid = min(w.bs, c + 1 - bb * w.bs)
+                    lo, hi = np_first_extreme_bits(kv2, r, h, bb, valid)
+                    np.testing.assert_array_equal(summ2[r, h, bb, 0], lo, err_msg=f"step {step} r {r} b {bb}")
+                    np.testing.assert_array_equal(summ2[r, h, bb, 1], hi)
+        ctx, kv, summ = ctx2, kv2, summ2
+    assert np.all(ctx == cap)                  # every request reached the capacity
+
+
+def test_append_keeps_the_first_of_equal_bounds_and_starts_fresh_blocks():
+    """+0 then -0 (equal values, different bits): the bound keeps the first;
+    a token that starts a block sets both bounds to its key whatever the stale
+    summary held."""
+    B, H, NB, bs, D = 1, 1, 2, 16, 128
+    kv = np.zeros((B, H, NB, 2, bs, D), dtype=np.uint16)
+    summ = np.zeros((B, H, NB, 2, D), dtype=np.uint16)
+    ctx = np.array([1], dtype=np.int32)        # token 0 holds +0 everywhere
+    neg0 = np.full((B, H, D), 0x8000, dtype=np.uint16)
+    ctx, kv, summ = oracle.append(neg0, neg0, ctx, kv, summ, bs)
+    assert np.all(summ[0, 0, 0] == 0x0000)      # the first (+0) stays
+    one = np.full((B, H, D), 0x3F80, dtype=np.uint16)          # 1.0
+    summ[0, 0, 1] = 0x7F80                      # stale +inf in the next block
+    ctx = np.array([bs], dtype=np.int32)
+    ctx, kv, summ = oracle.append(one, one, ctx, kv, summ, bs)
+    assert ctx[0] == bs + 1
+    assert np.all(summ[0, 0, 1] == 0x3F80)
+
+
+def test_append_skips_negative_context():
+    w = tiny()
+    ctx, kv, _ = inputs(w)
+    summ = oracle.build_summaries(kv, ctx, w.bs)
+    ctx = ctx.copy()
+    ctx[0] = -1
+    k = np.zeros((w.B, w.H_kv, w.D), dtype=np.uint16)
+    ctx2, kv2, summ2 = oracle.append(k, k, ctx, kv, summ, w.bs)
+    assert ctx2[0] == -1
+    np.testing.assert_array_equal(kv2[0], kv[0])
+    assert ctx2[1] == ctx[1] + 1
