@@ -237,6 +237,33 @@ typedef struct oasis_stage_args {
     void *plan_event;       /* optional: recorded after the plan kernels */
 } oasis_stage_args;
 
+/* Appending one decoded token per request (section 4: the full KV lives
+ * off-GPU while HBM keeps the per-block key summaries and the working set).
+ * For request r with c = ctx_len[r] in [0, NB_max * bs):
+ *   - K and V of the token (k_new, v_new [B][H_kv][D] bf16, device) are
+ *     written at block c / bs, row c % bs of every KV head of `pool`
+ *     ([B][H_kv][NB_max][2][bs][D] bf16, pinned host or device);
+ *   - that block's summary in kminmax ([B][H_kv][NB_max][2][D] bf16,
+ *     device) becomes the coordinate-wise min / max of its valid keys
+ *     including the new one: a block's first token sets both bounds, later
+ *     ones replace a bound only when strictly beyond it (the first of equal
+ *     values is kept, as oasis_build_summaries does), so appending token by
+ *     token equals building afresh;
+ *   - when ws_pool ([B][H_kv][S][2][bs][D] bf16, device) is not NULL and the
+ *     block is resident (slot_block[r][h][s] == c / bs, slot_block
+ *     [B][H_kv][S] int32, device, holding each block at most once), the
+ *     token is written into that slot too, so the next attention over the
+ *     working set sees it;
+ *   - then ctx_len[r] ([B] int32, device, in / out) becomes c + 1.
+ * Requests with c outside that range are left unchanged.  Enqueued on
+ * `stream`; the caller orders it after the work that reads the previous
+ * context and before the work that reads the new one.  Errors: EINVAL for
+ * NULL arguments or S < 1 with a working set, EUNSUPPORTED for S > 2048. */
+int oasis_append_kv(const oasis_dims *dims, const uint16_t *k_new,
+                    const uint16_t *v_new, int32_t *ctx_len,
+                    uint16_t *kminmax, void *pool, uint16_t *ws_pool,
+                    const int32_t *slot_block, int32_t S, void *stream);
+
 /* Bytes of the device plan workspace (and of the pinned host plan buffer):
  * 4 * (B * H_kv * (4 + 2 * max(C, 1)) + 4). */
 size_t oasis_stage_plan_bytes(const oasis_dims *dims, int32_t C);

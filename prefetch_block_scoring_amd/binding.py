@@ -90,6 +90,7 @@ _SIGNATURES = {
     "oasis_sparse_decode_attn": (ctypes.c_int, [
         ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
         ctypes.c_size_t, _I32, _P]),
+    "oasis_append_kv": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "oasis_lookahead_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32, _I32, _I32]),
     "oasis_lookahead_attn": (ctypes.c_int, [
         ctypes.POINTER(oasis_dims), _I32, _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
@@ -252,6 +253,36 @@ def oasis_select_topk(scores: torch.Tensor, ctx_len: torch.Tensor, K_b: int, sel
     _check(_lib.oasis_select_topk(ctypes.byref(d), _ptr(scores), _ptr(ctx_len), int(K_b), _ptr(sel),
                                   _ptr(n_sel), _stream(stream)))
     return sel, n_sel
+
+
+def oasis_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, ctx_len: torch.Tensor, kminmax: torch.Tensor,
+                    pool: torch.Tensor, ws_pool: Optional[torch.Tensor] = None,
+                    slot_block: Optional[torch.Tensor] = None, stream=None):
+    """One decoded token per request: k_new / v_new bf16 [B][H_kv][D] go to
+    position ctx_len[r] of pool (bf16 [B][H_kv][NB_max][2][bs][D], device or
+    pinned host), the block's summary in kminmax is updated, the resident
+    slot (ws_pool [B][H_kv][S][2][bs][D] with slot_block [B][H_kv][S]) too;
+    ctx_len is advanced in place."""
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    _need(kminmax, "kminmax", torch.bfloat16, 5)
+    _need(pool, "pool", torch.bfloat16, 6, device=None)
+    B, H_kv, NB, _, bs, D = pool.shape
+    if tuple(k_new.shape) != (B, H_kv, D) or tuple(v_new.shape) != (B, H_kv, D):
+        raise ValueError("k_new / v_new must be [B][H_kv][D]")
+    if tuple(kminmax.shape) != (B, H_kv, NB, 2, D) or tuple(ctx_len.shape) != (B,):
+        raise ValueError("kminmax / ctx_len shape mismatch")
+    S = 0
+    if ws_pool is not None:
+        _need(ws_pool, "ws_pool", torch.bfloat16, 6)
+        _need(slot_block, "slot_block", torch.int32, 3)
+        S = ws_pool.shape[2]
+        if tuple(ws_pool.shape[:2]) != (B, H_kv) or tuple(slot_block.shape) != (B, H_kv, S):
+            raise ValueError("ws_pool / slot_block shape mismatch")
+    d = dims(B, H_kv, H_kv, NB, D, bs)
+    _check(_lib.oasis_append_kv(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(ctx_len), _ptr(kminmax),
+                                _ptr(pool), _ptr(ws_pool), _ptr(slot_block), int(S), _stream(stream)))
 
 
 def oasis_stage_plan_bytes(B: int, H_kv: int, C: int) -> int:

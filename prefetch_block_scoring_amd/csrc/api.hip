@@ -182,6 +182,28 @@ int oasis_select_topk(const oasis_dims *dims, const float *scores, const int32_t
     return OASIS_OK;
 }
 
+int oasis_append_kv(const oasis_dims *dims, const uint16_t *k_new, const uint16_t *v_new, int32_t *ctx_len,
+                    uint16_t *kminmax, void *pool, uint16_t *ws_pool, const int32_t *slot_block, int32_t S,
+                    void *stream) {
+    clear_error();
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (ws_pool && (S < 1 || S > 2048))
+        FAIL(S < 1 ? OASIS_EINVAL : OASIS_EUNSUPPORTED, "S = %d (1 .. 2048 with a working set)", S);
+    if (dims->B == 0) return OASIS_OK;
+    NEED(k_new);
+    NEED(v_new);
+    NEED(ctx_len);
+    NEED(kminmax);
+    NEED(pool);
+    if (ws_pool) NEED(slot_block);
+    const void *pool_dev = nullptr;
+    if ((rc = device_view(pool, &pool_dev, "pool"))) return rc;
+    OASIS_HIP(launch_append(*dims, k_new, v_new, ctx_len, kminmax, const_cast<void *>(pool_dev), ws_pool,
+                            slot_block, ws_pool ? S : 0, static_cast<hipStream_t>(stream)));
+    return OASIS_OK;
+}
+
 size_t oasis_stage_plan_bytes(const oasis_dims *dims, int32_t C) {
     if (!dims || dims->B < 0 || dims->H_kv < 1) return 0;
     return sizeof(int32_t) * plan_ints(dims->B * dims->H_kv, C);

@@ -66,6 +66,11 @@ hipError_t launch_stage_plan(const oasis_dims &d, const oasis_stage_args &a,
 hipError_t launch_stage_gather(const oasis_dims &d, const oasis_stage_args &a,
                                const void *host_pool_dev, hipStream_t s);
 
+hipError_t launch_append(const oasis_dims &d, const uint16_t *k_new,
+                         const uint16_t *v_new, int32_t *ctx_len,
+                         uint16_t *kminmax, void *pool_dev, uint16_t *ws_pool,
+                         const int32_t *slot_block, int S, hipStream_t s);
+
 int attn_splits(const oasis_dims &d, int T, int n_split);
 // split-K workspace for n_q queries per request
 size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split);
