@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--n-split", type=int, default=0)
     p.add_argument("--joint", action="store_true",
                    help="look-ahead attention: the normal query and the step's J draft queries attend together")
+    p.add_argument("--attn-sweep", action="store_true",
+                   help="also time look-ahead attention alone for every supported number of queries per request")
     p.add_argument("--cap", type=float, default=None,
                    help="override the staged workload's fetch cap (fraction of the budget; >= 1 = fetch-all)")
     p.add_argument("--drift", type=float, default=None,
@@ -338,6 +340,35 @@ def main():
                           "GBps": round(attn_bytes / (alone_us * 1e-6) / 1e9, 1),
                           "frac_of_peak": round(attn_bytes / (alone_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                           "note": "same launch, alone on the GPU after the timed steps"}
+
+    if args.attn_sweep:
+        # look-ahead attention alone over the same blocks for n_q = 1, 2, ...
+        # query vectors per request (K / V read once for all of them)
+        sweep = {}
+        gq = torch.Generator(device=dev).manual_seed(17)
+        for nq in range(1, 16 // (H_q // H_kv) + 1):
+            qs = torch.randn((B, nq, H_q, D), generator=gq, device=dev).to(torch.bfloat16)
+            o_s = torch.empty_like(qs)
+            ws_s = torch.empty((max(oa.oasis_lookahead_attn_workspace_bytes(B, H_q, H_kv, nq, T, args.n_split), 1),),
+                               dtype=torch.uint8, device=dev)
+            if staged:
+                run_s = lambda: oa.oasis_lookahead_attn(qs, pipe.layers[0].ws_pool, tb[0], tb[1], tb[2], ctx,
+                                                        out=o_s, ws=ws_s, n_split=args.n_split)
+            else:
+                run_s = lambda: oa.oasis_lookahead_attn(qs, pool, sel, sel, ns, ctx, out=o_s, ws=ws_s,
+                                                        n_split=args.n_split)
+            run_s()
+            torch.cuda.synchronize()
+            ea.record()
+            for _ in range(20):
+                run_s()
+            eb.record()
+            torch.cuda.synchronize()
+            us = ea.elapsed_time(eb) / 20 * 1e3
+            kv_b = attn_bytes - 2 * n_q * B * H_q * D * 2
+            sweep[str(nq)] = {"columns": nq * (H_q // H_kv), "avg_us": round(us, 2),
+                              "kv_GBps": round(kv_b / (us * 1e-6) / 1e9, 1)}
+        kern["lookahead_attn_alone"] = sweep
 
     a_us = kern["attn"]["avg_us"]
     achieved = attn_bytes / (a_us * 1e-6) / 1e9
