@@ -42,6 +42,8 @@ def lib():
         L.oracle_attend.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, ctypes.c_double, P, P]
         L.oracle_append.argtypes = [I, I, I, I, I, P, P, P, P, P]
         L.oracle_append.restype = None
+        L.oracle_block_mass.argtypes = [I, I, I, I, I, I, P, P, P, ctypes.c_double, P]
+        L.oracle_block_mass.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = I
         for f in (L.oracle_build_summaries, L.oracle_score, L.oracle_select, L.oracle_stage,
@@ -182,3 +184,35 @@ def append(k_new, v_new, ctx_len, kv, kminmax, bs: int):
     assert s.shape == (B, H_kv, NB, 2, D) and ctx.shape == (B,)
     lib().oracle_append(B, H_kv, NB, bs, D, _p(k), _p(v), _p(ctx), _p(kv), _p(s))
     return ctx, kv, s
+
+
+def block_mass(q, kv, ctx_len, sm_scale: float):
+    """Exact attention mass per block of the query q over the whole context,
+    summed over each KV head's query heads (the true next-token set of the
+    lookahead-agreement analogue, section 4): fp64 [B][H_kv][NB_max].
+    q uint16 [B][H_q][D], kv uint16 [B][H_kv][NB_max][2][bs][D]."""
+    q = _c(q, _u16)
+    kv = _c(kv, _u16)
+    ctx = _c(ctx_len, _i32)
+    B, H_kv, NB, two, bs, D = kv.shape
+    H_q = q.shape[1]
+    assert two == 2 and q.shape == (B, H_q, D) and ctx.shape == (B,)
+    out = np.empty((B, H_kv, NB), dtype=np.float64)
+    lib().oracle_block_mass(B, H_q, H_kv, D, NB, bs, _p(q), _p(kv), _p(ctx), float(sm_scale), _p(out))
+    return out
+
+
+def agreement(pred_sel, pred_n, true_sel, true_n):
+    """Per (r, h): |predicted set & true set| / |true set| (1 where the true
+    set is empty); [B][H_kv] fp64."""
+    B, H = true_n.shape
+    out = np.ones((B, H), dtype=np.float64)
+    for r in range(B):
+        for h in range(H):
+            k = int(true_n[r, h])
+            if k <= 0:
+                continue
+            P = set(pred_sel[r, h, :int(pred_n[r, h])].tolist())
+            T = set(true_sel[r, h, :k].tolist())
+            out[r, h] = len(P & T) / k
+    return out

@@ -417,6 +417,53 @@ void oracle_append(int B, int H_kv, int NB_max, int bs, int D,
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Exact attention mass per block (for the lookahead-agreement analogue).     */
+/* Section 4 reports how often the draft-based top-K agrees with the true     */
+/* next token's top-K set.  Reading: the true set of KV head h is the top-K   */
+/* by the next query's exact attention mass over the whole context, summed    */
+/* over the query heads g of h's group:                                       */
+/*     mass[b] = sum_g sum_{t in block b, t < ctx} softmax_g(t),              */
+/*     softmax_g(t) = exp(l_t - m) / sum_{t' < ctx} exp(l_t' - m),            */
+/*     l_t = sm_scale * q_g . k_t,                                            */
+/* in fp64.  Blocks at or past the request's last block get 0; a request with */
+/* an empty context gets 0 everywhere.                                        */
+/* q [B][H_q][D]; kv [B][H_kv][NB_max][2][bs][D]; mass [B][H_kv][NB_max].     */
+/* ------------------------------------------------------------------------ */
+void oracle_block_mass(int B, int H_q, int H_kv, int D, int NB_max, int bs,
+                       const uint16_t *q, const uint16_t *kv, const int32_t *ctx_len,
+                       double sm_scale, double *mass)
+{
+    const int G = H_q / H_kv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int r = 0; r < B; r++) {
+        for (int h = 0; h < H_kv; h++) {
+            const size_t rh = (size_t)r * H_kv + h;
+            double *out = mass + rh * NB_max;
+            for (int b = 0; b < NB_max; b++) out[b] = 0.0;
+            int64_t n_tok = ctx_len[r];
+            if (n_tok > (int64_t)NB_max * bs) n_tok = (int64_t)NB_max * bs;
+            if (n_tok <= 0) continue;
+            double *logit = malloc(sizeof(double) * (size_t)n_tok);
+            for (int gi = 0; gi < G; gi++) {
+                const uint16_t *qv = q + ((size_t)r * H_q + (size_t)h * G + gi) * D;
+                double m = -INFINITY;
+                for (int64_t t = 0; t < n_tok; t++) {
+                    const uint16_t *k = kv + ((rh * NB_max + t / bs) * 2 + 0) * bs * D + (size_t)(t % bs) * D;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; d++) dot += bf16_value(qv[d]) * bf16_value(k[d]);
+                    logit[t] = sm_scale * dot;
+                    if (logit[t] > m) m = logit[t];
+                }
+                double den = 0.0;
+                for (int64_t t = 0; t < n_tok; t++) den += exp(logit[t] - m);
+                for (int64_t t = 0; t < n_tok; t++) out[t / bs] += exp(logit[t] - m) / den;
+            }
+            free(logit);
+        }
+    }
+}
+
 /* Number of threads the OpenMP loops above use (for reporting). */
 #ifdef _OPENMP
 #include <omp.h>

@@ -491,3 +491,72 @@ def test_append_skips_negative_context():
     assert ctx2[0] == -1
     np.testing.assert_array_equal(kv2[0], kv[0])
     assert ctx2[1] == ctx[1] + 1
+
+
+# --------------------------------------------------------------------------
+# exact block attention mass and agreement (lookahead-agreement analogue)
+
+
+def np_block_mass(q, kv, ctx, sm):
+    """Dense softmax in NumPy (matrix products, exp, block sums): a second
+    implementation of the same definition."""
+    B, H_kv, NB, _, bs, D = kv.shape
+    H_q = q.shape[1]
+    G = H_q // H_kv
+    out = np.zeros((B, H_kv, NB))
+    for r in range(B):
+        n = min(int(ctx[r]), NB * bs)
+        if n <= 0:
+            continue
+        for h in range(H_kv):
+            K = f64(kv[r, h, :, 0]).reshape(NB * bs, D)[:n]
+            Q = f64(q[r, h * G:(h + 1) * G])                      # [G][D]
+            L = sm * Q @ K.T                                     # [G][n]
+            P = np.exp(L - L.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            per_tok = P.sum(axis=0)
+            out[r, h] = np.bincount(np.arange(n) // bs, weights=per_tok, minlength=NB)[:NB]
+    return out
+
+
+def test_block_mass_matches_numpy_dense_softmax():
+    w = tiny(ctx=(70, 200), structure="planted", planted=2)
+    ctx, kv, _ = inputs(w)
+    q = u16(wl.attention_query(w, 1))
+    sm = 1 / math.sqrt(w.D)
+    got = oracle.block_mass(q, kv, ctx, sm)
+    ref = np_block_mass(q, kv, ctx, sm)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+    # each query head's softmax sums to one: G per (request, KV head)
+    np.testing.assert_allclose(got.sum(axis=2), np.full((w.B, w.H_kv), w.G), rtol=1e-12)
+    for r in range(w.B):
+        assert np.all(got[r, :, -(-int(ctx[r]) // w.bs):] == 0)
+
+
+def test_block_mass_of_equal_keys_counts_tokens():
+    """All keys equal: every token has the same weight, so a block's mass is
+    G * (its valid tokens) / context."""
+    w = tiny(ctx=(37, 90))
+    ctx, kv, _ = inputs(w)
+    kv = kv.copy()
+    kv[:, :, :, 0] = kv[:, :, :1, 0, :1]
+    q = u16(wl.attention_query(w, 1))
+    got = oracle.block_mass(q, kv, ctx, 0.1)
+    for r in range(w.B):
+        c = int(ctx[r])
+        valid = np.clip(c - np.arange(w.NB_max) * w.bs, 0, w.bs)
+        np.testing.assert_allclose(got[r], np.broadcast_to(w.G * valid / c, got[r].shape), rtol=1e-12)
+
+
+def test_block_mass_empty_context_and_agreement_by_hand():
+    w = tiny()
+    ctx, kv, _ = inputs(w)
+    ctx = ctx.copy()
+    ctx[0] = 0
+    q = u16(wl.attention_query(w, 1))
+    assert np.all(oracle.block_mass(q, kv, ctx, 0.1)[0] == 0)
+    pred = np.array([[[1, 2, 3, -1]]], dtype=np.int32)
+    true = np.array([[[2, 3, 4, 7]]], dtype=np.int32)
+    a = oracle.agreement(pred, np.array([[3]]), true, np.array([[3]]))
+    assert a[0, 0] == 2 / 3
+    assert oracle.agreement(pred, np.array([[3]]), true, np.array([[0]]))[0, 0] == 1.0

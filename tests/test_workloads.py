@@ -55,3 +55,13 @@ def test_drift_turns_over_about_five_percent_per_step():
         prev = sel
     frac = np.mean(changes) / w.K_b
     assert 0.02 < frac < 0.10, frac
+
+
+def test_true_next_query_is_the_first_draft_plus_noise():
+    w = wl.WORKLOADS["qwen3_8b_16k_b128_staged"].shrink(B=4)
+    base = wl.lookahead(w, 3)[:, 0]
+    assert torch.equal(wl.true_next_query(w, 3, 0.0), base)
+    noisy = wl.true_next_query(w, 3, 0.5).float()
+    diff = noisy - wl.lookahead_f32(w, 3)[:, 0]
+    assert abs(float(diff.std()) - 0.5) < 0.02
+    assert torch.equal(wl.true_next_query(w, 3, 0.5), wl.true_next_query(w, 3, 0.5))   # seeded

@@ -41,7 +41,7 @@ import torch
 PAD_VALUE = 64.0
 
 _PURPOSE = {"ctx": 1, "qbase": 2, "kv": 3, "plant": 4, "drift": 5, "qstep": 6,
-            "scores": 7, "sets": 8, "table": 9, "attnq": 10}
+            "scores": 7, "sets": 8, "table": 9, "attnq": 10, "truenext": 11}
 
 
 @dataclass(frozen=True)
@@ -204,6 +204,18 @@ def attention_query(w: Workload, step: int = 0, device="cpu") -> torch.Tensor:
     drafter is taken as exact, so the query attended at step s is the first
     lookahead query drawn at step s - 1 (at step 0, that of step 0)."""
     return lookahead(w, max(step - 1, 0), device)[:, 0].contiguous()
+
+
+def true_next_query(w: Workload, step: int, sigma: float, device="cpu") -> torch.Tensor:
+    """bf16 [B][H_q][D]: the query the next token really has, for the
+    lookahead-agreement analogue: the first draft of `step` plus seeded
+    N(0, sigma^2) noise per coordinate (the draft queries are N(0, 1) plus
+    the workload's structure), so sigma = 0 is a perfect drafter."""
+    q = lookahead_f32(w, step, device)[:, 0]
+    if sigma > 0:
+        g = generator(w, "truenext", step, device)
+        q = q + _randn(tuple(q.shape), g, device, sigma)
+    return q.to(torch.bfloat16).contiguous()
 
 
 def _qbar(w: Workload, device) -> torch.Tensor:
