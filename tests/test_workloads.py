@@ -1,5 +1,6 @@
 """The synthetic workloads have the shapes and structure the pages describe."""
 import numpy as np
+import torch
 
 import oracle
 import workloads as wl
