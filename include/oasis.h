@@ -264,6 +264,37 @@ int oasis_append_kv(const oasis_dims *dims, const uint16_t *k_new,
                     uint16_t *kminmax, void *pool, uint16_t *ws_pool,
                     const int32_t *slot_block, int32_t S, void *stream);
 
+/* Lookahead-agreement analogue.  Section 4 reports how often the top-K set
+ * predicted from the draft queries agrees with the true next token's top-K
+ * set.  oasis_block_attention_mass gives the true side: for each (request
+ * r, KV head h) and block b, the exact attention mass of query q over the
+ * request's whole context, summed over the query heads g of h's group,
+ *     mass[r][h][b] = sum_g sum_{t in b, t < ctx} exp(l_gt - M_g) / L_g,
+ *     l_gt = sm_scale * q[r][g] . k_t,  M_g = max_t l_gt,
+ *     L_g = sum_t exp(l_gt - M_g),
+ * fp32, 0 for blocks at or past the last block.  oasis_select_topk on it
+ * gives the true set.
+ *   q        [B][H_q][D] bf16, device (the next token's query)
+ *   kv_pool  [B][H_kv][NB_max][2][bs][D] bf16, device or pinned host (every
+ *            valid key is read once)
+ *   ctx_len  [B] int32, device
+ *   mass     [B][H_kv][NB_max] fp32, device, written
+ *   ws       device workspace of oasis_block_mass_workspace_bytes(dims) */
+size_t oasis_block_mass_workspace_bytes(const oasis_dims *dims);
+int oasis_block_attention_mass(const oasis_dims *dims, const uint16_t *q,
+                               const uint16_t *kv_pool, const int32_t *ctx_len,
+                               float sm_scale, float *mass, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/* |A & B| per (request, KV head) of two top-K lists as oasis_select_topk
+ * writes them (ascending ids, -1 padded, rows of K entries, counts n_a /
+ * n_b [B][H_kv] clamped to [0, K]): overlap [B][H_kv] int32, device.  The
+ * agreement of a prediction A with the true set B is overlap / n_b. */
+int oasis_topk_overlap(const oasis_dims *dims, const int32_t *sel_a,
+                       const int32_t *n_a, const int32_t *sel_b,
+                       const int32_t *n_b, int32_t K, int32_t *overlap,
+                       void *stream);
+
 /* Bytes of the device plan workspace (and of the pinned host plan buffer):
  * 4 * (B * H_kv * (4 + 2 * max(C, 1)) + 4). */
 size_t oasis_stage_plan_bytes(const oasis_dims *dims, int32_t C);

@@ -90,6 +90,10 @@ _SIGNATURES = {
     "oasis_sparse_decode_attn": (ctypes.c_int, [
         ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
         ctypes.c_size_t, _I32, _P]),
+    "oasis_block_mass_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims)]),
+    "oasis_block_attention_mass": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _P, ctypes.c_float, _P, _P,
+                                                  ctypes.c_size_t, _P]),
+    "oasis_topk_overlap": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _P, _P, _I32, _P, _P]),
     "oasis_append_kv": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "oasis_lookahead_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32, _I32, _I32]),
     "oasis_lookahead_attn": (ctypes.c_int, [
@@ -283,6 +287,48 @@ def oasis_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, ctx_len: torch.Ten
     d = dims(B, H_kv, H_kv, NB, D, bs)
     _check(_lib.oasis_append_kv(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(ctx_len), _ptr(kminmax),
                                 _ptr(pool), _ptr(ws_pool), _ptr(slot_block), int(S), _stream(stream)))
+
+
+def oasis_block_attention_mass(q: torch.Tensor, kv_pool: torch.Tensor, ctx_len: torch.Tensor,
+                               sm_scale: Optional[float] = None, mass=None, ws=None, stream=None):
+    """q bf16 [B][H_q][D], kv_pool bf16 [B][H_kv][NB_max][2][bs][D] (device
+    or pinned host) -> exact attention mass per block, fp32
+    [B][H_kv][NB_max], summed over each KV head's query heads."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 6, device=None)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    B, H_q, D = q.shape
+    _, H_kv, NB, _, bs, _ = kv_pool.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if mass is None:
+        mass = torch.empty((B, H_kv, NB), dtype=torch.float32, device=q.device)
+    _need(mass, "mass", torch.float32, 3)
+    d = dims(B, H_q, H_kv, NB, D, bs)
+    need = int(_lib.oasis_block_mass_workspace_bytes(ctypes.byref(d)))
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(_lib.oasis_block_attention_mass(ctypes.byref(d), _ptr(q), _ptr(kv_pool), _ptr(ctx_len), float(sm_scale),
+                                           _ptr(mass), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return mass
+
+
+def oasis_topk_overlap(sel_a: torch.Tensor, n_a: torch.Tensor, sel_b: torch.Tensor, n_b: torch.Tensor,
+                       out=None, stream=None) -> torch.Tensor:
+    """|A & B| per (request, KV head), int32 [B][H_kv], of two top-K lists."""
+    for t, n in ((sel_a, "sel_a"), (sel_b, "sel_b")):
+        _need(t, n, torch.int32, 3)
+    for t, n in ((n_a, "n_a"), (n_b, "n_b")):
+        _need(t, n, torch.int32, 2)
+    B, H_kv, K = sel_a.shape
+    if tuple(sel_b.shape) != (B, H_kv, K):
+        raise ValueError("sel_a and sel_b must have the same shape")
+    if out is None:
+        out = torch.empty((B, H_kv), dtype=torch.int32, device=sel_a.device)
+    d = dims(B, H_kv, H_kv, 1)
+    _check(_lib.oasis_topk_overlap(ctypes.byref(d), _ptr(sel_a), _ptr(n_a), _ptr(sel_b), _ptr(n_b), int(K),
+                                   _ptr(out), _stream(stream)))
+    return out
 
 
 def oasis_stage_plan_bytes(B: int, H_kv: int, C: int) -> int:

@@ -204,6 +204,49 @@ int oasis_append_kv(const oasis_dims *dims, const uint16_t *k_new, const uint16_
     return OASIS_OK;
 }
 
+size_t oasis_block_mass_workspace_bytes(const oasis_dims *dims) {
+    if (check_dims(dims) != OASIS_OK) return 0;
+    return block_mass_ws_bytes(*dims);
+}
+
+int oasis_block_attention_mass(const oasis_dims *dims, const uint16_t *q, const uint16_t *kv_pool,
+                               const int32_t *ctx_len, float sm_scale, float *mass, void *ws, size_t ws_bytes,
+                               void *stream) {
+    clear_error();
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!std::isfinite(sm_scale)) FAIL(OASIS_EINVAL, "sm_scale is not finite");
+    if (dims->B == 0) return OASIS_OK;
+    NEED(q);
+    NEED(kv_pool);
+    NEED(ctx_len);
+    NEED(mass);
+    NEED(ws);
+    const size_t need = block_mass_ws_bytes(*dims);
+    if (ws_bytes < need) FAIL(OASIS_ENOSPACE, "block-mass workspace %zu bytes < %zu", ws_bytes, need);
+    const void *kv_dev = nullptr;
+    if ((rc = device_view(kv_pool, &kv_dev, "kv_pool"))) return rc;
+    OASIS_HIP(launch_block_mass(*dims, q, kv_dev, ctx_len, sm_scale, mass, ws, static_cast<hipStream_t>(stream)));
+    return OASIS_OK;
+}
+
+int oasis_topk_overlap(const oasis_dims *dims, const int32_t *sel_a, const int32_t *n_a, const int32_t *sel_b,
+                       const int32_t *n_b, int32_t K, int32_t *overlap, void *stream) {
+    clear_error();
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (K < 1) FAIL(OASIS_EINVAL, "K = %d < 1", K);
+    if (dims->B == 0) return OASIS_OK;
+    NEED(sel_a);
+    NEED(n_a);
+    NEED(sel_b);
+    NEED(n_b);
+    NEED(overlap);
+    OASIS_HIP(launch_topk_overlap(dims->B * dims->H_kv, sel_a, n_a, sel_b, n_b, K, overlap,
+                                  static_cast<hipStream_t>(stream)));
+    return OASIS_OK;
+}
+
 size_t oasis_stage_plan_bytes(const oasis_dims *dims, int32_t C) {
     if (!dims || dims->B < 0 || dims->H_kv < 1) return 0;
     return sizeof(int32_t) * plan_ints(dims->B * dims->H_kv, C);

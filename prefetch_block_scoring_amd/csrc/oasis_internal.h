@@ -71,6 +71,15 @@ hipError_t launch_append(const oasis_dims &d, const uint16_t *k_new,
                          uint16_t *kminmax, void *pool_dev, uint16_t *ws_pool,
                          const int32_t *slot_block, int S, hipStream_t s);
 
+size_t block_mass_ws_bytes(const oasis_dims &d);
+hipError_t launch_block_mass(const oasis_dims &d, const uint16_t *q,
+                             const void *kv_dev, const int32_t *ctx_len,
+                             float sm_scale, float *mass, void *ws,
+                             hipStream_t s);
+hipError_t launch_topk_overlap(int pairs, const int32_t *a, const int32_t *na,
+                               const int32_t *b, const int32_t *nb, int K,
+                               int32_t *out, hipStream_t s);
+
 int attn_splits(const oasis_dims &d, int T, int n_split);
 // split-K workspace for n_q queries per request
 size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split);
