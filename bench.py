@@ -55,6 +55,9 @@ def parse():
                    help="look-ahead attention: the normal query and the step's J draft queries attend together")
     p.add_argument("--attn-sweep", action="store_true",
                    help="also time look-ahead attention alone for every supported number of queries per request")
+    p.add_argument("--agreement", action="store_true",
+                   help="instead of the throughput run: the lookahead-agreement analogue (top-K overlap of the "
+                        "draft-based selection with the next query's exact attention top-K, against drafting noise)")
     p.add_argument("--cap", type=float, default=None,
                    help="override the staged workload's fetch cap (fraction of the budget; >= 1 = fetch-all)")
     p.add_argument("--drift", type=float, default=None,
@@ -178,6 +181,10 @@ def main():
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by request and KV head with no exchange, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
+
+    if args.agreement:
+        agreement_run(args)
+        return
 
     import torch
     import prefetch_block_scoring_amd as oa
@@ -420,6 +427,102 @@ def main():
         "host_issue_ms_per_step": round(issued / layer_steps * 1e3, 4),
     }
     print(json.dumps(line), flush=True)
+
+
+def agreement_run(args):
+    """The synthetic analogue of the pages' lookahead agreement (section 4:
+    the draft-based top-K agrees with the true next token's top-K set).  Per
+    step s: the predicted set is the top-K of the block scores of the drafts
+    of step s; the true set is the top-K by the exact attention mass, over
+    the whole context, of the next token's query, taken as the first draft
+    plus N(0, sigma^2) noise per coordinate (sigma = 0: a perfect drafter,
+    so only the summary bound differs from exact attention).  Agreement is
+    |predicted & true| / |true|, averaged over requests, KV heads and steps.
+    `agreement_same_rule` takes the other reading of the true set: the same
+    block-score top-K applied to the next token's query, which isolates the
+    drafts' error from the summary bound's."""
+    import torch
+    import prefetch_block_scoring_amd as oa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[args.workload]
+    if args.drift is not None:
+        w = w.shrink(drift=args.drift)
+    B, H_q, H_kv, D, bs, K_b, NB = w.B, w.H_q, w.H_kv, w.D, w.bs, w.K_b, w.NB_max
+    ctx_cpu = wl.context_lengths(w)
+    ctx = ctx_cpu.to(dev)
+    if w.staged:   # the host pool of a staged workload is read over PCIe here
+        pool = oa.oasis_host_empty((B, H_kv, NB, 2, bs, D), torch.bfloat16)
+        wl.kv_pool(w, device=dev, out=pool)
+    else:
+        pool = wl.kv_pool(w, device=dev)
+    summ = oa.oasis_build_summaries(pool, ctx)
+    sm = 1.0 / math.sqrt(D)
+    sigmas = [0.0, 0.1, 0.25, 0.5, 1.0]
+    steps = list(range(1, 1 + max(1, min(args.steps, 8))))
+    ws = torch.empty((oa.oasis_block_mass_workspace_bytes(B, H_q, H_kv, NB),), dtype=torch.uint8, device=dev)
+    mass = torch.empty((B, H_kv, NB), dtype=torch.float32, device=dev)
+    per_sigma = {str(sg): [] for sg in sigmas}
+    same_rule = {str(sg): [] for sg in sigmas}
+    kept = {}
+    for s in steps:
+        sc = oa.oasis_score_blocks(wl.lookahead(w, s, dev), summ, ctx)
+        psel, pn = oa.oasis_select_topk(sc, ctx, K_b)
+        for sg in sigmas:
+            q = wl.true_next_query(w, s, sg, dev)
+            oa.oasis_block_attention_mass(q, pool, ctx, sm_scale=sm, mass=mass, ws=ws)
+            tsel, tn = oa.oasis_select_topk(mass, ctx, K_b)
+            ov = oa.oasis_topk_overlap(psel, pn, tsel, tn)
+            per_sigma[str(sg)].append(float((ov.float() / tn.clamp(min=1).float()).mean()))
+            # the other reading of the true set: the same block-score rule
+            # applied to the next token's query instead of the drafts
+            ssel, sn = oa.oasis_select_topk(oa.oasis_score_blocks(q[:, None].contiguous(), summ, ctx), ctx, K_b)
+            ov2 = oa.oasis_topk_overlap(psel, pn, ssel, sn)
+            same_rule[str(sg)].append(float((ov2.float() / sn.clamp(min=1).float()).mean()))
+            if s == steps[0]:
+                kept[str(sg)] = (q, psel[:1].cpu(), pn[:1].cpu(), ov[:1].cpu())
+    # the mass kernel alone (the dense pass over every valid key)
+    q0 = kept["0.0"][0]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        oa.oasis_block_attention_mass(q0, pool, ctx, sm_scale=sm, mass=mass, ws=ws)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / 5 * 1e3
+    n_keys = int(sum(int(c) for c in ctx_cpu)) * H_kv
+    k_bytes = n_keys * D * 2
+    result = {
+        "metric": "lookahead top-K agreement (synthetic analogue)",
+        "workload": w.name, "batch": B, "lookahead_queries": w.J, "kv_budget_tokens": w.budget,
+        "steps": len(steps), "structure": w.structure,
+        "agreement": {sg: round(sum(v) / len(v), 5) for sg, v in per_sigma.items()},
+        "agreement_same_rule": {sg: round(sum(v) / len(v), 5) for sg, v in same_rule.items()},
+        "mass_kernel": {"avg_us": round(us, 1), "key_bytes": k_bytes,
+                        "GBps": round(k_bytes / (us * 1e-6) / 1e9, 1),
+                        "read_from": "pinned host pool over PCIe" if w.staged else "HBM"},
+    }
+    if args.check:
+        # request 0 of the first step against the oracle: mass, true set and
+        # overlap (the predicted set is the GPU's, checked elsewhere)
+        import numpy as np
+        import oracle
+        u16 = lambda x: x.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        kv0 = u16(pool[:1])
+        bad = 0
+        for sg, (q, ps, pn0, ov0) in kept.items():
+            ref = oracle.block_mass(u16(q[:1]), kv0, ctx_cpu.numpy()[:1], sm)
+            tsel, tn = oracle.select(ref.astype(np.float32), ctx_cpu.numpy()[:1], bs, K_b)
+            agree = oracle.agreement(ps.numpy(), pn0.numpy(), tsel, tn)
+            got = ov0.numpy() / np.maximum(tn, 1)
+            bad += int(np.sum(np.abs(got - agree) > 1.5 / K_b))   # one tie swap allowed
+        result["oracle_check"] = {"request": 0, "sigmas": len(kept), "pairs_off": bad}
+        if bad:
+            print(json.dumps(result), flush=True)
+            raise SystemExit("agreement check failed")
+    print(json.dumps(result), flush=True)
 
 
 def cpu_baseline(w, pool, ctx_cpu, q_look, seconds, C):

@@ -289,6 +289,11 @@ def oasis_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, ctx_len: torch.Ten
                                 _ptr(pool), _ptr(ws_pool), _ptr(slot_block), int(S), _stream(stream)))
 
 
+def oasis_block_mass_workspace_bytes(B: int, H_q: int, H_kv: int, NB_max: int) -> int:
+    d = dims(B, H_q, H_kv, NB_max)
+    return int(_lib.oasis_block_mass_workspace_bytes(ctypes.byref(d)))
+
+
 def oasis_block_attention_mass(q: torch.Tensor, kv_pool: torch.Tensor, ctx_len: torch.Tensor,
                                sm_scale: Optional[float] = None, mass=None, ws=None, stream=None):
     """q bf16 [B][H_q][D], kv_pool bf16 [B][H_kv][NB_max][2][bs][D] (device
