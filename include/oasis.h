@@ -495,12 +495,14 @@ int oasis_pipeline_drain(oasis_pipeline *p);
 int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
 
 /* Event timing of the steps: capacity > 0 (re)arms timing of up to
- * `capacity` launches per kind and clears the totals; 0 disables it.
- * Kinds: 0 attention (main stream), 1 scores, 2 top-K, 3 staging plan
- * (compute stream); each interval starts once the stream's earlier waits are
- * satisfied.  timing_read synchronises on the recorded events and returns
- * their total milliseconds and count. */
-int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity);
+ * `capacity` launches of each kind whose bit is set in `kinds` and clears
+ * the totals; capacity 0 or kinds 0 disables it.  Kinds: 0 attention (main
+ * stream), 1 scores, 2 top-K, 3 staging plan (compute stream); each interval
+ * starts once the stream's earlier waits are satisfied.  Every timed launch
+ * records two timing events on its stream.  timing_read synchronises on the
+ * recorded events and returns their total milliseconds and count. */
+int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity,
+                          uint32_t kinds);
 int oasis_pipeline_timing_read(oasis_pipeline *p, int32_t kind,
                                double *total_ms, int32_t *count);
 

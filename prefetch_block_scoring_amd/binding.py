@@ -104,7 +104,7 @@ _SIGNATURES = {
     "oasis_pipeline_layer_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P]),
     "oasis_pipeline_drain": (ctypes.c_int, [_P]),
     "oasis_pipeline_stream": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_void_p)]),
-    "oasis_pipeline_timing": (ctypes.c_int, [_P, _I32]),
+    "oasis_pipeline_timing": (ctypes.c_int, [_P, _I32, ctypes.c_uint32]),
     "oasis_pipeline_timing_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(_I32)]),
     "oasis_pipeline_copy_host_seconds": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_double),
@@ -540,8 +540,8 @@ def oasis_pipeline_stream(h: int, which: int) -> Optional[int]:
     return s.value
 
 
-def oasis_pipeline_timing(h: int, capacity: int):
-    _check(_lib.oasis_pipeline_timing(h, int(capacity)))
+def oasis_pipeline_timing(h: int, capacity: int, kinds: int = 0xF):
+    _check(_lib.oasis_pipeline_timing(h, int(capacity), int(kinds)))
 
 
 def oasis_pipeline_timing_read(h: int, kind: int):

@@ -51,6 +51,7 @@ struct oasis_pipeline {
 
     // timing
     int t_cap = 0;
+    uint32_t t_kinds = 0;  // bit k: kind k is timed
     std::vector<hipEvent_t> t_ev[kTimedKinds];  // 2 * t_cap each
     int t_n[kTimedKinds] = {0, 0, 0, 0};
     double copy_host_s = 0.0;
@@ -83,11 +84,12 @@ namespace {
     } while (0)
 
 void timed_begin(oasis_pipeline *p, int kind, hipStream_t s) {
-    if (p->t_n[kind] < p->t_cap) (void)hipEventRecord(p->t_ev[kind][2 * p->t_n[kind]], s);
+    if ((p->t_kinds >> kind & 1u) && p->t_n[kind] < p->t_cap)
+        (void)hipEventRecord(p->t_ev[kind][2 * p->t_n[kind]], s);
 }
 
 void timed_end(oasis_pipeline *p, int kind, hipStream_t s) {
-    if (p->t_n[kind] < p->t_cap) {
+    if ((p->t_kinds >> kind & 1u) && p->t_n[kind] < p->t_cap) {
         (void)hipEventRecord(p->t_ev[kind][2 * p->t_n[kind] + 1], s);
         p->t_n[kind]++;
     }
@@ -408,10 +410,11 @@ int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream) {
     return OASIS_OK;
 }
 
-int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity) {
+int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity, uint32_t kinds) {
     clear_error();
     if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
     if (capacity < 0 || capacity > (1 << 20)) PFAIL(OASIS_EINVAL, "capacity = %d", capacity);
+    if (kinds >> kTimedKinds) PFAIL(OASIS_EINVAL, "kinds = 0x%x (bits 0 .. %d)", kinds, kTimedKinds - 1);
     int rc = oasis_pipeline_drain(p);
     if (rc) return rc;
     for (int k = 0; k < kTimedKinds; k++) {
@@ -424,6 +427,7 @@ int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity) {
         p->t_n[k] = 0;
     }
     p->t_cap = capacity;
+    p->t_kinds = kinds;
     std::lock_guard<std::mutex> lk(p->t_mu);
     p->copy_host_s = 0.0;
     p->copy_calls = 0;
