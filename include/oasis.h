@@ -117,7 +117,8 @@ int oasis_build_summaries(const oasis_dims *dims, const uint16_t *kv,
  *   ctx_len  [B] int32, device
  *   scores   [B][H_kv][NB_max] fp32, device, written
  * Requires J >= 1 and ctx_len[r] <= NB_max * bs (larger values are clamped to
- * NB_max blocks). */
+ * NB_max blocks).  J > 64, or B * H_kv * ceil(NB_max / 128) above 2^31 - 1,
+ * returns OASIS_EUNSUPPORTED. */
 int oasis_score_blocks(const oasis_dims *dims, const uint16_t *q_look,
                        int32_t J, const uint16_t *kminmax,
                        const int32_t *ctx_len, float *scores, void *stream);

@@ -158,6 +158,8 @@ int oasis_score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J
     if (rc) return rc;
     if (J < 1) FAIL(OASIS_EINVAL, "J = %d < 1", J);
     if (J > 64) FAIL(OASIS_EUNSUPPORTED, "J = %d (at most 64)", J);
+    if ((int64_t)dims->B * dims->H_kv * ((dims->NB_max + 127) / 128) > INT32_MAX)
+        FAIL(OASIS_EUNSUPPORTED, "B * H_kv * ceil(NB_max / 128) exceeds 2^31 - 1");
     if (dims->B == 0) return OASIS_OK;
     NEED(q_look);
     NEED(kminmax);

@@ -15,10 +15,14 @@
 // Arithmetic: Qp / Qm are summed in fp64 (exact for bf16 inputs of ordinary
 // range), the 2 * D products and their sum in fp64, rounded once to fp32.
 //
-// Mapping: the grid is persistent (compute units x resident workgroups); the
-// (request, KV head, 128-block chunk) items are split into equal contiguous
-// ranges, one per workgroup, so Qp / Qm are rebuilt only when a range crosses
-// into the next (request, KV head).  Eight lanes share a block (512 bytes of
+// Mapping: the grid is persistent (compute units x resident workgroups).  The
+// work items are the (request, KV head, 128-block chunk) triples whose chunk
+// holds at least one of the request's blocks; they are split into equal
+// contiguous ranges, one per workgroup, so that ragged contexts balance and
+// Qp / Qm are rebuilt only when a range crosses into the next (request, KV
+// head).  Each workgroup counts the items itself from the context lengths.
+// The chunks past a request's last block only get -inf, in a second, strided
+// loop.  Eight lanes share a block (512 bytes of
 // summary); lane i of the eight holds dims [8i, 8i + 8) and [64 + 8i, 72 + 8i)
 // of kmin and kmax, so each 16-byte load fills whole 128-byte lines per eight
 // lanes.  Four 32-block groups are loaded before any is used (16 KiB in flight
@@ -54,26 +58,74 @@ __device__ __forceinline__ double octet_sum(double x) {
     return x;
 }
 
-__global__ __launch_bounds__(kThreads) void score_kernel(
+// chunks of request r that hold at least one of its blocks
+__device__ __forceinline__ int valid_chunks(const int32_t *ctx_len, int r, int NB_max) {
+    return (n_blocks_of(ctx_len[r], NB_max) + kItemBlocks - 1) / kItemBlocks;
+}
+
+__global__ __launch_bounds__(kThreads, 3) void score_kernel(
     const uint16_t *__restrict__ q_look, int J, int H_q, int H_kv,
     const uint4 *__restrict__ kminmax, const int32_t *__restrict__ ctx_len,
-    float *__restrict__ scores, int NB_max, int chunks, int n_items) {
+    float *__restrict__ scores, int NB_max, int B) {
     __shared__ double Qsh[2][kD];  // [0] = Qm (pairs with kmin), [1] = Qp (pairs with kmax)
     const int G = H_q / H_kv;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int li = tid % kLanesPerBlock;
-    const int per = (n_items + gridDim.x - 1) / gridDim.x;
-    const int it0 = blockIdx.x * per;
-    const int it1 = min(n_items, it0 + per);
+
+    // the -inf rows this workgroup fills at the end (loads issued now, with
+    // the scan's, so that their latency is not paid at the end)
+    const int pairs = B * H_kv;
+    const int fill_ctx = (int)blockIdx.x < pairs ? ctx_len[blockIdx.x / H_kv] : 0;
+
+    // items before each request, by a scan over the context lengths that
+    // every wave does alike (uniform results, no synchronisation); up to 64
+    // requests need one load per lane
+    int c_lane = lane < B ? H_kv * valid_chunks(ctx_len, lane, NB_max) : 0;
+    int total = 0;
+    for (int r0 = 0; r0 < B; r0 += 64) {
+        int c = r0 == 0 ? c_lane : (r0 + lane < B ? H_kv * valid_chunks(ctx_len, r0 + lane, NB_max) : 0);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+        total += c;
+    }
+    total = __builtin_amdgcn_readfirstlane(total);  // uniform: keep the walk in scalar registers
+    const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int v0 = min(total, (int)blockIdx.x * per), v1 = min(total, v0 + per);
+    // the request holding item v0, and the item's place in it
+    int r = 0, before = 0;
+    if (v0 < v1) {
+        for (int r0 = 0; r0 < B; r0 += 64) {
+            const int c = r0 == 0 ? c_lane : (r0 + lane < B ? H_kv * valid_chunks(ctx_len, r0 + lane, NB_max) : 0);
+            int inc = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += y;
+            }
+            const int chunk_total = __shfl(inc, 63, 64);
+            if (before + chunk_total > v0) {
+                // first lane whose running count passes v0
+                const unsigned long long m = __ballot(before + inc > v0);
+                const int first = __ffsll((long long)m) - 1;
+                r = __builtin_amdgcn_readfirstlane(r0 + first);
+                before = __builtin_amdgcn_readfirstlane(before + __shfl(inc - c, first, 64));
+                break;
+            }
+            before = __builtin_amdgcn_readfirstlane(before + chunk_total);
+        }
+    }
+    int cr = v0 < v1 ? __builtin_amdgcn_readfirstlane(valid_chunks(ctx_len, r, NB_max)) : 0;  // chunks of r
+    const int rem = v0 - before;                               // item index within request r
+    int h = cr > 0 ? rem / cr : 0;
+    int chunk = cr > 0 ? rem - h * cr : 0;
 
     int cur = -1, nb = 0;
     double qm[16], qp[16];
-    for (int item = it0; item < it1; item++) {
-        const int rh = item / chunks;
-        const int chunk = item - rh * chunks;
+    for (int v = v0; v < v1; v++) {
+        const int rh = r * H_kv + h;
         if (rh != cur) {  // uniform across the workgroup
             cur = rh;
-            const int r = rh / H_kv, h = rh - (rh / H_kv) * H_kv;
             __syncthreads();
             if (tid < kD) {
                 double sp = 0.0, sm = 0.0;
@@ -136,6 +188,26 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
             acc = octet_sum(acc);
             if (li == 0) out[b] = (float)acc;
         }
+        // next item: the next chunk, then the next KV head, then the next
+        // request with any blocks
+        if (++chunk == cr) {
+            chunk = 0;
+            if (++h == H_kv) {
+                h = 0;
+                do {
+                    ++r;
+                    cr = r < B ? __builtin_amdgcn_readfirstlane(valid_chunks(ctx_len, r, NB_max)) : 1;
+                } while (cr == 0);
+            }
+        }
+    }
+
+    // -inf past each request's last valid chunk
+    for (int rh = blockIdx.x; rh < pairs; rh += gridDim.x) {
+        const int c = rh == (int)blockIdx.x ? fill_ctx : ctx_len[rh / H_kv];
+        const int first = (n_blocks_of(c, NB_max) + kItemBlocks - 1) / kItemBlocks * kItemBlocks;
+        float *out = scores + (size_t)rh * NB_max;
+        for (int b = first + tid; b < NB_max; b += kThreads) out[b] = -INFINITY;
     }
 }
 
@@ -156,10 +228,10 @@ hipError_t launch_score(const oasis_dims &d, const uint16_t *q_look, int J,
                         const uint16_t *kminmax, const int32_t *ctx_len,
                         float *scores, hipStream_t s) {
     const int chunks = (d.NB_max + kItemBlocks - 1) / kItemBlocks;
-    const int n_items = d.B * d.H_kv * chunks;
+    const int n_items = d.B * d.H_kv * chunks;  // at most this many items hold blocks
     hipLaunchKernelGGL(score_kernel, dim3((unsigned)score_grid(n_items)), dim3(kThreads), 0, s, q_look, J,
                        d.H_q, d.H_kv, reinterpret_cast<const uint4 *>(kminmax), ctx_len, scores, d.NB_max,
-                       chunks, n_items);
+                       d.B);
     return hipGetLastError();
 }
 
