@@ -393,7 +393,7 @@ size_t oasis_lookahead_attn_workspace_bytes(const oasis_dims *dims, int32_t n_q,
 
 int32_t oasis_attn_num_splits(const oasis_dims *dims, int32_t T, int32_t n_split) {
     if (check_dims(dims) != OASIS_OK || T < 0 || n_split < 0) return -1;
-    return attn_splits(*dims, T, n_split);
+    return attn_splits(*dims, 1, T, n_split);
 }
 
 int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q, const uint16_t *kv_pool,
@@ -421,7 +421,7 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
         NEED(tbl_slot);
         NEED(tbl_block);
     }
-    const int splits = attn_splits(*dims, T, n_split);
+    const int splits = attn_splits(*dims, n_q, T, n_split);
     const size_t need = attn_ws_bytes(*dims, n_q, T, n_split);
     if (need > 0) {
         NEED(ws);

@@ -576,13 +576,16 @@ hipError_t launch_g(const oasis_dims &d, const AttnArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int attn_splits(const oasis_dims &d, int T, int n_split) {
+int attn_splits(const oasis_dims &d, int n_q, int T, int n_split) {
     if (n_split > 0) return n_split < 64 ? n_split : 64;
     const long pairs = (long)d.B * d.H_kv;
     if (pairs <= 0 || T <= 0) return 1;
-    // Enough workgroups to give every compute unit several four-wave groups,
-    // without splitting a row below eight entries (two per wave).
-    const long target = 4L * device_cu_count();
+    // One round of workgroups: as many as the compute units hold at once for
+    // the kernel that runs (four per unit up to 4 columns and above 8, two at
+    // 8 columns, whose registers allow 2 waves per SIMD), without splitting a
+    // row below eight entries (two per wave).
+    const int NC = n_q * (d.H_q / d.H_kv);
+    const long target = (NC > 4 && NC <= 8 ? 2L : 4L) * device_cu_count();
     long s = (target + pairs - 1) / pairs;
     const long cap = (T + 7) / 8;
     if (s > cap) s = cap;
@@ -592,7 +595,7 @@ int attn_splits(const oasis_dims &d, int T, int n_split) {
 }
 
 size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split) {
-    const int s = attn_splits(d, T, n_split);
+    const int s = attn_splits(d, n_q, T, n_split);
     if (s <= 1) return 0;
     return (size_t)d.B * n_q * d.H_q * s * (kD + 2) * sizeof(float);
 }

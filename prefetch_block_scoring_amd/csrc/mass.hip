@@ -172,7 +172,12 @@ size_t block_mass_ws_bytes(const oasis_dims &d) { return (size_t)d.B * d.H_q * d
 
 hipError_t launch_block_mass(const oasis_dims &d, const uint16_t *q, const void *kv_dev, const int32_t *ctx_len,
                              float sm_scale, float *mass, void *ws, hipStream_t s) {
-    const int splits = attn_splits(d, d.NB_max, 0);
+    // enough workgroups for four per compute unit, at least eight blocks each
+    const long pairs = (long)d.B * d.H_kv;
+    long sp = (4L * device_cu_count() + pairs - 1) / pairs;
+    const long cap = (d.NB_max + 7) / 8;
+    sp = sp > cap ? cap : sp;
+    const int splits = (int)(sp < 1 ? 1 : (sp > 64 ? 64 : sp));
     hipLaunchKernelGGL(block_stats_kernel, dim3((unsigned)(d.B * d.H_kv), (unsigned)splits), dim3(kThreads), 0, s,
                        q, static_cast<const uint4 *>(kv_dev), ctx_len, sm_scale * 1.4426950408889634f, d.H_q, d.H_kv,
                        d.NB_max, splits, static_cast<float2 *>(ws));

@@ -80,7 +80,8 @@ hipError_t launch_topk_overlap(int pairs, const int32_t *a, const int32_t *na,
                                const int32_t *b, const int32_t *nb, int K,
                                int32_t *out, hipStream_t s);
 
-int attn_splits(const oasis_dims &d, int T, int n_split);
+// split count of an attention launch with n_q queries per request
+int attn_splits(const oasis_dims &d, int n_q, int T, int n_split);
 // split-K workspace for n_q queries per request
 size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split);
 
