@@ -71,11 +71,50 @@ struct AttnArgs {
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A wave's table entries i0 + wave + kWaves * k (k < nk): up to 64 at a time
+// sit in the lanes (one load), with a mask of the valid ones (slot in
+// [0, P), block in [0, nb)), so the loop takes (slot, block) from a lane
+// rather than reading memory before each block's loads.
+struct TableCursor {
+    const int32_t *ts, *tb;
+    int base, nk, P, nb, lane;
+    int slot = -1, blk = -1, chunk = 0;
+    unsigned long long mask = 0;
+
+    __device__ void load(int c) {
+        chunk = c;
+        const int k = c + lane;
+        int s = -1, b = -1;
+        if (k < nk) {
+            s = ts[base + k * kWaves];
+            b = tb[base + k * kWaves];
+        }
+        slot = s;
+        blk = b;
+        mask = __ballot(k < nk && s >= 0 && s < P && b >= 0 && b < nb);
+    }
+    // next valid entry (wave-uniform): its slot and block; false at the end
+    __device__ bool next(int &s, int &b) {
+        for (;;) {
+            if (mask) {
+                const int bit = __ffsll((long long)mask) - 1;
+                mask &= mask - 1;
+                s = __builtin_amdgcn_readlane(slot, bit);
+                b = __builtin_amdgcn_readlane(blk, bit);
+                return true;
+            }
+            if (chunk + 64 >= nk) return false;
+            load(chunk + 64);
+        }
+    }
+};
+
 // GP: columns compiled in (a power of two >= n_q * G, at most 8); G = H_q /
 // H_kv at run time.  Waves per SIMD the kernel is compiled for: four for up
 // to four columns (1024 workgroups of the 8-KV-head layers at batch 128 then
-// fit the 256 compute units in one round); eight columns need the registers
-// of two.  More columns run in attn_pv_kernel below.
+// fit the 256 compute units in one round); eight columns need more
+// registers: at least two (166 registers currently fit three).  More columns
+// run in attn_pv_kernel below.
 template <int GP>
 constexpr int attn_waves_per_simd() { return GP <= 4 ? 4 : 2; }
 
@@ -136,16 +175,13 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     const int32_t *tb = a.tbl_block + (size_t)rh * a.T;
     const uint4 *pool = reinterpret_cast<const uint4 *>(a.kv) + (size_t)rh * a.P * kVecPerBlock;
 
-    // next valid entry at or after i (wave-uniform); returns i1 if none
-    auto next_valid = [&](int i, int &blk) -> const uint4 * {
-        for (; i < i1; i += kWaves) {
-            const int s = ts[i], b = tb[i];
-            if (s >= 0 && s < a.P && b >= 0 && b < nb) {
-                blk = b;
-                return pool + (size_t)s * kVecPerBlock;
-            }
-        }
-        return nullptr;
+    TableCursor cur{ts, tb, i0 + wave, i1 - i0 - wave > 0 ? (i1 - i0 - wave + kWaves - 1) / kWaves : 0, a.P, nb,
+                    lane};
+    cur.load(0);
+    // next valid entry (wave-uniform); nullptr at the end
+    auto next_valid = [&](int &blk) -> const uint4 * {
+        int s;
+        return cur.next(s, blk) ? pool + (size_t)s * kVecPerBlock : nullptr;
     };
     auto load = [&](const uint4 *src, uint4 (&kr)[4], uint4 (&vr)[4]) {
 #pragma unroll
@@ -154,24 +190,15 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
         for (int qq = 0; qq < 4; qq++) vr[qq] = src[256 + (qq * 4 + grp) * 16 + col];
     };
 
-    int i = i0 + wave;
     int blk_c = 0;
-    const uint4 *src_c = nullptr;
-    for (; i < i1; i += kWaves) {
-        const int s = ts[i], b = tb[i];
-        if (s >= 0 && s < a.P && b >= 0 && b < nb) {
-            blk_c = b;
-            src_c = pool + (size_t)s * kVecPerBlock;
-            break;
-        }
-    }
+    const uint4 *src_c = next_valid(blk_c);
     uint4 kc[4], vc[4];
     if (src_c) load(src_c, kc, vc);
 
     float(*pl)[16] = p_lds[wave];
     while (src_c) {
         int blk_n = 0;
-        const uint4 *src_n = next_valid(i + kWaves, blk_n);
+        const uint4 *src_n = next_valid(blk_n);
         uint4 kn[4], vn[4];
         if (src_n) load(src_n, kn, vn);
 
@@ -234,15 +261,7 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         if (!src_n) break;
-        // advance: the entry just prefetched becomes current
-        {
-            int j = i + kWaves;
-            for (; j < i1; j += kWaves) {
-                const int s = ts[j], b = tb[j];
-                if (s >= 0 && s < a.P && b >= 0 && b < nb) break;
-            }
-            i = j;
-        }
+        // the entry just prefetched becomes current
         src_c = src_n;
         blk_c = blk_n;
 #pragma unroll
@@ -375,16 +394,13 @@ __global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
     const uint4 *pool = reinterpret_cast<const uint4 *>(a.kv) + (size_t)rh * a.P * kVecPerBlock;
     uint16_t(*vt)[kVtStride] = reinterpret_cast<uint16_t(*)[kVtStride]>(scratch + wave * kVtBytes);
 
-    // next valid entry at or after i (wave-uniform); returns nullptr if none
-    auto next_valid = [&](int i, int &blk) -> const uint4 * {
-        for (; i < i1; i += kWaves) {
-            const int s = ts[i], b = tb[i];
-            if (s >= 0 && s < a.P && b >= 0 && b < nb) {
-                blk = b;
-                return pool + (size_t)s * kVecPerBlock;
-            }
-        }
-        return nullptr;
+    TableCursor cur{ts, tb, i0 + wave, i1 - i0 - wave > 0 ? (i1 - i0 - wave + kWaves - 1) / kWaves : 0, a.P, nb,
+                    lane};
+    cur.load(0);
+    // next valid entry (wave-uniform); nullptr at the end
+    auto next_valid = [&](int &blk) -> const uint4 * {
+        int s;
+        return cur.next(s, blk) ? pool + (size_t)s * kVecPerBlock : nullptr;
     };
     auto load = [&](const uint4 *src, uint4 (&kr)[4], uint4 (&vr)[4]) {
 #pragma unroll
@@ -393,23 +409,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
         for (int qq = 0; qq < 4; qq++) vr[qq] = src[256 + (qq * 4 + grp) * 16 + col];
     };
 
-    int i = i0 + wave;
     int blk_c = 0;
-    const uint4 *src_c = nullptr;
-    for (; i < i1; i += kWaves) {
-        const int s = ts[i], b = tb[i];
-        if (s >= 0 && s < a.P && b >= 0 && b < nb) {
-            blk_c = b;
-            src_c = pool + (size_t)s * kVecPerBlock;
-            break;
-        }
-    }
+    const uint4 *src_c = next_valid(blk_c);
     uint4 kc[4], vc[4];
     if (src_c) load(src_c, kc, vc);
 
     while (src_c) {
         int blk_n = 0;
-        const uint4 *src_n = next_valid(i + kWaves, blk_n);
+        const uint4 *src_n = next_valid(blk_n);
         uint4 kn[4], vn[4];
         if (src_n) load(src_n, kn, vn);
 
@@ -480,15 +487,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         if (!src_n) break;
-        // advance: the entry just prefetched becomes current
-        {
-            int j = i + kWaves;
-            for (; j < i1; j += kWaves) {
-                const int s = ts[j], b = tb[j];
-                if (s >= 0 && s < a.P && b >= 0 && b < nb) break;
-            }
-            i = j;
-        }
+        // the entry just prefetched becomes current
         src_c = src_n;
         blk_c = blk_n;
 #pragma unroll
@@ -580,10 +579,12 @@ int attn_splits(const oasis_dims &d, int n_q, int T, int n_split) {
     if (n_split > 0) return n_split < 64 ? n_split : 64;
     const long pairs = (long)d.B * d.H_kv;
     if (pairs <= 0 || T <= 0) return 1;
-    // One round of workgroups: as many as the compute units hold at once for
-    // the kernel that runs (four per unit up to 4 columns and above 8, two at
-    // 8 columns, whose registers allow 2 waves per SIMD), without splitting a
-    // row below eight entries (two per wave).
+    // About one round of workgroups for the kernel that runs: four per
+    // compute unit up to 4 columns and above 8, two at 8 columns (its larger
+    // register file; at G = 8 with 128 pairs, 4 splits measured shorter than
+    // 6 or 8, whose extra partial outputs and combine cost more than the
+    // fuller round saves), without splitting a row below eight entries (two
+    // per wave).
     const int NC = n_q * (d.H_q / d.H_kv);
     const long target = (NC > 4 && NC <= 8 ? 2L : 4L) * device_cu_count();
     long s = (target + pairs - 1) / pairs;
