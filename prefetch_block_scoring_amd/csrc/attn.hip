@@ -579,14 +579,13 @@ int attn_splits(const oasis_dims &d, int n_q, int T, int n_split) {
     if (n_split > 0) return n_split < 64 ? n_split : 64;
     const long pairs = (long)d.B * d.H_kv;
     if (pairs <= 0 || T <= 0) return 1;
-    // About one round of workgroups for the kernel that runs: four per
-    // compute unit up to 4 columns and above 8, two at 8 columns (its larger
-    // register file; at G = 8 with 128 pairs, 4 splits measured shorter than
-    // 6 or 8, whose extra partial outputs and combine cost more than the
-    // fuller round saves), without splitting a row below eight entries (two
-    // per wave).
-    const int NC = n_q * (d.H_q / d.H_kv);
-    const long target = (NC > 4 && NC <= 8 ? 2L : 4L) * device_cu_count();
+    // About two workgroups per compute unit, without splitting a row below
+    // eight entries (two per wave).  Measured: one round of the kernel's
+    // full residency (four per unit) wrote more partial outputs than it
+    // saved; with 256 pairs at G = 4, 2 splits ran 4% faster alone and 3%
+    // faster in the pipeline than 4; with 128 pairs at G = 8, 4 splits beat
+    // 6 and 8; and two leave unit slots to the pipeline's other kernels.
+    const long target = 2L * device_cu_count();
     long s = (target + pairs - 1) / pairs;
     const long cap = (T + 7) / 8;
     if (s > cap) s = cap;
