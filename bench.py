@@ -230,6 +230,9 @@ def main():
     q_look = [wl.lookahead(w, s, dev) for s in range(n_look)]
     q_attn = [q_look[max(s - 1, 0)][:, 0].contiguous() for s in range(n_look)]
     n_q = 1 + w.J if args.joint else 1
+    if n_q * (H_q // H_kv) > 16:
+        raise SystemExit(f"--joint: {n_q} queries x {H_q // H_kv} heads per KV head = {n_q * (H_q // H_kv)} "
+                         "columns; look-ahead attention supports at most 16")
     if args.joint:
         # the normal query, then the draft queries that score this step's blocks
         q_attn = [torch.cat([q_attn[s][:, None], q_look[s]], dim=1).contiguous() for s in range(n_look)]
@@ -251,7 +254,7 @@ def main():
                 pipe.layer_step(l, t, q_look[s], q_attn[s])
                 if counting and staged and t >= 1:
                     pipe.drain()
-                    with torch.cuda.stream(pipe.comp):
+                    with torch.cuda.stream(pipe.comp_stream(l)):
                         admitted.add_(pipe.admitted(l, t))
 
     # initial fill (step 0) and warm-up; the warm-up steps also count the

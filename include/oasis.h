@@ -399,7 +399,10 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
  *
  *   main stream (the caller's)   attention of (l, t) over the working set
  *                                staged at (l, t - 1)
- *   compute stream (owned)       scores and top-K of (l, t), staging plan
+ *   compute streams (owned)      scores and top-K of (l, t), staging plan;
+ *                                without staging, even and odd layers
+ *                                alternate two, so one layer's top-K
+ *                                overlaps the next layer's scores
  *   copy streams (owned)         the copies of (l, t); the zero-copy engine
  *                                alternates two by layer so that one
  *                                layer's gather tail overlaps the next
@@ -491,8 +494,9 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t layer, int32_t step,
  * synchronisation). */
 int oasis_pipeline_drain(oasis_pipeline *p);
 
-/* The pipeline's streams: which = 0 main, 1 compute, 2 and 3 the copy
- * streams of even and odd layers (NULL where not used). */
+/* The pipeline's streams: which = 0 main, 1 compute (of even layers, or of
+ * every layer when staged), 2 and 3 the copy streams of even and odd
+ * layers, 4 the compute stream of odd layers (NULL where not used). */
 int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
 
 /* Event timing of the steps: capacity > 0 (re)arms timing of up to

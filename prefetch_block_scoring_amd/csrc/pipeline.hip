@@ -46,7 +46,7 @@ struct oasis_pipeline {
     std::vector<int> next_step;  // per layer: the step the next call must issue
     int device = 0;
     int S = 0;
-    hipStream_t main = nullptr, comp = nullptr, copy[2] = {nullptr, nullptr};
+    hipStream_t main = nullptr, comp[2] = {nullptr, nullptr}, copy[2] = {nullptr, nullptr};
     std::vector<hipEvent_t> ev;  // [kind][layer][kRing]
 
     // timing
@@ -196,7 +196,8 @@ void release(oasis_pipeline *p) {
         p->cv_job.notify_all();
         p->worker.join();
     }
-    if (p->comp) (void)hipStreamSynchronize(p->comp);
+    for (hipStream_t c : p->comp)
+        if (c) (void)hipStreamSynchronize(c);
     for (hipStream_t c : p->copy)
         if (c) (void)hipStreamSynchronize(c);
     (void)hipStreamSynchronize(p->main);
@@ -205,7 +206,8 @@ void release(oasis_pipeline *p) {
     for (auto &v : p->t_ev)
         for (hipEvent_t e : v)
             if (e) (void)hipEventDestroy(e);
-    if (p->comp) (void)hipStreamDestroy(p->comp);
+    for (hipStream_t c : p->comp)
+        if (c) (void)hipStreamDestroy(c);
     for (hipStream_t c : p->copy)
         if (c) (void)hipStreamDestroy(c);
     delete p;
@@ -259,8 +261,13 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     };
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) return fail(e, "hipGetDevice");
-    if ((e = hipStreamCreateWithFlags(&p->comp, hipStreamNonBlocking)) != hipSuccess)
-        return fail(e, "hipStreamCreateWithFlags");
+    // compute streams: without staging, even and odd layers alternate two, so
+    // that one layer's latency-bound top-K overlaps the next layer's scores;
+    // a staged pipeline keeps one (its copy streams take the other hardware
+    // queues)
+    for (int c = 0; c < (ds.staged ? 1 : 2); c++)
+        if ((e = hipStreamCreateWithFlags(&p->comp[c], hipStreamNonBlocking)) != hipSuccess)
+            return fail(e, "hipStreamCreateWithFlags");
     // copy streams: the zero-copy engine alternates two by layer, so that the
     // tail of one layer's gather overlaps the start of the next one's; the
     // DMA engine's copies all go through one (its packing is serial anyway)
@@ -321,7 +328,7 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     }
 
     // background: prediction and staging plan for step t + 1
-    hipStream_t cs = p->comp;
+    hipStream_t cs = p->comp[p->comp[1] ? (l & 1) : 0];
     timed_begin(p, 1, cs);
     if ((rc = oasis_score_blocks(d, q_look, ds.J, ds.kminmax, ds.ctx_len, b.scores, cs))) return rc;
     timed_end(p, 1, cs);
@@ -405,8 +412,11 @@ int oasis_pipeline_drain(oasis_pipeline *p) {
 int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream) {
     clear_error();
     if (!p || !stream) PFAIL(OASIS_EINVAL, "pipeline or stream is NULL");
-    if (which < 0 || which > 3) PFAIL(OASIS_EINVAL, "which = %d outside [0, 3]", which);
-    *stream = which == 0 ? (void *)p->main : which == 1 ? (void *)p->comp : (void *)p->copy[which - 2];
+    if (which < 0 || which > 4) PFAIL(OASIS_EINVAL, "which = %d outside [0, 4]", which);
+    *stream = which == 0   ? (void *)p->main
+              : which == 1 ? (void *)p->comp[0]
+              : which == 4 ? (void *)p->comp[1]
+                           : (void *)p->copy[which - 2];
     return OASIS_OK;
 }
 

@@ -10,6 +10,7 @@ include/oasis.h) schedules that chain on one GPU:
   main stream     attention of (layer l, step t), after the transfer of
                   (l, t - 1) only
   compute stream  scores and top-K of (l, t), then the staging plan of (l, t)
+                  (two streams by layer parity when nothing is staged)
   copy streams    the copies of (l, t) (gather kernels on two streams by
                   layer parity, or DMA copy + scatter on the pipeline's worker
                   thread)
@@ -123,6 +124,8 @@ class LayerPipeline:
             layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)))
         self._h = oa.oasis_pipeline_create(oa.dims(B, H_q, H_kv, NB, D, bs), desc)
         self.comp = torch.cuda.ExternalStream(oa.oasis_pipeline_stream(self._h, 1))
+        odd = oa.oasis_pipeline_stream(self._h, 4)
+        self._comp_odd = torch.cuda.ExternalStream(odd) if odd else self.comp
         self.copy = [torch.cuda.ExternalStream(c) for c in
                      (oa.oasis_pipeline_stream(self._h, k) for k in (2, 3)) if c]
 
@@ -139,6 +142,10 @@ class LayerPipeline:
             raise ValueError(f"q_attn shape {tuple(q_attn.shape)}: expected [B][n_q = {self.n_q}][H_q][D]")
         ly = self.layers[l]
         oa.oasis_pipeline_layer_step(self._h, l, t, q_look, q_attn if t >= 1 else None, ly.out, ly.lse)
+
+    def comp_stream(self, l: int):
+        """The compute stream that runs layer l's scores, top-K and plan."""
+        return self._comp_odd if l & 1 else self.comp
 
     def admitted(self, l: int, t: int) -> torch.Tensor:
         """Device scalar: total admits of layer l's staging at step t (valid

@@ -74,7 +74,7 @@ def run_gpu(w, copy_mode, rs):
             snap = {}
             # stream-ordered snapshots of the sampled requests; no host wait,
             # so the streams keep running ahead of each other as in the bench
-            with torch.cuda.stream(pipe.comp):
+            with torch.cuda.stream(pipe.comp_stream(l)):
                 snap["scores"] = ly.scores.index_select(0, idx)
                 snap["sel"] = ly.sel[t % 2].index_select(0, idx)
                 snap["n_sel"] = ly.n_sel[t % 2].index_select(0, idx)
