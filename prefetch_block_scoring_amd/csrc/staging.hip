@@ -144,7 +144,10 @@ struct StageUse {
     hipEvent_t done = nullptr;
     bool pending = false;
 };
-constexpr int kStageUses = 4;
+// enough entries for every staging buffer a thread cycles through (a layer
+// pipeline uses two per layer), so that an entry is rarely evicted, which
+// waits for its copy
+constexpr int kStageUses = 128;
 thread_local StageUse t_stage_use[kStageUses];
 thread_local int t_stage_next = 0;
 
