@@ -7,11 +7,13 @@
 // written ascending.
 //
 // One workgroup per (request, KV head).  Scores are mapped to order-preserving
-// uint32 keys in LDS; a four-pass radix select (8-bit digits, most significant
-// first) finds the K_b-th largest key T and how many keys equal to T must be
-// taken; a compaction in index order then writes every key > T and the first
-// `need` keys == T, which is exactly the (score desc, id asc) prefix.  All
-// work is integer, so the result is bit-exact.
+// uint32 keys in LDS; a radix select (8-bit digits, most significant first)
+// finds the K_b-th largest key T and how many keys equal to T must be taken,
+// starting at the first digit where the keys differ (the leading digits all
+// keys share, from an AND / OR of the keys, go straight into the prefix); a
+// compaction in index order then writes every key > T and the first `need`
+// keys == T, which is exactly the (score desc, id asc) prefix.  All work is
+// integer, so the result is bit-exact.
 #include "oasis_internal.h"
 
 namespace oasis {
@@ -51,6 +53,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     __shared__ uint32_t hist[kWaves][256];
     __shared__ uint32_t tmp[kWaves];
     __shared__ uint32_t s_digit, s_above;
+    __shared__ uint32_t s_and[kWaves], s_or[kWaves];
 
     const int rh = blockIdx.x;
     const int r = rh / H_kv;
@@ -66,12 +69,42 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     }
 
     const float *row = scores + (size_t)rh * NB_max;
-    for (int b = tid; b < nb; b += kThreads) keys[b] = rank_key(row[b]);
+    uint32_t k_and = 0xffffffffu, k_or = 0u;
+    for (int b = tid; b < nb; b += kThreads) {
+        const uint32_t key = rank_key(row[b]);
+        keys[b] = key;
+        k_and &= key;
+        k_or |= key;
+    }
+    // bits every key shares: the leading digits made of them need no pass
+    // (the scores of one row usually share sign and most of the exponent)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        k_and &= __shfl_xor(k_and, o, 64);
+        k_or |= __shfl_xor(k_or, o, 64);
+    }
+    if ((tid & 63) == 0) {
+        s_and[wave] = k_and;
+        s_or[wave] = k_or;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        k_and &= s_and[w];
+        k_or |= s_or[w];
+    }
+    const uint32_t diff = k_and ^ k_or;  // bits where some keys differ
 
     // ---- radix select of the K_b-th largest key
     uint32_t prefix = 0, mask = 0;
     uint32_t k = (uint32_t)K_b;  // rank still to find among keys matching prefix
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    int first_shift = 24;
+    while (first_shift > 0 && ((diff >> first_shift) & 255u) == 0) {
+        prefix |= k_and & (255u << first_shift);
+        mask |= 255u << first_shift;
+        first_shift -= 8;
+    }
+    for (int shift = first_shift; shift >= 0; shift -= 8) {
         for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
         __syncthreads();
         for (int b = tid; b < nb; b += kThreads) {
