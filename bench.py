@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--copy-mode", choices=["kernel", "dma"], default="kernel")
     p.add_argument("--host-threads", type=int, default=8, help="packing threads of the DMA copy engine")
     p.add_argument("--n-split", type=int, default=0)
+    p.add_argument("--compute-streams", type=int, default=0, choices=[0, 1, 2],
+                   help="streams for scores, top-K and plan (0 = the library's automatic choice)")
     p.add_argument("--joint", action="store_true",
                    help="look-ahead attention: the normal query and the step's J draft queries attend together")
     p.add_argument("--attn-sweep", action="store_true",
@@ -74,6 +76,9 @@ def parse():
                    help="summarize rocprofv3 CSV output directories (kernel stats, FETCH_SIZE and "
                         "WRITE_SIZE runs) instead of benchmarking")
     p.add_argument("--command", default="", help="with --summarize-profile: the profiled command line")
+    p.add_argument("--bench-log", default=None,
+                   help="with --summarize-profile: the profiled bench run's output (stderr and the JSON line); "
+                        "splits the attention launches of the kernel trace by phase")
     return p.parse_args()
 
 
@@ -100,7 +105,45 @@ def _short(name):
     return name.split("(")[0][-60:]
 
 
-def summarize_profile(dirs, command):
+def _attention_phases(trace_path, bench_log):
+    """Mean duration of the attention launches of each bench phase, from a
+    rocprofv3 kernel trace and the bench run's log (its launch counts per
+    phase and its JSON line); the attention kernel runs once per layer-step
+    and once per alone launch, in that order."""
+    import csv
+    phases, line = None, None
+    for ln in open(bench_log):
+        if "attention launches: " in ln:
+            phases = json.loads(ln.split("attention launches: ", 1)[1])
+        elif ln.startswith("{"):
+            line = json.loads(ln)
+    if phases is None:
+        return []
+    rows = [r for r in csv.DictReader(open(trace_path)) if "attn_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    out = [f"attention launches by bench phase ({os.path.basename(trace_path)}, {len(dur)} launches):"]
+    expect = sum(phases.values())
+    if len(dur) != expect:
+        out.append(f"  launch count {len(dur)} differs from the bench's {expect}: not split")
+        return out
+    i = 0
+    res = {}
+    for name in ("warmup", "timed", "extra", "alone"):
+        n = phases[name]
+        if n:
+            seg = dur[i:i + n]
+            res[name] = sum(seg) / n
+            out.append(f"  {name:7s} {n:5d} launches  mean {res[name]:9.2f} us  min {min(seg):9.2f}  max {max(seg):9.2f}")
+        i += n
+    if line and "timed" in res:
+        b = line["roofline"]["avg_launch_us"]
+        out.append(f"  bench line (HIP events on the attention's stream, timed steps): {b:.2f} us; "
+                   f"trace / events = {res['timed'] / b:.3f}")
+    return out
+
+
+def summarize_profile(dirs, command, bench_log=None):
     """Reduce rocprofv3 CSV output to a short text summary: per-kernel call
     counts and durations, and, from FETCH_SIZE / WRITE_SIZE runs, HBM bytes
     per dispatch scaled by what the same counters read for the plain
@@ -123,6 +166,9 @@ def summarize_profile(dirs, command):
                            f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
                 if "oasis" in r["Name"]:
                     machine.setdefault(_short(r["Name"]), {})["avg_us"] = float(r["AverageNs"]) / 1e3
+        if bench_log:
+            for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+                out.extend(_attention_phases(path, bench_log))
         for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
             rows = list(csv.DictReader(open(path)))
             if not rows:
@@ -178,7 +224,7 @@ def profiled_traffic(kernel_key, profile_file):
 def main():
     args = parse()
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.command)
+        summarize_profile(args.summarize_profile, args.command, args.bench_log)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -242,7 +288,7 @@ def main():
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
     pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=H_q, K_b=K_b, C=C, n_layers=L, staged=staged,
                          copy_mode=copy_mode, host_threads=args.host_threads, n_split=args.n_split, J=w.J,
-                         n_q=n_q)
+                         n_q=n_q, compute_streams=args.compute_streams)
     T = K_b
     splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
     admitted = torch.zeros((), dtype=torch.int64, device=dev)
@@ -365,6 +411,10 @@ def main():
             q4, pool, sel, sel, ns, ctx, out=out_alone, ws=pipe.layers[0].attn_ws, n_split=args.n_split)
     alone()
     torch.cuda.synchronize()
+    # attention launches of each phase in launch order, so that a profiled
+    # run's kernel trace can be split the same way (--summarize-profile)
+    log("attention launches: " + json.dumps({"warmup": args.warmup * L, "timed": args.steps * L,
+                                             "extra": n_extra * L if extra else 0, "alone": 21}))
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ea.record()
     for _ in range(20):
@@ -448,7 +498,8 @@ def main():
                    "kv_location": "pinned host pool + HBM working set" if staged else "HBM",
                    "copy_engine": args.copy_mode if staged else None,
                    "host_threads": args.host_threads if staged and copy_mode == oa.OASIS_COPY_DMA else None,
-                   "attn_splits": splits},
+                   "attn_splits": splits, "compute_streams": pipe.compute_streams,
+                   "copy_streams": len(pipe.copy) if staged else None},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "h2d": h2d,

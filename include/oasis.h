@@ -466,6 +466,20 @@ typedef struct oasis_pipeline_desc {
     void *main_stream;        /* attention stream (hipStream_t; NULL = null
                                  stream) */
     const oasis_layer_buffers *layers;  /* n_layers entries, copied */
+    int32_t compute_streams;  /* streams for scores, top-K and the plan: 1,
+                                 or 2 (even and odd layers alternate, so one
+                                 layer's top-K overlaps the next layer's
+                                 scores); 0 = automatic: 2 when nothing is
+                                 staged or when B * H_kv is below the device's
+                                 compute-unit count (top-K and the plan run
+                                 one workgroup per (request, KV head) and
+                                 would leave most compute units idle), else 1.
+                                 Staged with 2: one copy stream; staged with
+                                 1 and OASIS_COPY_KERNEL: two copy streams
+                                 (even and odd layers), so one gather's tail
+                                 overlaps the next one's start.  At most four
+                                 streams in all, the hardware queues of a
+                                 process. */
 } oasis_pipeline_desc;
 
 typedef struct oasis_pipeline oasis_pipeline;
@@ -494,9 +508,10 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t layer, int32_t step,
  * synchronisation). */
 int oasis_pipeline_drain(oasis_pipeline *p);
 
-/* The pipeline's streams: which = 0 main, 1 compute (of even layers, or of
- * every layer when staged), 2 and 3 the copy streams of even and odd
- * layers, 4 the compute stream of odd layers (NULL where not used). */
+/* The pipeline's streams: which = 0 main, 1 compute (of even layers with
+ * two compute streams, else of every layer), 2 and 3 the copy streams (of
+ * even and odd layers with two, else 2 for every layer), 4 the compute
+ * stream of odd layers (NULL where not used). */
 int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
 
 /* Event timing of the steps: capacity > 0 (re)arms timing of up to

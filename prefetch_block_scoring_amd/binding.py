@@ -67,7 +67,8 @@ class oasis_pipeline_desc(ctypes.Structure):
         ("n_layers", _I32), ("K_b", _I32), ("C", _I32), ("J", _I32), ("n_q", _I32), ("staged", _I32),
         ("copy_mode", _I32),
         ("host_threads", _I32), ("n_split", _I32), ("sm_scale", ctypes.c_float), ("pool", _P),
-        ("kminmax", _P), ("ctx_len", _P), ("main_stream", _P), ("layers", ctypes.POINTER(oasis_layer_buffers))]
+        ("kminmax", _P), ("ctx_len", _P), ("main_stream", _P), ("layers", ctypes.POINTER(oasis_layer_buffers)),
+        ("compute_streams", _I32)]
 
 
 # name -> (restype, argtypes)

@@ -233,6 +233,8 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
         PFAIL(OASIS_EINVAL, "copy_mode = %d", ds.copy_mode);
     if (!ds.pool || !ds.kminmax || !ds.ctx_len || !ds.layers) PFAIL(OASIS_EINVAL, "pool, kminmax, ctx_len or layers is NULL");
     if (ds.n_split < 0 || ds.n_split > 64) PFAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", ds.n_split);
+    if (ds.compute_streams < 0 || ds.compute_streams > 2)
+        PFAIL(OASIS_EINVAL, "compute_streams = %d outside [0, 2]", ds.compute_streams);
     int rc0 = check_dims(dims);
     if (rc0) return rc0;
     if ((int64_t)ds.n_q * (dims->H_q / dims->H_kv) > kMaxG)
@@ -261,17 +263,25 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     };
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) return fail(e, "hipGetDevice");
-    // compute streams: without staging, even and odd layers alternate two, so
-    // that one layer's latency-bound top-K overlaps the next layer's scores;
-    // a staged pipeline keeps one (its copy streams take the other hardware
-    // queues)
-    for (int c = 0; c < (ds.staged ? 1 : 2); c++)
+    // compute streams: with two, even and odd layers alternate, so that one
+    // layer's latency-bound top-K and plan overlap the next layer's scores.
+    // That pays when those kernels leave compute units idle: always without
+    // staging, and with staging when there are fewer (request, KV head)
+    // pairs than compute units.  With more pairs a staged step is bound by
+    // the link, and the hardware queue is worth more to a second gather
+    // stream (the 32B-class ragged layer, 128 pairs: 104k -> 160k tok/s with
+    // two; the Qwen3-8B layer at batch 128, 1024 pairs: 159k -> 151k).
+    int n_comp = ds.compute_streams;
+    if (n_comp == 0) n_comp = (!ds.staged || (int64_t)dims->B * dims->H_kv < device_cu_count()) ? 2 : 1;
+    for (int c = 0; c < n_comp; c++)
         if ((e = hipStreamCreateWithFlags(&p->comp[c], hipStreamNonBlocking)) != hipSuccess)
             return fail(e, "hipStreamCreateWithFlags");
-    // copy streams: the zero-copy engine alternates two by layer, so that the
-    // tail of one layer's gather overlaps the start of the next one's; the
-    // DMA engine's copies all go through one (its packing is serial anyway)
-    const int n_copy = !ds.staged ? 0 : (ds.copy_mode == OASIS_COPY_KERNEL ? 2 : 1);
+    // copy streams: with one compute stream the zero-copy engine alternates
+    // two by layer, so that the tail of one layer's gather overlaps the start
+    // of the next one's; otherwise one (at most four streams in all, the
+    // process's hardware queues).  The DMA engine's copies all go through
+    // one (its packing is serial anyway).
+    const int n_copy = !ds.staged ? 0 : (ds.copy_mode == OASIS_COPY_KERNEL && n_comp == 1 ? 2 : 1);
     for (int c = 0; c < n_copy; c++)
         if ((e = hipStreamCreateWithFlags(&p->copy[c], hipStreamNonBlocking)) != hipSuccess)
             return fail(e, "hipStreamCreateWithFlags");

@@ -10,10 +10,12 @@ include/oasis.h) schedules that chain on one GPU:
   main stream     attention of (layer l, step t), after the transfer of
                   (l, t - 1) only
   compute stream  scores and top-K of (l, t), then the staging plan of (l, t)
-                  (two streams by layer parity when nothing is staged)
-  copy streams    the copies of (l, t) (gather kernels on two streams by
-                  layer parity, or DMA copy + scatter on the pipeline's worker
-                  thread)
+                  (two streams by layer parity when nothing is staged or
+                  when there are fewer (request, KV head) pairs than compute
+                  units; `compute_streams` overrides)
+  copy streams    the copies of (l, t) (gather kernels, on two streams by
+                  layer parity when there is one compute stream, or DMA
+                  copy + scatter on the pipeline's worker thread)
 
 `LayerPipeline` allocates the per-layer buffers the native pipeline works in
 (three attention tables, two selections and two plan buffers per layer, the
@@ -104,7 +106,7 @@ class LayerPipeline:
 
     def __init__(self, *, pool, summ, ctx, H_q: int, K_b: int, C: int, n_layers: int, staged: bool,
                  copy_mode: int = oa.OASIS_COPY_KERNEL, host_threads: int = 8, n_split: int = 0, J: int = 1,
-                 n_q: int = 1):
+                 n_q: int = 1, compute_streams: int = 0):
         B, H_kv, NB, _, bs, D = pool.shape
         self.B, self.H_q, self.H_kv, self.NB, self.K_b, self.C = B, H_q, H_kv, NB, K_b, C
         self.pool, self.summ, self.ctx = pool, summ, ctx
@@ -121,11 +123,12 @@ class LayerPipeline:
             copy_mode=copy_mode,
             host_threads=host_threads, n_split=n_split, sm_scale=1.0 / math.sqrt(D), pool=pool.data_ptr(),
             kminmax=summ.data_ptr(), ctx_len=ctx.data_ptr(), main_stream=self.main.cuda_stream,
-            layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)))
+            layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)), compute_streams=compute_streams)
         self._h = oa.oasis_pipeline_create(oa.dims(B, H_q, H_kv, NB, D, bs), desc)
         self.comp = torch.cuda.ExternalStream(oa.oasis_pipeline_stream(self._h, 1))
         odd = oa.oasis_pipeline_stream(self._h, 4)
         self._comp_odd = torch.cuda.ExternalStream(odd) if odd else self.comp
+        self.compute_streams = 2 if odd else 1
         self.copy = [torch.cuda.ExternalStream(c) for c in
                      (oa.oasis_pipeline_stream(self._h, k) for k in (2, 3)) if c]
 

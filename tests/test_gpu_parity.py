@@ -387,13 +387,16 @@ def test_chain_end_to_end(name, B, ctx, copy_mode):
 # ---------------------------------------------------------------- pipelined layers
 
 
-@pytest.mark.parametrize("copy_mode,joint", [(0, False), (1, False), (0, True)])
-def test_layer_pipeline_matches_oracle(copy_mode, joint):
+@pytest.mark.parametrize("copy_mode,joint,compute_streams",
+                         [(0, False, 0), (1, False, 0), (0, True, 0), (0, False, 1), (1, False, 1)])
+def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams):
     """Three layers in flight on separate streams (the schedule the benchmark
     times): every layer's attention output at every step equals the oracle
     chain run serially for that layer.  joint: look-ahead attention of the
     normal query and the step's draft queries (n_q = 1 + J), each query
-    against the oracle's attention for it alone."""
+    against the oracle's attention for it alone.  compute_streams 0 is the
+    automatic choice (two here: 16 (request, KV head) pairs); 1 puts every
+    layer's scores, top-K and plan on one stream beside two gather streams."""
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
     m = oa()
     w = wl.WORKLOADS["qwen3_8b_16k_b128_staged"].shrink(B=2, ctx=(3000, 9000))
@@ -410,7 +413,8 @@ def test_layer_pipeline_matches_oracle(copy_mode, joint):
         attn_q = [torch.cat([attn_q[s][:, None], looks[s]], dim=1).contiguous() for s in range(steps + 2 * L)]
     n_q = 1 + w.J if joint else 1
     pipe = LayerPipeline(pool=host, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=True, J=w.J,
-                         copy_mode=copy_mode, host_threads=4, n_q=n_q)
+                         copy_mode=copy_mode, host_threads=4, n_q=n_q, compute_streams=compute_streams)
+    assert pipe.compute_streams == (compute_streams or 2)
     outs = {}
     for t in range(steps):
         for l in range(L):
