@@ -82,6 +82,17 @@ def parse():
     return p.parse_args()
 
 
+def percentiles(values):
+    """p10 / p50 / p90 of a list of microsecond figures (linear
+    interpolation between order statistics)."""
+    if not values:
+        return {}
+    import numpy as np
+    p10, p50, p90 = np.percentile(np.asarray(values, dtype=np.float64), [10, 50, 90])
+    return {"p10_us": round(float(p10), 2), "p50_us": round(float(p50), 2), "p90_us": round(float(p90), 2),
+            "n": len(values)}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -293,7 +304,7 @@ def main():
     splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
     admitted = torch.zeros((), dtype=torch.int64, device=dev)
 
-    def run(t0, t1, counting=False):
+    def run(t0, t1, counting=False, step_events=None):
         for t in range(t0, t1):
             for l in range(L):
                 s = t + 3 * l
@@ -302,6 +313,11 @@ def main():
                     pipe.drain()
                     with torch.cuda.stream(pipe.comp_stream(l)):
                         admitted.add_(pipe.admitted(l, t))
+            if step_events is not None:
+                # the main stream passes the step's last attention
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(pipe.main)
+                step_events.append(ev)
 
     # initial fill (step 0) and warm-up; the warm-up steps also count the
     # admitted blocks per layer-step (a property of the workload's drift), so
@@ -315,8 +331,9 @@ def main():
     all_kinds = ("attn", "score", "topk", "plan") if staged else ("attn", "score", "topk")
     timed_kinds = all_kinds if args.kernel_timing == "all" else ("attn",)
     pipe.enable_timing(args.steps * L, timed_kinds)
+    step_events = []
     t0 = time.perf_counter()
-    run(1 + args.warmup, n_steps)
+    run(1 + args.warmup, n_steps, step_events=step_events)
     issued = time.perf_counter() - t0
     pipe.drain()
     torch.cuda.synchronize()
@@ -332,6 +349,10 @@ def main():
         return us
 
     live = {k: read_us(k, args.steps * L) for k in timed_kinds}
+    # distributions: each timed launch, and each decode step (intervals
+    # between the main stream's passes of consecutive steps), per layer-step
+    spread = {k: pipe.timing_values(k, args.steps * L) for k in timed_kinds}
+    step_us = [step_events[i - 1].elapsed_time(step_events[i]) * 1e3 / L for i in range(1, len(step_events))]
     copy_s, copy_n = pipe.copy_host_seconds()
     # the kinds not timed above: an extra pass of n_extra steps with events on
     # every launch, after the timed steps
@@ -342,6 +363,7 @@ def main():
         pipe.drain()
         torch.cuda.synchronize()
         extra = {k: read_us(k, n_extra * L) for k in all_kinds if k not in timed_kinds}
+        spread.update({k: pipe.timing_values(k, n_extra * L) for k in extra})
     t_last = n_total - 1
 
     def avg_us(name):
@@ -363,11 +385,13 @@ def main():
         us = avg_us(name)
         kern[name] = {"avg_us": round(us, 2), "bytes": nbytes,
                       "GBps": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None,
-                      "timed": "live, timed steps" if name in live else f"extra pass of {n_extra} steps"}
+                      "timed": "live, timed steps" if name in live else f"extra pass of {n_extra} steps",
+                      **percentiles(spread.get(name, []))}
     h2d = None
     if staged:
         kern["plan"] = {"avg_us": round(avg_us("plan"), 2), "note": "plan and prefix kernels",
-                        "timed": "live, timed steps" if "plan" in live else f"extra pass of {n_extra} steps"}
+                        "timed": "live, timed steps" if "plan" in live else f"extra pass of {n_extra} steps",
+                        **percentiles(spread.get("plan", []))}
         kern["copy_host"] = {"avg_us": round(copy_s / max(copy_n, 1) * 1e6, 2),
                               "note": ("host time of a staging call: plan read-back and packing up to the "
                                        "copy's enqueue") if copy_mode == oa.OASIS_COPY_DMA
@@ -505,6 +529,8 @@ def main():
         "h2d": h2d,
         "kernels": kern,
         "host_issue_ms_per_step": round(issued / layer_steps * 1e3, 4),
+        "layer_step_us": {**percentiles(step_us), "note": "per decode step of the timed region (main-stream "
+                          "events between consecutive steps) / layers in flight"},
     }
     print(json.dumps(line), flush=True)
 

@@ -526,6 +526,13 @@ int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity,
 int oasis_pipeline_timing_read(oasis_pipeline *p, int32_t kind,
                                double *total_ms, int32_t *count);
 
+/* The same timed launches one by one: ms[i] = milliseconds of the i-th timed
+ * launch of `kind` in launch order, for i < min(*count, capacity) (ms
+ * caller-owned host memory, may be NULL when capacity is 0); *count
+ * receives the number of timed launches.  Synchronises like timing_read. */
+int oasis_pipeline_timing_values(oasis_pipeline *p, int32_t kind, float *ms,
+                                 int32_t capacity, int32_t *count);
+
 /* Host seconds spent in the copy half of staging (plan read-back and packing
  * with OASIS_COPY_DMA, the enqueue with OASIS_COPY_KERNEL) since timing was
  * last armed, and the number of calls. */

@@ -108,6 +108,8 @@ _SIGNATURES = {
     "oasis_pipeline_timing": (ctypes.c_int, [_P, _I32, ctypes.c_uint32]),
     "oasis_pipeline_timing_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(_I32)]),
+    "oasis_pipeline_timing_values": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_float), _I32,
+                                                    ctypes.POINTER(_I32)]),
     "oasis_pipeline_copy_host_seconds": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_double),
                                                         ctypes.POINTER(_I32)]),
     "oasis_pipeline_destroy": (ctypes.c_int, [_P]),
@@ -550,6 +552,15 @@ def oasis_pipeline_timing_read(h: int, kind: int):
     ms, n = ctypes.c_double(), _I32()
     _check(_lib.oasis_pipeline_timing_read(h, int(kind), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def oasis_pipeline_timing_values(h: int, kind: int, capacity: int):
+    """Milliseconds of each timed launch of one kind, in launch order (at
+    most `capacity` of them)."""
+    buf = (ctypes.c_float * max(int(capacity), 1))()
+    n = _I32()
+    _check(_lib.oasis_pipeline_timing_values(h, int(kind), buf, int(capacity), ctypes.byref(n)))
+    return [buf[i] for i in range(min(n.value, int(capacity)))]
 
 
 def oasis_pipeline_copy_host_seconds(h: int):

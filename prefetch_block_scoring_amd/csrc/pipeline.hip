@@ -472,6 +472,22 @@ int oasis_pipeline_timing_read(oasis_pipeline *p, int32_t kind, double *total_ms
     return OASIS_OK;
 }
 
+int oasis_pipeline_timing_values(oasis_pipeline *p, int32_t kind, float *ms, int32_t capacity, int32_t *count) {
+    clear_error();
+    if (!p || !count || (!ms && capacity > 0)) PFAIL(OASIS_EINVAL, "pipeline, ms or count is NULL");
+    if (kind < 0 || kind >= kTimedKinds) PFAIL(OASIS_EINVAL, "kind = %d", kind);
+    if (capacity < 0) PFAIL(OASIS_EINVAL, "capacity = %d", capacity);
+    int rc = oasis_pipeline_drain(p);
+    if (rc) return rc;
+    const int n = p->t_n[kind] < capacity ? p->t_n[kind] : capacity;
+    for (int i = 0; i < n; i++) {
+        OASIS_HIP(hipEventSynchronize(p->t_ev[kind][2 * i + 1]));
+        OASIS_HIP(hipEventElapsedTime(&ms[i], p->t_ev[kind][2 * i], p->t_ev[kind][2 * i + 1]));
+    }
+    *count = p->t_n[kind];
+    return OASIS_OK;
+}
+
 int oasis_pipeline_copy_host_seconds(oasis_pipeline *p, double *seconds, int32_t *calls) {
     clear_error();
     if (!p || !seconds || !calls) PFAIL(OASIS_EINVAL, "pipeline, seconds or calls is NULL");

@@ -172,6 +172,10 @@ class LayerPipeline:
         ms, n = oa.oasis_pipeline_timing_read(self._h, TIMING_KINDS[kind])
         return (ms * 1e3 / n if n else 0.0), n
 
+    def timing_values(self, kind: str, capacity: int):
+        """Microseconds of each timed launch of `kind`, in launch order."""
+        return [ms * 1e3 for ms in oa.oasis_pipeline_timing_values(self._h, TIMING_KINDS[kind], capacity)]
+
     def copy_host_seconds(self):
         """(host seconds in the copy half of staging, calls) since timing
         was last enabled."""

@@ -454,3 +454,34 @@ def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams):
             for qi in range(n_q):
                 ref, _ = oracle.attend(u16(attn_q[s + 1][:, qi]), kv, ctx_np, blocks, nb, 1 / math.sqrt(w.D))
                 assert_attn_close(got[:, qi], ref)
+
+
+def test_pipeline_timing_values_match_totals():
+    """Per-launch timings of the native pipeline: one value per timed launch
+    of each kind (attention from step 1 on), all positive, summing to the
+    kind's total; launches past the capacity are not timed."""
+    from prefetch_block_scoring_amd.pipeline import LayerPipeline
+    m = oa()
+    w = wl.WORKLOADS["qwen3_8b_16k_b128_staged"].shrink(B=2, ctx=(3000, 9000))
+    C = oracle.fetch_cap_blocks(w.cap, w.K_b)
+    L, steps, cap = 2, 5, 6
+    ctx = wl.context_lengths(w).to(DEV)
+    host = m.oasis_host_empty((w.B, w.H_kv, w.NB_max, 2, w.bs, w.D))
+    host.copy_(wl.kv_pool(w))
+    summ = m.oasis_build_summaries(host, ctx)
+    looks = [wl.lookahead(w, s).to(DEV) for s in range(steps)]
+    attn_q = [looks[max(s - 1, 0)][:, 0].contiguous() for s in range(steps)]
+    pipe = LayerPipeline(pool=host, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=True, J=w.J)
+    pipe.enable_timing(cap, ("attn", "score", "topk", "plan"))
+    for t in range(steps):
+        for l in range(L):
+            pipe.layer_step(l, t, looks[t], attn_q[t])
+    launches = {"attn": (steps - 1) * L, "score": steps * L, "topk": steps * L, "plan": steps * L}
+    for kind, n in launches.items():
+        vals = pipe.timing_values(kind, 64)
+        avg, count = pipe.timing(kind)
+        assert count == min(n, cap) == len(vals), kind
+        assert all(v > 0 for v in vals), kind
+        assert abs(sum(vals) / count - avg) <= 1e-3 * avg + 1e-3, kind
+    assert len(pipe.timing_values("attn", 2)) == 2
+    pipe.close()
