@@ -130,14 +130,24 @@ def _attention_phases(trace_path, bench_log):
             line = json.loads(ln)
     if phases is None:
         return []
-    rows = [r for r in csv.DictReader(open(trace_path)) if "attn_kernel" in r["Kernel_Name"]]
-    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    all_rows = list(csv.DictReader(open(trace_path)))
+    by_start = lambda r: int(r["Start_Timestamp"])
+    rows = sorted((r for r in all_rows if "attn_kernel" in r["Kernel_Name"]), key=by_start)
+    comb = sorted((r for r in all_rows if "attn_combine_kernel" in r["Kernel_Name"]), key=by_start)
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
     out = [f"attention launches by bench phase ({os.path.basename(trace_path)}, {len(dur)} launches):"]
     expect = sum(phases.values())
     if len(dur) != expect:
         out.append(f"  launch count {len(dur)} differs from the bench's {expect}: not split")
         return out
+    # with split-K, each launch is the attention kernel and then its combine
+    # kernel; the HIP events bracket both, so the span (attention start to
+    # combine end) is what they compare with
+    span = None
+    if comb and len(comb) == len(rows):
+        out.append("  each launch: attention kernel + combine kernel (split-K); span = attention start to "
+                   "combine end")
+        span = [(int(c["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r, c in zip(rows, comb)]
     i = 0
     res = {}
     for name in ("warmup", "timed", "extra", "alone"):
@@ -145,12 +155,16 @@ def _attention_phases(trace_path, bench_log):
         if n:
             seg = dur[i:i + n]
             res[name] = sum(seg) / n
-            out.append(f"  {name:7s} {n:5d} launches  mean {res[name]:9.2f} us  min {min(seg):9.2f}  max {max(seg):9.2f}")
+            txt = f"  {name:7s} {n:5d} launches  mean {res[name]:9.2f} us  min {min(seg):9.2f}  max {max(seg):9.2f}"
+            if span:
+                res[name] = sum(span[i:i + n]) / n
+                txt += f"  span mean {res[name]:9.2f} us"
+            out.append(txt)
         i += n
     if line and "timed" in res:
         b = line["roofline"]["avg_launch_us"]
         out.append(f"  bench line (HIP events on the attention's stream, timed steps): {b:.2f} us; "
-                   f"trace / events = {res['timed'] / b:.3f}")
+                   f"trace {'span' if span else 'mean'} / events = {res['timed'] / b:.3f}")
     return out
 
 
