@@ -48,7 +48,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=4)
     p.add_argument("--layers", type=int, default=4, help="layers in flight")
     p.add_argument("--workload", default="qwen3_8b_16k_b128_staged")
-    p.add_argument("--copy-mode", choices=["kernel", "dma"], default="kernel")
+    p.add_argument("--copy-mode", choices=["kernel", "dma", "mixed"], default="kernel")
     p.add_argument("--host-threads", type=int, default=8, help="packing threads of the DMA copy engine")
     p.add_argument("--n-split", type=int, default=0)
     p.add_argument("--compute-streams", type=int, default=0, choices=[0, 1, 2],
@@ -280,7 +280,7 @@ def main():
     L = max(1, args.layers)
     C = oa.oasis_fetch_cap_blocks(w.cap, K_b) if staged else 0
     S = K_b + C
-    copy_mode = oa.OASIS_COPY_DMA if args.copy_mode == "dma" else oa.OASIS_COPY_KERNEL
+    copy_mode = {"kernel": oa.OASIS_COPY_KERNEL, "dma": oa.OASIS_COPY_DMA, "mixed": oa.OASIS_COPY_MIXED}[args.copy_mode]
     n_steps = 1 + args.warmup + args.steps              # step 0 = initial fill
     n_extra = min(args.steps, 16)                       # per-kernel timing pass after the timed steps
     n_total = n_steps + n_extra
@@ -408,7 +408,7 @@ def main():
                         **percentiles(spread.get("plan", []))}
         kern["copy_host"] = {"avg_us": round(copy_s / max(copy_n, 1) * 1e6, 2),
                               "note": ("host time of a staging call: plan read-back and packing up to the "
-                                       "copy's enqueue") if copy_mode == oa.OASIS_COPY_DMA
+                                       "copy's enqueue") if copy_mode != oa.OASIS_COPY_KERNEL
                               else "host time of a staging call (enqueue only)"}
         adm = int(admitted) / max(args.warmup * L, 1)
         h2d_bytes = adm * 2 * bs * D * 2
@@ -535,7 +535,7 @@ def main():
                    "layers_in_flight": L, "step_unit": "layer-step",
                    "kv_location": "pinned host pool + HBM working set" if staged else "HBM",
                    "copy_engine": args.copy_mode if staged else None,
-                   "host_threads": args.host_threads if staged and copy_mode == oa.OASIS_COPY_DMA else None,
+                   "host_threads": args.host_threads if staged and copy_mode != oa.OASIS_COPY_KERNEL else None,
                    "attn_splits": splits, "compute_streams": pipe.compute_streams,
                    "copy_streams": len(pipe.copy) if staged else None},
         "roofline": roofline,

@@ -58,6 +58,8 @@ extern "C" {
 /* Copy engines for oasis_stage_blocks. */
 #define OASIS_COPY_KERNEL 0      /* device kernel reads the mapped pinned pool */
 #define OASIS_COPY_DMA 1         /* host packs, DMA engine copies, device scatters */
+#define OASIS_COPY_MIXED 2       /* layer pipeline only: even layers OASIS_COPY_DMA,
+                                    odd layers OASIS_COPY_KERNEL */
 
 typedef struct oasis_dims {
     int32_t B;       /* requests in the batch (0 = nothing to do) */
@@ -456,7 +458,12 @@ typedef struct oasis_pipeline_desc {
                                  <= 16) */
     int32_t staged;           /* 1: pool is pinned host memory staged into
                                  per-layer working sets; 0: pool in HBM */
-    int32_t copy_mode;        /* OASIS_COPY_KERNEL or OASIS_COPY_DMA */
+    int32_t copy_mode;        /* OASIS_COPY_KERNEL, OASIS_COPY_DMA or
+                                 OASIS_COPY_MIXED (the DMA engine for even
+                                 layers, on one copy stream and the worker
+                                 thread, and the gather kernel for odd
+                                 layers, on a second copy stream: the link
+                                 carries both at once) */
     int32_t host_threads;     /* DMA packing threads (0 = 8) */
     int32_t n_split;          /* attention split count (0 = automatic) */
     float sm_scale;           /* attention scale, e.g. 1 / sqrt(D) */

@@ -4,7 +4,7 @@ top-K selection under a token budget, fetch-capped staging from a pinned host
 pool into an HBM working set, and sparse GQA decode attention, as HIP kernels
 for gfx950 behind the C ABI of liboasis.so (include/oasis.h)."""
 from .binding import (  # noqa: F401
-    OASIS_COPY_DMA, OASIS_COPY_KERNEL, OASIS_EHIP, OASIS_EINVAL, OASIS_ENOSPACE, OASIS_EUNSUPPORTED,
+    OASIS_COPY_DMA, OASIS_COPY_KERNEL, OASIS_COPY_MIXED, OASIS_EHIP, OASIS_EINVAL, OASIS_ENOSPACE, OASIS_EUNSUPPORTED,
     OASIS_OK, OasisError, dims, library, oasis_append_kv, oasis_attn_num_splits, oasis_block_attention_mass, oasis_block_mass_workspace_bytes,
     oasis_topk_overlap, oasis_attn_workspace_bytes,
     oasis_build_summaries, oasis_fetch_cap_blocks, oasis_host_empty, oasis_last_error, oasis_layer_buffers, oasis_lookahead_attn,

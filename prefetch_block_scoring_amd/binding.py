@@ -26,6 +26,7 @@ OASIS_EHIP = -3
 OASIS_ENOSPACE = -4
 OASIS_COPY_KERNEL = 0
 OASIS_COPY_DMA = 1
+OASIS_COPY_MIXED = 2  # layer pipeline only: even layers DMA, odd layers gather kernel
 
 _I32 = ctypes.c_int32
 _P = ctypes.c_void_p

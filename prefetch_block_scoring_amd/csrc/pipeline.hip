@@ -147,6 +147,12 @@ int worker_error(oasis_pipeline *p) {
     return p->err;
 }
 
+// The copy engine of layer l's staging.
+int layer_copy_mode(const oasis_pipeline_desc &ds, int l) {
+    if (ds.copy_mode == OASIS_COPY_MIXED) return (l & 1) ? OASIS_COPY_KERNEL : OASIS_COPY_DMA;
+    return ds.copy_mode;
+}
+
 int check_layer(const oasis_pipeline_desc &ds, const oasis_layer_buffers &b, int l, size_t plan_need,
                 size_t ws_need) {
 #define LNEED(ptr)                                                                   \
@@ -175,7 +181,7 @@ int check_layer(const oasis_pipeline_desc &ds, const oasis_layer_buffers &b, int
     for (int k = 0; k < 2; k++) LNEED(b.plan[k]);
     if (b.plan_bytes < plan_need)
         PFAIL(OASIS_ENOSPACE, "layer %d: plan buffers %zu bytes < %zu", l, b.plan_bytes, plan_need);
-    if (ds.copy_mode == OASIS_COPY_DMA) {
+    if (layer_copy_mode(ds, l) == OASIS_COPY_DMA) {
         LNEED(b.host_plan);
         LNEED(b.stage_host[0]);
         LNEED(b.stage_host[1]);
@@ -229,7 +235,7 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     if (ds.n_q < 1) PFAIL(OASIS_EINVAL, "n_q = %d < 1", ds.n_q);
     if (ds.staged != 0 && ds.staged != 1) PFAIL(OASIS_EINVAL, "staged = %d", ds.staged);
     if (ds.staged && (ds.C < 0 || ds.C > ds.K_b)) PFAIL(OASIS_EINVAL, "C = %d outside [0, K_b]", ds.C);
-    if (ds.copy_mode != OASIS_COPY_KERNEL && ds.copy_mode != OASIS_COPY_DMA)
+    if (ds.copy_mode != OASIS_COPY_KERNEL && ds.copy_mode != OASIS_COPY_DMA && ds.copy_mode != OASIS_COPY_MIXED)
         PFAIL(OASIS_EINVAL, "copy_mode = %d", ds.copy_mode);
     if (!ds.pool || !ds.kminmax || !ds.ctx_len || !ds.layers) PFAIL(OASIS_EINVAL, "pool, kminmax, ctx_len or layers is NULL");
     if (ds.n_split < 0 || ds.n_split > 64) PFAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", ds.n_split);
@@ -280,8 +286,12 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     // two by layer, so that the tail of one layer's gather overlaps the start
     // of the next one's; otherwise one (at most four streams in all, the
     // process's hardware queues).  The DMA engine's copies all go through
-    // one (its packing is serial anyway).
-    const int n_copy = !ds.staged ? 0 : (ds.copy_mode == OASIS_COPY_KERNEL && n_comp == 1 ? 2 : 1);
+    // one (its packing is serial anyway); the mixed engine has one for the
+    // DMA layers and one for the gather layers.
+    const int n_copy = !ds.staged                           ? 0
+                       : ds.copy_mode == OASIS_COPY_MIXED    ? 2
+                       : ds.copy_mode == OASIS_COPY_KERNEL && n_comp == 1 ? 2
+                                                              : 1;
     for (int c = 0; c < n_copy; c++)
         if ((e = hipStreamCreateWithFlags(&p->copy[c], hipStreamNonBlocking)) != hipSuccess)
             return fail(e, "hipStreamCreateWithFlags");
@@ -289,7 +299,7 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     for (auto &x : p->ev)
         if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess)
             return fail(e, "hipEventCreateWithFlags");
-    if (ds.staged && ds.copy_mode == OASIS_COPY_DMA) p->worker = std::thread(worker_loop, p);
+    if (ds.staged && ds.copy_mode != OASIS_COPY_KERNEL) p->worker = std::thread(worker_loop, p);
     *out = p;
     return OASIS_OK;
 }
@@ -309,11 +319,12 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     const oasis_dims *d = &p->d;
     const int K_b = ds.K_b;
     const int j = t % 2;
+    const int mode = layer_copy_mode(ds, l);
 
     // foreground: attention of step t
     if (t >= 1) {
         if (ds.staged) {
-            if (ds.copy_mode == OASIS_COPY_DMA) {
+            if (mode == OASIS_COPY_DMA) {
                 std::unique_lock<std::mutex> lk(p->mu);
                 p->cv_done.wait(lk, [&] { return p->done[l] >= t - 1 || p->err != OASIS_OK; });
             }
@@ -387,8 +398,10 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     a.stage_dev = b.stage_dev;
     a.stage_dev_bytes = b.stage_bytes;
     a.host_threads = ds.host_threads;
-    a.copy_mode = ds.copy_mode;
+    a.copy_mode = mode;
     a.stream = cs;
+    // mixed: copy[0] carries the DMA (even) layers, copy[1] the gathers (odd);
+    // otherwise the layers alternate over the copy streams there are
     a.copy_stream = p->copy[p->copy[1] ? (l & 1) : 0];
     a.wait_event = t >= 1 ? p->event(kEvAttn, l, t - 1) : nullptr;
     a.done_event = p->event(kEvStage, l, t);
@@ -396,7 +409,7 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     timed_begin(p, 3, cs);
     if ((rc = oasis_stage_plan(d, &a))) return rc;
     timed_end(p, 3, cs);
-    if (ds.copy_mode == OASIS_COPY_DMA) {
+    if (mode == OASIS_COPY_DMA) {
         {
             std::lock_guard<std::mutex> lk(p->mu);
             p->jobs.push_back(job);

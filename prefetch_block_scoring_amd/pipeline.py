@@ -15,7 +15,8 @@ include/oasis.h) schedules that chain on one GPU:
                   units; `compute_streams` overrides)
   copy streams    the copies of (l, t) (gather kernels, on two streams by
                   layer parity when there is one compute stream, or DMA
-                  copy + scatter on the pipeline's worker thread)
+                  copy + scatter on the pipeline's worker thread, or, mixed,
+                  DMA for even layers and gathers for odd layers)
 
 `LayerPipeline` allocates the per-layer buffers the native pipeline works in
 (three attention tables, two selections and two plan buffers per layer, the
@@ -61,7 +62,7 @@ class _Layer:
                           torch.zeros((B, H_kv), dtype=i32, device=dev)) for _ in range(3)]
             n_plan = oa.oasis_stage_plan_bytes(B, H_kv, K_b) // 4
             self.plans = [torch.empty(n_plan, dtype=i32, device=dev) for _ in range(2)]
-            if copy_mode == oa.OASIS_COPY_DMA:
+            if copy_mode in (oa.OASIS_COPY_DMA, oa.OASIS_COPY_MIXED):
                 self.host_plan = oa.oasis_host_empty((n_plan,), i32)
                 sbytes = oa.oasis_stage_buffer_bytes(B * H_kv * max(C, 1))
                 self.stage_host = [oa.oasis_host_empty((sbytes,), torch.uint8) for _ in range(2)]
