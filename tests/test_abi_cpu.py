@@ -235,3 +235,30 @@ def test_lookahead_attention_argument_errors():
     assert oa.oasis_lookahead_attn_workspace_bytes(2, 32, 8, 3, 128, 3) == 2 * 3 * 32 * 3 * 130 * 4
     assert oa.oasis_lookahead_attn_workspace_bytes(2, 32, 8, 1, 128, 3) == oa.oasis_attn_workspace_bytes(
         2, 32, 8, 128, 3)
+
+
+def test_mixed_copy_mode_needs_dma_buffers_on_even_layers_only():
+    """OASIS_COPY_MIXED stages even layers through the DMA engine: their
+    host staging buffers are required, the odd layers' are not."""
+    d, bufs = _pipeline_desc(L=3, copy_mode=oa.OASIS_COPY_MIXED)
+    bufs[0].stage_dev = None
+    with pytest.raises(oa.OasisError) as e:
+        oa.oasis_pipeline_create(oa.dims(4, 32, 8, 1024), d)
+    assert e.value.code == oa.OASIS_EINVAL
+    assert "layer 0" in oa.oasis_last_error()
+    # an odd layer without them passes the buffer checks: the description
+    # is then refused for the next layer that needs them (layer 2)
+    d, bufs = _pipeline_desc(L=3, copy_mode=oa.OASIS_COPY_MIXED)
+    bufs[1].stage_dev = None
+    bufs[1].host_plan = None
+    bufs[2].stage_dev = None
+    with pytest.raises(oa.OasisError) as e:
+        oa.oasis_pipeline_create(oa.dims(4, 32, 8, 1024), d)
+    assert e.value.code == oa.OASIS_EINVAL
+    assert "layer 2" in oa.oasis_last_error()
+
+
+def test_timing_values_rejects_bad_arguments():
+    lib = binding.library()
+    n = ctypes.c_int32()
+    assert lib.oasis_pipeline_timing_values(None, 0, None, 0, ctypes.byref(n)) == oa.OASIS_EINVAL
