@@ -129,6 +129,7 @@ def resident_table(st, R, H, K_b):
     ("reasoning_32k_b64_j4", 0),
     ("gqa32b_ragged_b16_staged", 0),
     ("gqa32b_ragged_b16_staged", 1),
+    ("qwen3_8b_16k_b128_staged", 2),
 ])
 def test_full_size_sampled(name, copy_mode):
     w = wl.WORKLOADS[name]
