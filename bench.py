@@ -168,6 +168,25 @@ def _attention_phases(trace_path, bench_log):
     return out
 
 
+def _raw_counters(rows, fname, machine):
+    """Counters other than FETCH_SIZE / WRITE_SIZE, per dispatch of each of
+    the library's kernels in dispatch order (TCC_EA0_*_32B counters also as
+    bytes: 32 per count)."""
+    out = [f"counters ({fname}), per dispatch:"]
+    per = {}
+    for r in rows:
+        if "oasis" not in r["Kernel_Name"]:
+            continue
+        key = (_short(r["Kernel_Name"]), int(r["Dispatch_Id"]))
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    for (k, disp), vals in sorted(per.items(), key=lambda kv: kv[0][1]):
+        txt = "  ".join(f"{c} {v:.0f}" + (f" ({v * 32 / 1e6:.2f} MB)" if c.endswith("_32B_sum") else "")
+                        for c, v in sorted(vals.items()))
+        out.append(f"  {k:28s} dispatch {disp:6d}  {txt}")
+        machine.setdefault(k, {}).setdefault("dispatches", []).append(vals)
+    return out
+
+
 def summarize_profile(dirs, command, bench_log=None):
     """Reduce rocprofv3 CSV output to a short text summary: per-kernel call
     counts and durations, and, from FETCH_SIZE / WRITE_SIZE runs, HBM bytes
@@ -198,7 +217,11 @@ def summarize_profile(dirs, command, bench_log=None):
             rows = list(csv.DictReader(open(path)))
             if not rows:
                 continue
-            counter = rows[0]["Counter_Name"]
+            counters = sorted({r["Counter_Name"] for r in rows})
+            if counters not in (["FETCH_SIZE"], ["WRITE_SIZE"]):
+                out.extend(_raw_counters(rows, os.path.basename(path), machine))
+                continue
+            counter = counters[0]
             per = {}
             for r in rows:
                 per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
@@ -215,6 +238,13 @@ def summarize_profile(dirs, command, bench_log=None):
                 out.append(f"  {_short(k):40s} dispatches {len(v):4d} mean {kib:12.1f} KiB -> "
                            f"{byt / 1e6 if byt else float('nan'):10.2f} MB per dispatch (calibrated)")
                 machine.setdefault(_short(k), {})[counter] = byt
+    if bench_log:
+        for ln in open(bench_log):
+            if ln.startswith("{"):
+                h2d = json.loads(ln).get("h2d")
+                if h2d:
+                    out.append(f"bench line: admitted blocks per layer-step over the warm-up steps "
+                               f"{h2d['blocks_per_layer_step']}, {h2d['bytes_per_layer_step'] / 1e6:.2f} MB")
     for k, v in machine.items():
         for src_key, fname in KERNEL_SOURCES.items():
             if k.endswith(src_key) or src_key in k:
