@@ -283,7 +283,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by request and KV head with no exchange, see DESIGN.md", file=sys.stderr)
+              "the path shards by request and KV head with no exchange between GPUs", file=sys.stderr)
         sys.exit(2)
 
     if args.agreement:
