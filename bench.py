@@ -282,7 +282,7 @@ def main():
         summarize_profile(args.summarize_profile, args.command, args.bench_log)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by request and KV head with no exchange between GPUs", file=sys.stderr)
         sys.exit(2)
 
