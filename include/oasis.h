@@ -481,12 +481,15 @@ typedef struct oasis_pipeline_desc {
                                  compute-unit count (top-K and the plan run
                                  one workgroup per (request, KV head) and
                                  would leave most compute units idle), else 1.
-                                 Staged with 2: one copy stream; staged with
-                                 1 and OASIS_COPY_KERNEL: two copy streams
-                                 (even and odd layers), so one gather's tail
-                                 overlaps the next one's start.  At most four
-                                 streams in all, the hardware queues of a
-                                 process. */
+                                 Copy streams: OASIS_COPY_KERNEL with one
+                                 compute stream, two (even and odd layers),
+                                 so one gather's tail overlaps the next one's
+                                 start; OASIS_COPY_MIXED, two (the DMA layers
+                                 and the gather layers); otherwise one.  With
+                                 one compute stream that keeps to four
+                                 streams, the hardware queues of a process;
+                                 two compute streams with the mixed engine
+                                 make five. */
 } oasis_pipeline_desc;
 
 typedef struct oasis_pipeline oasis_pipeline;
