@@ -227,17 +227,22 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
             psum += p;
         }
         l_run = l_run * alpha + psum;
+        // the accumulators need rescaling only if some column's running max
+        // moved (otherwise alpha is exactly 1, or 0 on still-zero sums)
+        const bool moved = __ballot(m_new != m_run) != 0;
         m_run = m_new;
         if (grp == 0) pl[16][col] = alpha;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+        if (moved) {
 #pragma unroll
-        for (int g = 0; g < GP; g++) {
-            const float al = pl[16][g];
+            for (int g = 0; g < GP; g++) {
+                const float al = pl[16][g];
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[g][e] *= al;
+                for (int e = 0; e < 8; e++) acc[g][e] *= al;
+            }
         }
 #pragma unroll
         for (int qq = 0; qq < 4; qq++) {
