@@ -6,6 +6,7 @@ Each test names what fixes the expected value: brute force written differently
 worked by hand from that section's staging rule.  No GPU is used.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -206,16 +207,36 @@ def test_planted_blocks_are_all_selected(name):
 # fetch cap and staging
 
 
+def _golden(name):
+    """key -> float from a fixture under tests/golden/ (# lines are comments)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    out = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            out[k] = float(v)
+    return out
+
+
 def test_fetch_cap_closed_forms():
-    """Cap 0.01 moves 0.30 GB per step for Qwen3-8B at batch 128 (agihunt
-    summary, fetch-cap ablation): C = 1 block of 8 KiB per KV head, 8 KV heads,
-    36 layers (Qwen3-8B's layer count), 128 requests, in decimal GB."""
-    K_b = 2048 // 16
-    block_bytes = 2 * 16 * 128 * 2
-    C = oracle.fetch_cap_blocks(0.01, K_b)
+    """The pages' traffic at the lowest fetch cap (agihunt summary,
+    fetch-cap ablation; fixture tests/golden/fetch_cap_ablation.txt): the
+    oracle's cap rule gives C = 1 block of 8 KiB K+V per KV head and layer,
+    which over 8 KV heads, 36 layers and 128 requests is the printed 0.30 GB
+    per step in decimal GB (a ceiling would give 0.60)."""
+    g = _golden("fetch_cap_ablation.txt")
+    bs, D = int(g["block_tokens"]), int(g["head_dim"])
+    K_b = int(g["kv_budget_tokens"]) // bs
+    block_bytes = 2 * bs * D * 2
+    per_step = block_bytes * g["kv_heads"] * g["layers"] * g["batch"]
+    C = oracle.fetch_cap_blocks(g["cap_low"], K_b)
     assert C == 1
-    gb = C * block_bytes * 8 * 36 * 128 / 1e9
-    assert round(gb, 2) == 0.30
+    assert round(C * per_step / 1e9, 2) == g["traffic_gb_per_step_at_cap_low"]
+    # fetch-all moves every newly selected block: the printed 5.05 GB per
+    # step is ~16.7 blocks per (request, KV head, layer), within the budget
+    fetch_all_blocks = g["traffic_gb_per_step_fetch_all"] * 1e9 / per_step
+    assert 16 < fetch_all_blocks < 17 and fetch_all_blocks < K_b
     assert oracle.fetch_cap_blocks(0.05, K_b) == 6
     assert oracle.fetch_cap_blocks(1.0, K_b) == K_b
     assert oracle.fetch_cap_blocks(0.0, K_b) == 0
