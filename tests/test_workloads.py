@@ -8,14 +8,18 @@ from test_oracle_pins import u16
 
 
 def test_32b_class_footprint_closed_form():
-    """A 32B-class GQA model keeps 256 KiB of KV per token in bf16 over its 64
-    layers, 8.6 GB per request at 32.7K context, 9 requests in 80 GB
-    (paperlayer summary, section 2; agihunt summary)."""
+    """The pages' KV footprint of a 32B-class GQA model (paperlayer summary,
+    section 2; fixture tests/golden/kv_footprint_32b_class.txt): the
+    workload's KV heads and head dim over 64 layers give the printed 256 KiB
+    per token in bf16, 8.6 GB per request at 32.7K context and nine requests
+    in 80 GB."""
+    from test_oracle_pins import _golden
+    g = _golden("kv_footprint_32b_class.txt")
     w = wl.WORKLOADS["gqa32b_ragged_b16_staged"]
-    per_token = 64 * w.H_kv * w.D * 2 * 2
-    assert per_token == 256 * 1024
-    assert round(32.7e3 * per_token / 1e9, 1) == 8.6
-    assert int(80e9 // (32.7e3 * per_token)) == 9
+    per_token = int(g["layers"]) * w.H_kv * w.D * 2 * 2
+    assert per_token == g["kib_per_token"] * 1024
+    assert round(g["avg_context_tokens"] * per_token / 1e9, 1) == g["gb_per_request"]
+    assert int(g["hbm_gb"] * 1e9 // (g["avg_context_tokens"] * per_token)) == g["requests_fit"]
 
 
 def test_qwen3_8b_shapes():
