@@ -38,7 +38,7 @@ def lib():
         L.oracle_select.argtypes = [I, I, I, I, P, P, I, P, P]
         L.oracle_fetch_cap_blocks.argtypes = [ctypes.c_double, I]
         L.oracle_fetch_cap_blocks.restype = I
-        L.oracle_stage.argtypes = [I, I, I, I, P, P, P, I, P, I, I, I, P, P, P, P, P]
+        L.oracle_stage.argtypes = [I, I, I, I, P, P, P, I, P, I, I, I, P, P, P, P, P, P]
         L.oracle_attend.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, ctypes.c_double, P, P]
         L.oracle_append.argtypes = [I, I, I, I, I, P, P, P, P, P]
         L.oracle_append.restype = None
@@ -122,6 +122,9 @@ class StageState:
 
     def __init__(self, B, H_kv, NB_max):
         self.stamp = np.full((B, H_kv, NB_max), -1, dtype=_i32)
+        # per (r, h), after each step: predicted blocks that were neither
+        # resident nor admitted (held back by the cap)
+        self.deferred = np.zeros((B, H_kv), dtype=_i32)
 
     def resident(self, r, h):
         return np.nonzero(self.stamp[r, h] >= 0)[0]
@@ -130,8 +133,10 @@ class StageState:
 def stage(state: StageState, sel, n_sel, scores, ctx_len, bs: int, K_b: int, C: int, step: int):
     """One staging step (section 4: keep resident predicted blocks, admit at
     most C non-resident ones, pair them with least-recently-selected victims).
-    Updates ``state`` in place; returns (admitted, n_admitted, evicted,
-    n_evicted) with admitted/evicted int32 [B][H_kv][max(C,1)] in order."""
+    Updates ``state`` in place (``state.deferred`` receives the predicted
+    blocks held back by the cap, |P \\ R| - |A| per pair); returns (admitted,
+    n_admitted, evicted, n_evicted) with admitted/evicted int32
+    [B][H_kv][max(C,1)] in order."""
     sel = _c(sel, _i32)
     n_sel = _c(n_sel, _i32)
     sc = _c(scores, np.float32)
@@ -144,7 +149,7 @@ def stage(state: StageState, sel, n_sel, scores, ctx_len, bs: int, K_b: int, C: 
     ne = np.zeros((B, H_kv), dtype=_i32)
     assert sc.shape == (B, H_kv, NB)
     lib().oracle_stage(B, H_kv, NB, bs, _p(ctx), _p(sel), _p(n_sel), sel.shape[2], _p(sc),
-                       K_b, C, step, _p(state.stamp), _p(adm), _p(na), _p(ev), _p(ne))
+                       K_b, C, step, _p(state.stamp), _p(adm), _p(na), _p(ev), _p(ne), _p(state.deferred))
     return adm, na, ev, ne
 
 

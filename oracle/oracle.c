@@ -218,6 +218,8 @@ int oracle_fetch_cap_blocks(double cap, int K_b)
 /* bring them back); resident blocks no longer predicted stay resident until */
 /* evicted.  Predicted ids outside [0, n_b) or repeated are ignored.          */
 /* admitted [B][H_kv][max(C,1)] in admission order, evicted likewise.         */
+/* n_deferred [B][H_kv] (may be NULL): |P \ R| - |A|, the predicted blocks    */
+/* that were neither resident nor admitted, i.e. held back by the cap C.      */
 /* ------------------------------------------------------------------------ */
 typedef struct { int32_t key; int32_t id; } stamped_block;
 
@@ -232,7 +234,7 @@ void oracle_stage(int B, int H_kv, int NB_max, int bs, const int32_t *ctx_len,
                   const int32_t *sel, const int32_t *n_sel, int K_sel,
                   const float *scores, int K_b, int C, int step,
                   int32_t *res_stamp, int32_t *admitted, int32_t *n_admitted,
-                  int32_t *evicted, int32_t *n_evicted)
+                  int32_t *evicted, int32_t *n_evicted, int32_t *n_deferred)
 {
     const int Cs = C > 0 ? C : 1;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -295,6 +297,7 @@ void oracle_stage(int B, int H_kv, int NB_max, int bs, const int32_t *ctx_len,
             }
             n_admitted[rh] = na;
             n_evicted[rh] = need;
+            if (n_deferred) n_deferred[rh] = nc - na;
             free(old);
             free(cand);
             free(pred);

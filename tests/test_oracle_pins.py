@@ -243,12 +243,14 @@ def test_fetch_cap_closed_forms():
     assert oracle.fetch_cap_blocks(1e-9, K_b) == 1
 
 
-def run_stage(steps_P, steps_scores, n_b, K_b, Cs):
-    """Drive the oracle for one (r, h) through hand-written predicted sets."""
+def run_stage(steps_P, steps_scores, n_b, K_b, Cs, deferred=None):
+    """Drive the oracle for one (r, h) through hand-written predicted sets;
+    `deferred` (a list) receives the held-back count of each step."""
     NB = n_b
     st = oracle.StageState(1, 1, NB)
     ctx = np.array([n_b * 16], dtype=np.int32)
     log = []
+    deferred = [] if deferred is None else deferred
     for s, (P, sc, C) in enumerate(zip(steps_P, steps_scores, Cs)):
         sel = np.full((1, 1, K_b), -1, dtype=np.int32)
         sel[0, 0, :len(P)] = sorted(P)
@@ -259,6 +261,7 @@ def run_stage(steps_P, steps_scores, n_b, K_b, Cs):
         adm, na, ev, ne = oracle.stage(st, sel, n, score, ctx, 16, K_b, C, s)
         log.append((adm[0, 0, :na[0, 0]].tolist(), ev[0, 0, :ne[0, 0]].tolist(),
                     {int(b): int(st.stamp[0, 0, b]) for b in st.resident(0, 0)}))
+        deferred.append(int(st.deferred[0, 0]))
     return log
 
 
@@ -276,11 +279,16 @@ def test_stage_worked_example():
       R = {2:3, 3:3, 5:2}.
     step 4 (C = 1): P = {0,1,3}, s0 = s1 = 2.  3 -> 4; tie -> admit 0; victim
       among {2 (stamp 3), 5 (stamp 2)}: 5, though its id is larger.
-      R = {0:4, 2:3, 3:4}."""
+      R = {0:4, 2:3, 3:4}.
+    Held back by the cap (predicted, neither resident nor admitted): step 2
+    leaves block 2 out, step 4 block 1; the other steps admit every missing
+    predicted block."""
+    deferred = []
     log = run_stage(
         steps_P=[[1, 3, 5], [0, 3, 4], [2, 3, 5], [2, 3], [0, 1, 3]],
         steps_scores=[{}, {0: 5, 4: 7}, {2: 1, 5: 9}, {}, {0: 2, 1: 2}],
-        n_b=6, K_b=3, Cs=[3, 2, 1, 1, 1])
+        n_b=6, K_b=3, Cs=[3, 2, 1, 1, 1], deferred=deferred)
+    assert deferred == [0, 0, 1, 0, 1]
     assert log[0] == ([1, 3, 5], [], {1: 0, 3: 0, 5: 0})
     assert log[1] == ([4, 0], [1, 5], {0: 1, 3: 1, 4: 1})
     assert log[2] == ([5], [0], {3: 2, 4: 1, 5: 2})
@@ -322,6 +330,10 @@ def test_stage_invariants_over_random_sequences(C, turnover):
                 assert len(A) <= Cs and len(R1) <= K_b
                 assert set(A) <= P - R0 and R1 == (R0 - set(E)) | set(A)
                 assert len(A) == min(Cs, len(P - R0))
+                # the held-back count: missing predicted blocks not admitted
+                assert int(st.deferred[r, h]) == len(P - R0) - len(A)
+                if Cs == K_b:
+                    assert int(st.deferred[r, h]) == 0
                 # admitted are the best-scoring of P \ R0
                 sc = scores[s][r, h].numpy()
                 rest = (P - R0) - set(A)
