@@ -3,14 +3,14 @@
  * scoring with sparse KV staging, for AMD Instinct MI355X (gfx950).
  *
  * The method is OasisKV (arXiv 2608.08097, "OasisKV: Scaling In-Decode KV
- * Cache Beyond HBM with Lookahead Sparse Prefetching").  Its per-layer decode
- * chain, as the paperlayer summary's section 4 ("System Design") states it:
- * draft (lookahead) queries scan per-block min/max key summaries to rank
- * blocks; a top-K block set under a token budget is predicted; selection keeps
- * resident predicted blocks and admits at most C new blocks per KV head per
- * layer, evicting least-recently-selected ones; the admitted blocks are copied
- * from off-GPU memory into an HBM working set; attention then runs over the
- * staged blocks only.  One entry point below per step.
+ * Cache Beyond HBM with Lookahead Sparse Prefetching"); the paperlayer
+ * summary's section 4 ("System Design") describes the per-layer decode chain
+ * that these calls implement, one entry point per step: block scores from the
+ * draft queries against two summary vectors per block (coordinate-wise key
+ * minimum and maximum); the best blocks that fit a token budget; an update of
+ * the HBM working set that brings in at most C missing blocks per KV head and
+ * layer in place of the blocks predicted longest ago, copying them from the
+ * host copy of the cache; attention over the working set alone.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -119,7 +119,7 @@ int oasis_build_summaries(const oasis_dims *dims, const uint16_t *kv,
  *   ctx_len  [B] int32, device
  *   scores   [B][H_kv][NB_max] fp32, device, written
  * Requires J >= 1 and ctx_len[r] <= NB_max * bs (larger values are clamped to
- * NB_max blocks).  J > 64, or B * H_kv * ceil(NB_max / 128) above 2^31 - 1,
+ * NB_max blocks).  J > 64, or B * H_kv * ceil(NB_max / 64) above 2^31 - 1,
  * returns OASIS_EUNSUPPORTED. */
 int oasis_score_blocks(const oasis_dims *dims, const uint16_t *q_look,
                        int32_t J, const uint16_t *kminmax,
@@ -139,12 +139,11 @@ int oasis_select_topk(const oasis_dims *dims, const float *scores,
                       const int32_t *ctx_len, int32_t K_b, int32_t *sel,
                       int32_t *n_sel, void *stream);
 
-/* Staging of the predicted set into the HBM working set (section 4: selection
- * preserves resident predicted blocks, admits at most C non-resident
- * predicted blocks per KV head per layer and pairs them with
- * least-recently-selected eviction targets; the admitted blocks are copied
- * from the off-GPU pool into HBM before the next step's attention).
- *
+/* Staging of the predicted set into the HBM working set (section 4: the
+ * predicted blocks already resident stay; at most C missing ones per KV head
+ * and layer are brought in, each displacing the resident block whose last
+ * prediction is oldest; the copies come from the off-GPU pool and must land
+ * before the next step's attention). *
  * State per (request r, KV head h) lives in a slot table of S slots:
  * slot_block[s] is the block held by slot s (-1 = free) and slot_stamp[s] the
  * last step at which that block was predicted or admitted.  The resident set
@@ -238,7 +237,26 @@ typedef struct oasis_stage_args {
     void *wait_event;
     void *done_event;
     void *plan_event;       /* optional: recorded after the plan kernels */
+    int64_t *stats_accum;   /* optional, device int64[4]: the plan kernels add
+                               this step's admits, evictions and deferred
+                               admits (oasis_stage_stats) to [0], [1], [2] and
+                               1 to [3], with device atomics, so a caller can
+                               count any run of steps without reading back
+                               each plan; the caller clears it */
 } oasis_stage_args;
+
+/* Counts of one staging step, summed over the (request, KV head) pairs.
+ * Deferred admits are the predicted blocks that were neither resident nor
+ * admitted, |P \ R| - |A| per pair: the blocks the fetch cap C (section 4:
+ * at most C blocks per KV head and layer) held back this step.  A later
+ * prediction may bring them in; until then attention runs without them. */
+typedef struct oasis_stage_stats {
+    int64_t admits;        /* blocks admitted, each copied host -> HBM */
+    int64_t evictions;     /* resident blocks evicted to make room */
+    int64_t deferred;      /* predicted blocks neither resident nor admitted */
+    int64_t capped_pairs;  /* pairs with at least one deferred admit */
+    int64_t bytes;         /* admits * 2 * bs * D * 2: bytes copied */
+} oasis_stage_stats;
 
 /* Appending one decoded token per request (section 4: the full KV lives
  * off-GPU while HBM keeps the per-block key summaries and the working set).
@@ -308,10 +326,23 @@ size_t oasis_stage_buffer_bytes(const oasis_dims *dims, int32_t n_blocks);
 /* One staging step.  Once the plan kernels have run, the plan workspace holds
  * int32 [B * H_kv][4 + 2 * max(C, 1)] followed by 4 int32: per (r, h) the
  * admit count, the evict count, the packed position of its first admit (the
- * running total of admits over the (r, h) before it), a reserved word, then
- * the admitted (slot, block) pairs in admission order; after the rows the
- * total number of admits.  The host plan (OASIS_COPY_DMA) receives a copy. */
-int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *args);
+ * running total of admits over the (r, h) before it), the deferred admits,
+ * then the admitted (slot, block) pairs in admission order; after the rows
+ * the step's total admits, evictions and deferred admits, and the number of
+ * pairs with deferred admits.  The host plan (OASIS_COPY_DMA) receives a
+ * copy.  `stats` may be NULL; otherwise the call also waits (blocking the
+ * calling thread) until the plan kernels have run and fills it in for this
+ * step. */
+int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *args,
+                       oasis_stage_stats *stats);
+
+/* The counts of the step whose plan is in `plan` (a plan workspace for
+ * `dims` and fetch cap C, as oasis_stage_plan or oasis_stage_blocks wrote
+ * it): waits for `stream` (blocking the calling thread), then reads the
+ * plan's totals.  Errors: EINVAL for NULL arguments or C < 0. */
+int oasis_stage_read_stats(const oasis_dims *dims, int32_t C,
+                           const int32_t *plan, oasis_stage_stats *stats,
+                           void *stream);
 
 /* The two halves of oasis_stage_blocks, for callers that overlap staging
  * across layers: oasis_stage_plan enqueues the plan kernels (steps 1-4 and
@@ -392,13 +423,11 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
 /* ---------------------------------------------------------------------------
  * Layer pipeline: the per-layer decode chain, scheduled in native code.
  *
- * Section 4 of the paperlayer summary runs, per layer, a background chain of
- * prediction (scores and top-K), selection (the staging plan) and transfer,
- * overlapped across layers and decode steps; the foreground waits only for a
- * layer's own transfer before that layer's next-step attention.  A pipeline
- * enqueues one layer-step of that schedule per call, every launch, event
- * record and stream wait made from native code:
- *
+ * Section 4 of the paperlayer summary keeps prediction, selection and copies
+ * off the attention's critical path, with several layers and decode steps in
+ * flight, and holds a layer's attention back only until its own copies are
+ * in.  A pipeline enqueues one layer-step of that schedule per call, every
+ * launch, event record and stream wait made from native code: *
  *   main stream (the caller's)   attention of (l, t) over the working set
  *                                staged at (l, t - 1)
  *   compute streams (owned)      scores and top-K of (l, t), staging plan;
@@ -490,6 +519,11 @@ typedef struct oasis_pipeline_desc {
                                  streams, the hardware queues of a process;
                                  two compute streams with the mixed engine
                                  make five. */
+    int64_t *stage_stats;     /* optional, device int64[4]: every staging
+                                 step of every layer adds its admits,
+                                 evictions, deferred admits and 1 (see
+                                 oasis_stage_args.stats_accum); the caller
+                                 clears it */
 } oasis_pipeline_desc;
 
 typedef struct oasis_pipeline oasis_pipeline;

@@ -52,7 +52,15 @@ class oasis_stage_args(ctypes.Structure):
         ("host_plan_bytes", ctypes.c_size_t), ("stage_host", _P), ("stage_host_bytes", ctypes.c_size_t),
         ("stage_dev", _P), ("stage_dev_bytes", ctypes.c_size_t), ("host_threads", _I32),
         ("copy_mode", _I32), ("stream", _P), ("copy_stream", _P), ("wait_event", _P),
-        ("done_event", _P), ("plan_event", _P)]
+        ("done_event", _P), ("plan_event", _P), ("stats_accum", _P)]
+
+
+class oasis_stage_stats(ctypes.Structure):
+    _fields_ = [("admits", ctypes.c_int64), ("evictions", ctypes.c_int64), ("deferred", ctypes.c_int64),
+                ("capped_pairs", ctypes.c_int64), ("bytes", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {k: int(getattr(self, k)) for k, _ in self._fields_}
 
 
 class oasis_layer_buffers(ctypes.Structure):
@@ -69,7 +77,7 @@ class oasis_pipeline_desc(ctypes.Structure):
         ("copy_mode", _I32),
         ("host_threads", _I32), ("n_split", _I32), ("sm_scale", ctypes.c_float), ("pool", _P),
         ("kminmax", _P), ("ctx_len", _P), ("main_stream", _P), ("layers", ctypes.POINTER(oasis_layer_buffers)),
-        ("compute_streams", _I32)]
+        ("compute_streams", _I32), ("stage_stats", _P)]
 
 
 # name -> (restype, argtypes)
@@ -84,7 +92,10 @@ _SIGNATURES = {
     "oasis_select_topk": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P]),
     "oasis_stage_plan_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32]),
     "oasis_stage_buffer_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32]),
-    "oasis_stage_blocks": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args)]),
+    "oasis_stage_blocks": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args),
+                                          ctypes.POINTER(oasis_stage_stats)]),
+    "oasis_stage_read_stats": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _I32, _P,
+                                              ctypes.POINTER(oasis_stage_stats), _P]),
     "oasis_stage_plan": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args)]),
     "oasis_stage_copy": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args)]),
     "oasis_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32, _I32]),
@@ -162,17 +173,43 @@ def _event(ev) -> Optional[int]:
     return ev.cuda_event
 
 
-def _need(t: torch.Tensor, name: str, dtype, ndim: int, device: Optional[str] = "cuda"):
+def _on_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device: Optional[str] = "cuda", shape=None):
+    """Type, rank, contiguity and device of one argument; with `shape`, its
+    exact shape.  The C entry points see only pointers, so every size they
+    index with is checked here before anything is enqueued."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: expected shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if device == "cuda" and not t.is_cuda:
+    if device == "cuda" and not _on_device(t):
         raise ValueError(f"{name} must be a device tensor")
+
+
+def _need_bytes(t: torch.Tensor, name: str, device: Optional[str] = "cuda"):
+    """A workspace of any dtype: contiguous, on the device (or host)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device == "cuda" and not _on_device(t):
+        raise ValueError(f"{name} must be a device tensor")
+    if device == "host" and _on_device(t):
+        raise ValueError(f"{name} must be a host tensor")
+
+
+def _group(H_q: int, H_kv: int):
+    if H_kv <= 0 or H_q % H_kv != 0:
+        raise ValueError(f"H_q = {H_q} is not a multiple of H_kv = {H_kv}")
 
 
 def dims(B, H_q, H_kv, NB_max, D=128, bs=16) -> oasis_dims:
@@ -217,10 +254,13 @@ def oasis_build_summaries(kv: torch.Tensor, ctx_len: torch.Tensor, kminmax=None,
     kminmax bf16 [B][H_kv][NB_max][2][D]."""
     _need(kv, "kv", torch.bfloat16, 6, device=None)
     _need(ctx_len, "ctx_len", torch.int32, 1)
-    B, H_kv, NB, _, bs, D = kv.shape
+    B, H_kv, NB, two, bs, D = kv.shape
+    if two != 2:
+        raise ValueError(f"kv: dimension 3 must be 2 (K, V), got {two}")
+    _need(ctx_len, "ctx_len", torch.int32, 1, shape=(B,))
     if kminmax is None:
         kminmax = torch.empty((B, H_kv, NB, 2, D), dtype=torch.bfloat16, device=ctx_len.device)
-    _need(kminmax, "kminmax", torch.bfloat16, 5)
+    _need(kminmax, "kminmax", torch.bfloat16, 5, shape=(B, H_kv, NB, 2, D))
     d = dims(B, H_kv, H_kv, NB, D, bs)
     _check(_lib.oasis_build_summaries(ctypes.byref(d), _ptr(kv), _ptr(ctx_len), _ptr(kminmax),
                                       _stream(stream)))
@@ -235,10 +275,13 @@ def oasis_score_blocks(q_look: torch.Tensor, kminmax: torch.Tensor, ctx_len: tor
     _need(kminmax, "kminmax", torch.bfloat16, 5)
     _need(ctx_len, "ctx_len", torch.int32, 1)
     B, J, H_q, D = q_look.shape
-    _, H_kv, NB, _, _ = kminmax.shape
+    H_kv, NB = kminmax.shape[1], kminmax.shape[2]
+    _group(H_q, H_kv)
+    _need(kminmax, "kminmax", torch.bfloat16, 5, shape=(B, H_kv, NB, 2, D))
+    _need(ctx_len, "ctx_len", torch.int32, 1, shape=(B,))
     if scores is None:
         scores = torch.empty((B, H_kv, NB), dtype=torch.float32, device=q_look.device)
-    _need(scores, "scores", torch.float32, 3)
+    _need(scores, "scores", torch.float32, 3, shape=(B, H_kv, NB))
     d = dims(B, H_q, H_kv, NB, D, bs)
     _check(_lib.oasis_score_blocks(ctypes.byref(d), _ptr(q_look), J, _ptr(kminmax), _ptr(ctx_len),
                                    _ptr(scores), _stream(stream)))
@@ -251,12 +294,13 @@ def oasis_select_topk(scores: torch.Tensor, ctx_len: torch.Tensor, K_b: int, sel
     _need(scores, "scores", torch.float32, 3)
     _need(ctx_len, "ctx_len", torch.int32, 1)
     B, H_kv, NB = scores.shape
+    _need(ctx_len, "ctx_len", torch.int32, 1, shape=(B,))
     if sel is None:
         sel = torch.empty((B, H_kv, K_b), dtype=torch.int32, device=scores.device)
     if n_sel is None:
         n_sel = torch.empty((B, H_kv), dtype=torch.int32, device=scores.device)
-    _need(sel, "sel", torch.int32, 3)
-    _need(n_sel, "n_sel", torch.int32, 2)
+    _need(sel, "sel", torch.int32, 3, shape=(B, H_kv, K_b))
+    _need(n_sel, "n_sel", torch.int32, 2, shape=(B, H_kv))
     d = dims(B, H_kv, H_kv, NB, 128, bs)
     _check(_lib.oasis_select_topk(ctypes.byref(d), _ptr(scores), _ptr(ctx_len), int(K_b), _ptr(sel),
                                   _ptr(n_sel), _stream(stream)))
@@ -283,11 +327,11 @@ def oasis_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, ctx_len: torch.Ten
         raise ValueError("kminmax / ctx_len shape mismatch")
     S = 0
     if ws_pool is not None:
-        _need(ws_pool, "ws_pool", torch.bfloat16, 6)
-        _need(slot_block, "slot_block", torch.int32, 3)
-        S = ws_pool.shape[2]
-        if tuple(ws_pool.shape[:2]) != (B, H_kv) or tuple(slot_block.shape) != (B, H_kv, S):
-            raise ValueError("ws_pool / slot_block shape mismatch")
+        if slot_block is None:
+            raise ValueError("a working set needs its slot_block table")
+        S = ws_pool.shape[2] if ws_pool.dim() == 6 else 0
+        _need(ws_pool, "ws_pool", torch.bfloat16, 6, shape=(B, H_kv, S, 2, bs, D))
+        _need(slot_block, "slot_block", torch.int32, 3, shape=(B, H_kv, S))
     d = dims(B, H_kv, H_kv, NB, D, bs)
     _check(_lib.oasis_append_kv(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(ctx_len), _ptr(kminmax),
                                 _ptr(pool), _ptr(ws_pool), _ptr(slot_block), int(S), _stream(stream)))
@@ -307,16 +351,20 @@ def oasis_block_attention_mass(q: torch.Tensor, kv_pool: torch.Tensor, ctx_len: 
     _need(kv_pool, "kv_pool", torch.bfloat16, 6, device=None)
     _need(ctx_len, "ctx_len", torch.int32, 1)
     B, H_q, D = q.shape
-    _, H_kv, NB, _, bs, _ = kv_pool.shape
+    H_kv, NB, bs = kv_pool.shape[1], kv_pool.shape[2], kv_pool.shape[4]
+    _group(H_q, H_kv)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 6, device=None, shape=(B, H_kv, NB, 2, bs, D))
+    _need(ctx_len, "ctx_len", torch.int32, 1, shape=(B,))
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if mass is None:
         mass = torch.empty((B, H_kv, NB), dtype=torch.float32, device=q.device)
-    _need(mass, "mass", torch.float32, 3)
+    _need(mass, "mass", torch.float32, 3, shape=(B, H_kv, NB))
     d = dims(B, H_q, H_kv, NB, D, bs)
     need = int(_lib.oasis_block_mass_workspace_bytes(ctypes.byref(d)))
     if ws is None or ws.numel() * ws.element_size() < need:
         ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _need_bytes(ws, "ws")
     _check(_lib.oasis_block_attention_mass(ctypes.byref(d), _ptr(q), _ptr(kv_pool), _ptr(ctx_len), float(sm_scale),
                                            _ptr(mass), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return mass
@@ -330,10 +378,12 @@ def oasis_topk_overlap(sel_a: torch.Tensor, n_a: torch.Tensor, sel_b: torch.Tens
     for t, n in ((n_a, "n_a"), (n_b, "n_b")):
         _need(t, n, torch.int32, 2)
     B, H_kv, K = sel_a.shape
-    if tuple(sel_b.shape) != (B, H_kv, K):
-        raise ValueError("sel_a and sel_b must have the same shape")
+    _need(sel_b, "sel_b", torch.int32, 3, shape=(B, H_kv, K))
+    _need(n_a, "n_a", torch.int32, 2, shape=(B, H_kv))
+    _need(n_b, "n_b", torch.int32, 2, shape=(B, H_kv))
     if out is None:
         out = torch.empty((B, H_kv), dtype=torch.int32, device=sel_a.device)
+    _need(out, "out", torch.int32, 2, shape=(B, H_kv))
     d = dims(B, H_kv, H_kv, 1)
     _check(_lib.oasis_topk_overlap(ctypes.byref(d), _ptr(sel_a), _ptr(n_a), _ptr(sel_b), _ptr(n_b), int(K),
                                    _ptr(out), _stream(stream)))
@@ -352,7 +402,7 @@ def oasis_stage_buffer_bytes(n_blocks: int, D: int = 128, bs: int = 16) -> int:
 
 def _stage_args(sel, n_sel, scores, ctx_len, K_b, C, step, slot_block, slot_stamp, host_pool, ws_pool,
                 tbl_slot, tbl_block, tbl_n, plan, host_plan, stage_host, stage_dev, host_threads, copy_mode,
-                stream, copy_stream, wait_event, done_event, plan_event):
+                stream, copy_stream, wait_event, done_event, plan_event, stats_accum=None):
     _need(sel, "sel", torch.int32, 3)
     _need(n_sel, "n_sel", torch.int32, 2)
     _need(scores, "scores", torch.float32, 3)
@@ -364,17 +414,33 @@ def _stage_args(sel, n_sel, scores, ctx_len, K_b, C, step, slot_block, slot_stam
     _need(tbl_slot, "tbl_slot", torch.int32, 3)
     _need(tbl_block, "tbl_block", torch.int32, 3)
     _need(tbl_n, "tbl_n", torch.int32, 2)
-    B, H_kv, NB, _, bs, D = host_pool.shape
+    B, H_kv, NB, two, bs, D = host_pool.shape
+    if two != 2:
+        raise ValueError(f"host_pool: dimension 3 must be 2 (K, V), got {two}")
     S = ws_pool.shape[2]
-    if tuple(slot_block.shape) != (B, H_kv, S) or tuple(slot_stamp.shape) != (B, H_kv, S):
-        raise ValueError("slot tables must be [B][H_kv][S]")
-    if tuple(tbl_slot.shape) != (B, H_kv, K_b) or tuple(tbl_block.shape) != (B, H_kv, K_b):
-        raise ValueError("attention tables must be [B][H_kv][K_b]")
-    if tuple(scores.shape) != (B, H_kv, NB) or sel.shape[:2] != (B, H_kv):
-        raise ValueError("scores / sel shape mismatch")
+    K_sel = sel.shape[2]
+    _need(ws_pool, "ws_pool", torch.bfloat16, 6, shape=(B, H_kv, S, 2, bs, D))
+    _need(slot_block, "slot_block", torch.int32, 3, shape=(B, H_kv, S))
+    _need(slot_stamp, "slot_stamp", torch.int32, 3, shape=(B, H_kv, S))
+    _need(tbl_slot, "tbl_slot", torch.int32, 3, shape=(B, H_kv, K_b))
+    _need(tbl_block, "tbl_block", torch.int32, 3, shape=(B, H_kv, K_b))
+    _need(tbl_n, "tbl_n", torch.int32, 2, shape=(B, H_kv))
+    _need(scores, "scores", torch.float32, 3, shape=(B, H_kv, NB))
+    _need(sel, "sel", torch.int32, 3, shape=(B, H_kv, K_sel))
+    _need(n_sel, "n_sel", torch.int32, 2, shape=(B, H_kv))
+    _need(ctx_len, "ctx_len", torch.int32, 1, shape=(B,))
+    _need_bytes(plan, "plan")
+    if host_plan is not None:
+        _need_bytes(host_plan, "host_plan", device="host")
+    if stage_host is not None:
+        _need_bytes(stage_host, "stage_host", device="host")
+    if stage_dev is not None:
+        _need_bytes(stage_dev, "stage_dev")
+    if stats_accum is not None:
+        _need(stats_accum, "stats_accum", torch.int64, 1, shape=(4,))
     d = dims(B, H_kv, H_kv, NB, D, bs)
     a = oasis_stage_args()
-    a.sel, a.n_sel, a.K_sel, a.scores = sel.data_ptr(), n_sel.data_ptr(), sel.shape[2], scores.data_ptr()
+    a.sel, a.n_sel, a.K_sel, a.scores = sel.data_ptr(), n_sel.data_ptr(), K_sel, scores.data_ptr()
     a.K_b, a.C, a.S, a.step = int(K_b), int(C), int(S), int(step)
     a.slot_block, a.slot_stamp, a.ctx_len = slot_block.data_ptr(), slot_stamp.data_ptr(), ctx_len.data_ptr()
     a.host_pool, a.ws_pool = host_pool.data_ptr(), ws_pool.data_ptr()
@@ -391,6 +457,7 @@ def _stage_args(sel, n_sel, scores, ctx_len, K_b, C, step, slot_block, slot_stam
     a.wait_event = _event(wait_event)
     a.done_event = _event(done_event)
     a.plan_event = _event(plan_event)
+    a.stats_accum = None if stats_accum is None else stats_accum.data_ptr()
     return d, a
 
 
@@ -398,17 +465,32 @@ def oasis_stage_blocks(*, sel, n_sel, scores, ctx_len, K_b: int, C: int, step: i
                        slot_stamp, host_pool, ws_pool, tbl_slot, tbl_block, tbl_n, plan,
                        host_plan=None, stage_host=None, stage_dev=None, host_threads: int = 0,
                        copy_mode: int = OASIS_COPY_KERNEL, stream=None, copy_stream=None, wait_event=None,
-                       done_event=None, plan_event=None):
+                       done_event=None, plan_event=None, stats_accum=None, want_stats: bool = False):
     """One staging step (include/oasis.h).  host_pool: pinned bf16
     [B][H_kv][NB_max][2][bs][D]; ws_pool: device bf16 [B][H_kv][S][2][bs][D];
     slot tables int32 [B][H_kv][S]; tables int32 [B][H_kv][K_b]; plan: device
     int32 of oasis_stage_plan_bytes() bytes.  The DMA engine also needs
     host_plan (pinned, as large as plan) and the staging buffers stage_host
-    (pinned) and stage_dev (device)."""
+    (pinned) and stage_dev (device).  stats_accum: optional device int64[4]
+    that the step's admits, evictions, deferred admits and 1 are added to.
+    With want_stats the call waits for the plan and returns the step's
+    counts (oasis_stage_stats as a dict); otherwise it returns None."""
     d, a = _stage_args(sel, n_sel, scores, ctx_len, K_b, C, step, slot_block, slot_stamp, host_pool, ws_pool,
                        tbl_slot, tbl_block, tbl_n, plan, host_plan, stage_host, stage_dev, host_threads,
-                       copy_mode, stream, copy_stream, wait_event, done_event, plan_event)
-    _check(_lib.oasis_stage_blocks(ctypes.byref(d), ctypes.byref(a)))
+                       copy_mode, stream, copy_stream, wait_event, done_event, plan_event, stats_accum)
+    st = oasis_stage_stats() if want_stats else None
+    _check(_lib.oasis_stage_blocks(ctypes.byref(d), ctypes.byref(a), None if st is None else ctypes.byref(st)))
+    return None if st is None else st.as_dict()
+
+
+def oasis_stage_read_stats(plan: torch.Tensor, B: int, H_kv: int, C: int, stream=None) -> dict:
+    """The counts of the staging step whose plan is in `plan` (fetch cap C):
+    waits for `stream`, then reads the plan's totals."""
+    _need_bytes(plan, "plan")
+    d = dims(B, H_kv, H_kv, 1)
+    st = oasis_stage_stats()
+    _check(_lib.oasis_stage_read_stats(ctypes.byref(d), int(C), _ptr(plan), ctypes.byref(st), _stream(stream)))
+    return st.as_dict()
 
 
 def oasis_stage_plan(**kw):
@@ -425,7 +507,8 @@ def oasis_stage_copy(**kw):
 
 def _stage_kw(kw):
     full = dict(host_plan=None, stage_host=None, stage_dev=None, host_threads=0, copy_mode=OASIS_COPY_KERNEL,
-                stream=None, copy_stream=None, wait_event=None, done_event=None, plan_event=None)
+                stream=None, copy_stream=None, wait_event=None, done_event=None, plan_event=None,
+                stats_accum=None)
     full.update(kw)
     return full
 
@@ -453,18 +536,29 @@ def oasis_sparse_decode_attn(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: t
     _need(tbl_n, "tbl_n", torch.int32, 2)
     _need(ctx_len, "ctx_len", torch.int32, 1)
     B, H_q, D = q.shape
-    _, H_kv, P, _, bs, _ = kv_pool.shape
+    H_kv, P, bs = kv_pool.shape[1], kv_pool.shape[2], kv_pool.shape[4]
+    _group(H_q, H_kv)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 6, shape=(B, H_kv, P, 2, bs, D))
     T = tbl_slot.shape[2]
+    _need(tbl_slot, "tbl_slot", torch.int32, 3, shape=(B, H_kv, T))
+    _need(tbl_block, "tbl_block", torch.int32, 3, shape=(B, H_kv, T))
+    _need(tbl_n, "tbl_n", torch.int32, 2, shape=(B, H_kv))
+    _need(ctx_len, "ctx_len", torch.int32, 1, shape=(B,))
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3, shape=(B, H_q, D))
     if lse is None and want_lse:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, shape=(B, H_q))
     d = dims(B, H_q, H_kv, max(P, 1), D, bs)
     need = int(_lib.oasis_attn_workspace_bytes(ctypes.byref(d), T, int(n_split)))
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    if ws is not None:
+        _need_bytes(ws, "ws")
     _check(_lib.oasis_sparse_decode_attn(
         ctypes.byref(d), _ptr(q), _ptr(kv_pool), int(P), _ptr(tbl_slot), _ptr(tbl_block), _ptr(tbl_n),
         int(T), _ptr(ctx_len), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
@@ -490,18 +584,29 @@ def oasis_lookahead_attn(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: torch
     _need(tbl_n, "tbl_n", torch.int32, 2)
     _need(ctx_len, "ctx_len", torch.int32, 1)
     B, n_q, H_q, D = q.shape
-    _, H_kv, P, _, bs, _ = kv_pool.shape
+    H_kv, P, bs = kv_pool.shape[1], kv_pool.shape[2], kv_pool.shape[4]
+    _group(H_q, H_kv)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 6, shape=(B, H_kv, P, 2, bs, D))
     T = tbl_slot.shape[2]
+    _need(tbl_slot, "tbl_slot", torch.int32, 3, shape=(B, H_kv, T))
+    _need(tbl_block, "tbl_block", torch.int32, 3, shape=(B, H_kv, T))
+    _need(tbl_n, "tbl_n", torch.int32, 2, shape=(B, H_kv))
+    _need(ctx_len, "ctx_len", torch.int32, 1, shape=(B,))
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, n_q, H_q, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 4, shape=(B, n_q, H_q, D))
     if lse is None and want_lse:
         lse = torch.empty((B, n_q, H_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3, shape=(B, n_q, H_q))
     d = dims(B, H_q, H_kv, max(P, 1), D, bs)
     need = int(_lib.oasis_lookahead_attn_workspace_bytes(ctypes.byref(d), int(n_q), T, int(n_split)))
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    if ws is not None:
+        _need_bytes(ws, "ws")
     _check(_lib.oasis_lookahead_attn(
         ctypes.byref(d), int(n_q), _ptr(q), _ptr(kv_pool), int(P), _ptr(tbl_slot), _ptr(tbl_block), _ptr(tbl_n),
         int(T), _ptr(ctx_len), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),

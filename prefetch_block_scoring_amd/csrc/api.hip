@@ -158,8 +158,8 @@ int oasis_score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J
     if (rc) return rc;
     if (J < 1) FAIL(OASIS_EINVAL, "J = %d < 1", J);
     if (J > 64) FAIL(OASIS_EUNSUPPORTED, "J = %d (at most 64)", J);
-    if ((int64_t)dims->B * dims->H_kv * ((dims->NB_max + 127) / 128) > INT32_MAX)
-        FAIL(OASIS_EUNSUPPORTED, "B * H_kv * ceil(NB_max / 128) exceeds 2^31 - 1");
+    if ((int64_t)dims->B * dims->H_kv * ((dims->NB_max + 63) / 64) > INT32_MAX)
+        FAIL(OASIS_EUNSUPPORTED, "B * H_kv * ceil(NB_max / 64) exceeds 2^31 - 1");
     if (dims->B == 0) return OASIS_OK;
     NEED(q_look);
     NEED(kminmax);
@@ -325,10 +325,13 @@ static int stage_plan_phase(const oasis_dims *dims, const oasis_stage_args *a) {
     return OASIS_OK;
 }
 
-static int stage_copy_phase(const oasis_dims *dims, const oasis_stage_args *a) {
+// Pointer checks of the copy phase that need the runtime: the pool must be
+// device memory or pinned host memory with a device mapping (pageable host
+// memory is refused), the DMA engine's host buffers pinned.  Done before
+// anything is enqueued.
+static int resolve_copy_args(const oasis_stage_args *a, const void **pool_dev) {
     int rc;
-    const void *pool_dev = nullptr;
-    if ((rc = device_view(a->host_pool, &pool_dev, "host_pool"))) return rc;
+    if ((rc = device_view(a->host_pool, pool_dev, "host_pool"))) return rc;
     if (a->copy_mode == OASIS_COPY_DMA) {
         for (const void *hb : {a->host_plan, a->stage_host}) {
             hipPointerAttribute_t at;
@@ -338,6 +341,11 @@ static int stage_copy_phase(const oasis_dims *dims, const oasis_stage_args *a) {
             }
         }
     }
+    return OASIS_OK;
+}
+
+static int stage_copy_phase(const oasis_dims *dims, const oasis_stage_args *a, const void *pool_dev) {
+    int rc;
     hipStream_t s = static_cast<hipStream_t>(a->stream);
     hipStream_t cs = a->copy_stream ? static_cast<hipStream_t>(a->copy_stream) : s;
     // the plan this copy uses: `plan_event` if given, else everything on `stream` so far
@@ -368,17 +376,52 @@ int oasis_stage_copy(const oasis_dims *dims, const oasis_stage_args *a) {
     clear_error();
     int rc = check_copy_args(dims, a);
     if (rc || dims->B == 0) return rc;
-    return stage_copy_phase(dims, a);
+    const void *pool_dev = nullptr;
+    if ((rc = resolve_copy_args(a, &pool_dev))) return rc;
+    return stage_copy_phase(dims, a, pool_dev);
 }
 
-int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *a) {
+// Reads the step totals at the end of a plan (the stream's work is done).
+static int read_plan_totals(const oasis_dims *dims, int C, const int32_t *plan, hipStream_t s,
+                            oasis_stage_stats *out) {
+    int32_t tail[kPlanTail] = {0, 0, 0, 0};
+    const size_t off = (size_t)dims->B * dims->H_kv * plan_row(C);
+    OASIS_HIP(hipMemcpyAsync(tail, plan + off, sizeof(tail), hipMemcpyDeviceToHost, s));
+    OASIS_HIP(hipStreamSynchronize(s));
+    out->admits = tail[0];
+    out->evictions = tail[1];
+    out->deferred = tail[2];
+    out->capped_pairs = tail[3];
+    out->bytes = (int64_t)tail[0] * 2 * dims->bs * dims->D * (int64_t)sizeof(uint16_t);
+    return OASIS_OK;
+}
+
+int oasis_stage_read_stats(const oasis_dims *dims, int32_t C, const int32_t *plan, oasis_stage_stats *stats,
+                           void *stream) {
+    clear_error();
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (C < 0) FAIL(OASIS_EINVAL, "C = %d < 0", C);
+    NEED(stats);
+    *stats = oasis_stage_stats{0, 0, 0, 0, 0};
+    if (dims->B == 0) return OASIS_OK;
+    NEED(plan);
+    return read_plan_totals(dims, C, plan, static_cast<hipStream_t>(stream), stats);
+}
+
+int oasis_stage_blocks(const oasis_dims *dims, const oasis_stage_args *a, oasis_stage_stats *stats) {
     clear_error();
     int rc = check_plan_args(dims, a);
     if (rc) return rc;
     if ((rc = check_copy_args(dims, a))) return rc;
+    if (stats) *stats = oasis_stage_stats{0, 0, 0, 0, 0};
     if (dims->B == 0) return OASIS_OK;
+    const void *pool_dev = nullptr;
+    if ((rc = resolve_copy_args(a, &pool_dev))) return rc;  // before the plan changes any state
     if ((rc = stage_plan_phase(dims, a))) return rc;
-    return stage_copy_phase(dims, a);
+    if ((rc = stage_copy_phase(dims, a, pool_dev))) return rc;
+    if (stats) return read_plan_totals(dims, a->C, a->plan, static_cast<hipStream_t>(a->stream), stats);
+    return OASIS_OK;
 }
 
 size_t oasis_attn_workspace_bytes(const oasis_dims *dims, int32_t T, int32_t n_split) {

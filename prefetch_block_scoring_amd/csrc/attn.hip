@@ -236,6 +236,13 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+        // rows past the context get p = 0, but 0 * V is NaN when the pool's
+        // padding holds NaN or Inf: their V words are zeroed instead
+        if (valid < kBs) {
+#pragma unroll
+            for (int qq = 0; qq < 4; qq++)
+                if (qq * 4 + grp >= valid) vc[qq] = make_uint4(0, 0, 0, 0);
+        }
         if (moved) {
 #pragma unroll
             for (int g = 0; g < GP; g++) {
@@ -426,10 +433,15 @@ __global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
         if (src_n) load(src_n, kn, vn);
 
         // V^T into this wave's LDS tile: lane (col, grp) holds token
-        // qq * 4 + grp, dims col * 8 + [0, 8) of vc[qq]
+        // qq * 4 + grp, dims col * 8 + [0, 8) of vc[qq]; rows past the
+        // context go in as zeros (their p is 0, but 0 * NaN or 0 * Inf
+        // padding would not be)
+        const int valid = ctx - blk_c * kBs;
 #pragma unroll
         for (int qq = 0; qq < 4; qq++) {
-            const uint32_t w[4] = {vc[qq].x, vc[qq].y, vc[qq].z, vc[qq].w};
+            const bool keep = qq * 4 + grp < valid;
+            const uint32_t w[4] = {keep ? vc[qq].x : 0u, keep ? vc[qq].y : 0u, keep ? vc[qq].z : 0u,
+                                   keep ? vc[qq].w : 0u};
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 vt[col * 8 + 2 * e][qq * 4 + grp] = (uint16_t)(w[e] & 0xffffu);
@@ -444,7 +456,6 @@ __global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[kk]),
                                                          __builtin_bit_cast(bf16x8, q_lds[col][kk * 4 + grp]), c,
                                                          0, 0, 0);
-        const int valid = ctx - blk_c * kBs;
         float sv[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) sv[t] = (4 * grp + t < valid) ? c[t] * a.scale_log2 : -INFINITY;

@@ -94,9 +94,11 @@ hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q,
 
 // Plan workspace: per (r, h) a row of int32
 //   [0] admits, [1] evictions, [2] packed position of the first admit (the
-//   exclusive prefix of admits over (r, h)), [3] reserved, then one
-//   (slot, block) pair per admit;
-// after the rows, kPlanTail int32: [0] total admits.
+//   exclusive prefix of admits over (r, h)), [3] deferred admits (predicted
+//   blocks neither resident nor admitted), then one (slot, block) pair per
+//   admit;
+// after the rows, kPlanTail int32: [0] total admits, [1] total evictions,
+// [2] total deferred admits, [3] pairs with deferred admits.
 constexpr int kPlanHead = 4;
 constexpr int kPlanTail = 4;
 __host__ __device__ inline int plan_row(int C) { return kPlanHead + 2 * (C > 0 ? C : 1); }

@@ -1,10 +1,10 @@
 // Native scheduler of the per-layer decode chain (oasis_pipeline_*).
 //
-// OasisKV (arXiv 2608.08097), paperlayer summary, section 4: per layer, a
-// background chain of top-K prediction, KV selection and KV transfer runs on
-// independent workers overlapped across layers and decode steps; the
-// foreground waits only for the relevant layer's transfer before that
-// layer's next-step attention.  One call here enqueues one layer-step of that
+// OasisKV (arXiv 2608.08097), paperlayer summary, section 4.  Scoring, top-K,
+// the staging plan and the block copies of a layer are kept off the attention
+// stream, on streams of their own, so that the work of several layers and
+// steps overlaps; an attention launch waits only on the copies into its own
+// layer's working set.  One call here enqueues one layer-step of that
 // schedule through the library's own entry points, so a decode step costs a
 // few microseconds of host time per layer instead of a round of interpreter
 // calls per launch.  The dependency rules are stated in include/oasis.h.
@@ -406,6 +406,7 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     a.wait_event = t >= 1 ? p->event(kEvAttn, l, t - 1) : nullptr;
     a.done_event = p->event(kEvStage, l, t);
     a.plan_event = p->event(kEvPlan, l, t);
+    a.stats_accum = ds.stage_stats;
     timed_begin(p, 3, cs);
     if ((rc = oasis_stage_plan(d, &a))) return rc;
     timed_end(p, 3, cs);

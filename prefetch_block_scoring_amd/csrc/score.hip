@@ -16,27 +16,55 @@
 // range), the 2 * D products and their sum in fp64, rounded once to fp32.
 //
 // Mapping: the grid is persistent (compute units x resident workgroups).  The
-// work items are the (request, KV head, 128-block chunk) triples whose chunk
+// work items are the (request, KV head, 64-block chunk) triples whose chunk
 // holds at least one of the request's blocks; they are split into equal
 // contiguous ranges, one per workgroup, so that ragged contexts balance and
 // Qp / Qm are rebuilt only when a range crosses into the next (request, KV
 // head).  Each workgroup counts the items itself from the context lengths.
 // The chunks past a request's last block only get -inf, in a second, strided
-// loop.  Eight lanes share a block (512 bytes of
-// summary); lane i of the eight holds dims [8i, 8i + 8) and [64 + 8i, 72 + 8i)
-// of kmin and kmax, so each 16-byte load fills whole 128-byte lines per eight
-// lanes.  Four 32-block groups are loaded before any is used (16 KiB in flight
-// per wave).  The eight partial sums meet through three DPP steps.
+// loop.
+//
+// Sixteen lanes share a block (512 bytes of summary): lane i of the sixteen
+// holds dims [8i, 8i + 8) of kmin and of kmax (two 16-byte loads), so a wave's
+// load instruction reads four consecutive blocks' halves, 1 KiB in whole
+// 128-byte lines, and a lane keeps only 16 of the 256 Qp / Qm values (32
+// registers).  The sixteen partial sums meet through four DPP steps.  A wave
+// owns 16 consecutive blocks of each 64-block chunk and writes their 16
+// scores with one 64-byte store.
+//
+// Software pipeline: the registers hold two items' load groups (eight groups,
+// 16 KiB per wave).  As each group of the current item is used, the same
+// registers are refilled with that group of the item two ahead, so a wave
+// keeps about 14 KiB of loads in flight while its fp64 arithmetic runs.  When
+// a range crosses into another (request, KV head), the Qp / Qm rebuild waits
+// for its query loads, and with them for the loads already in flight (the
+// load counter is in order): one drain per crossing.
 #include "oasis_internal.h"
 
 namespace oasis {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLanesPerBlock = 8;                       // lanes sharing one block
-constexpr int kBlocksPerGroup = kThreads / kLanesPerBlock;  // 32
-constexpr int kUnroll = 4;
-constexpr int kItemBlocks = kBlocksPerGroup * kUnroll;  // 128 blocks per item
+constexpr int kLanesPerBlock = 16;                          // lanes sharing one block
+constexpr int kBlocksPerGroup = kThreads / kLanesPerBlock;  // 16: blocks per load instruction of the workgroup
+constexpr int kGroups = 4;                                  // load groups per item
+constexpr int kItemBlocks = kBlocksPerGroup * kGroups;      // 64 blocks per item
+constexpr int kBuf = 2 * kGroups;                           // uint4 per lane per item
+constexpr int kMaxItems = 32;                               // items per workgroup, their scores kept in LDS
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer resource for dword loads (no swizzle, no format
+// conversion): the value gfx9-family raw buffers use.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kSummaryBytes = 2 * kD * 2;  // one block's kmin and kmax, bf16
+
+// 16 bytes at byte offset `off` of a raw buffer; zeros when off is at or past
+// the buffer's size.  The whole offset goes in the vector operand, which the
+// range check always covers.
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 __device__ __forceinline__ double bf16_d(uint32_t bits16) {
     return (double)__uint_as_float(bits16 << 16);
@@ -50,11 +78,12 @@ __device__ __forceinline__ double dpp_d(double x) {
     return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
-// Sum over the eight lanes of an aligned octet; every lane gets the total.
-__device__ __forceinline__ double octet_sum(double x) {
+// Sum over the sixteen lanes of a DPP row; every lane gets the total.
+__device__ __forceinline__ double row_sum(double x) {
     x += dpp_d<0xB1>(x);   // quad_perm [1,0,3,2]
     x += dpp_d<0x4E>(x);   // quad_perm [2,3,0,1]
     x += dpp_d<0x141>(x);  // row_half_mirror: lane i <- lane 7 - i within 8
+    x += dpp_d<0x140>(x);  // row_mirror: lane i <- lane 15 - i within 16
     return x;
 }
 
@@ -63,11 +92,21 @@ __device__ __forceinline__ int valid_chunks(const int32_t *ctx_len, int r, int N
     return (n_blocks_of(ctx_len[r], NB_max) + kItemBlocks - 1) / kItemBlocks;
 }
 
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __global__ __launch_bounds__(kThreads, 3) void score_kernel(
     const uint16_t *__restrict__ q_look, int J, int H_q, int H_kv,
     const uint4 *__restrict__ kminmax, const int32_t *__restrict__ ctx_len,
     float *__restrict__ scores, int NB_max, int B) {
-    __shared__ double Qsh[2][kD];  // [0] = Qm (pairs with kmin), [1] = Qp (pairs with kmax)
+    // per half of the workgroup: [half][0] = its part of Qm (pairs with kmin),
+    // [half][1] of Qp (pairs with kmax); each lane adds the two halves
+    __shared__ double Qpart[2][2][kD];
+    // the scores of the workgroup's items (at most kMaxItems, which the grid
+    // size guarantees), written out together at the end, with each item's
+    // place in the score array and how many of its 64 blocks lie below NB_max
+    __shared__ float sbuf[kMaxItems * kItemBlocks];
+    __shared__ int sdst[kMaxItems];
+    __shared__ int scnt[kMaxItems];
     const int G = H_q / H_kv;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -81,7 +120,8 @@ __global__ __launch_bounds__(kThreads, 3) void score_kernel(
     // items before each request, by a scan over the context lengths that
     // every wave does alike (uniform results, no synchronisation); up to 64
     // requests need one load per lane
-    int c_lane = lane < B ? H_kv * valid_chunks(ctx_len, lane, NB_max) : 0;
+    const int ctx_lane = lane < B ? ctx_len[lane] : 0;  // requests 0 .. 63
+    int c_lane = lane < B ? H_kv * ((n_blocks_of(ctx_lane, NB_max) + kItemBlocks - 1) / kItemBlocks) : 0;
     int total = 0;
     for (int r0 = 0; r0 < B; r0 += 64) {
         int c = r0 == 0 ? c_lane : (r0 + lane < B ? H_kv * valid_chunks(ctx_len, r0 + lane, NB_max) : 0);
@@ -93,10 +133,11 @@ __global__ __launch_bounds__(kThreads, 3) void score_kernel(
     const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
     const int v0 = min(total, (int)blockIdx.x * per), v1 = min(total, v0 + per);
     // the request holding item v0, and the item's place in it
-    int r = 0, before = 0;
+    int r = 0, before = 0, ctx_r = 0;
     if (v0 < v1) {
         for (int r0 = 0; r0 < B; r0 += 64) {
-            const int c = r0 == 0 ? c_lane : (r0 + lane < B ? H_kv * valid_chunks(ctx_len, r0 + lane, NB_max) : 0);
+            const int ctx_l = r0 == 0 ? ctx_lane : (r0 + lane < B ? ctx_len[r0 + lane] : 0);
+            const int c = H_kv * ((n_blocks_of(ctx_l, NB_max) + kItemBlocks - 1) / kItemBlocks);
             int inc = c;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -110,96 +151,159 @@ __global__ __launch_bounds__(kThreads, 3) void score_kernel(
                 const int first = __ffsll((long long)m) - 1;
                 r = __builtin_amdgcn_readfirstlane(r0 + first);
                 before = __builtin_amdgcn_readfirstlane(before + __shfl(inc - c, first, 64));
+                ctx_r = __builtin_amdgcn_readfirstlane(__shfl(ctx_l, first, 64));
                 break;
             }
             before = __builtin_amdgcn_readfirstlane(before + chunk_total);
         }
     }
-    int cr = v0 < v1 ? __builtin_amdgcn_readfirstlane(valid_chunks(ctx_len, r, NB_max)) : 0;  // chunks of r
-    const int rem = v0 - before;                               // item index within request r
-    int h = cr > 0 ? rem / cr : 0;
-    int chunk = cr > 0 ? rem - h * cr : 0;
 
-    int cur = -1, nb = 0;
-    double qm[16], qp[16];
-    for (int v = v0; v < v1; v++) {
-        const int rh = r * H_kv + h;
-        if (rh != cur) {  // uniform across the workgroup
-            cur = rh;
-            __syncthreads();
-            if (tid < kD) {
-                double sp = 0.0, sm = 0.0;
-                for (int j = 0; j < J; j++) {
-                    const uint16_t *qrow = q_look + (((size_t)r * J + j) * H_q + (size_t)h * G) * kD + tid;
-                    for (int gi = 0; gi < G; gi++) {
-                        const double v = bf16_d(qrow[(size_t)gi * kD]);
-                        if (v > 0.0) sp += v; else sm += v;
-                    }
+    double qm[8], qp[8];
+
+    // Qp / Qm of (request r, KV head h) into the registers
+    auto rebuild = [&](int rr, int hh) {
+        __syncthreads();  // every wave has read the previous Qp / Qm
+        {
+            // dim tid % 128 over the J * G query rows of the group; the two
+            // halves of the workgroup take alternate rows, four independent
+            // loads at a time (rows past the last re-read it, then count as 0)
+            const int dim = tid & (kD - 1), half = tid >> 7;
+            const int nk = J * G;
+            double sp = 0.0, sm = 0.0;
+            for (int k0 = half; k0 < nk; k0 += 8) {
+                uint32_t raw[4];
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const int k = min(k0 + 2 * t, nk - 1), j = k / G, gi = k - j * G;
+                    raw[t] = q_look[(((size_t)rr * J + j) * H_q + (size_t)hh * G + gi) * kD + dim];
                 }
-                Qsh[0][tid] = sm;
-                Qsh[1][tid] = sp;
-            }
-            __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                qm[e] = Qsh[0][li * 8 + e];
-                qm[8 + e] = Qsh[0][64 + li * 8 + e];
-                qp[e] = Qsh[1][li * 8 + e];
-                qp[8 + e] = Qsh[1][64 + li * 8 + e];
+                for (int t = 0; t < 4; t++) {
+                    const double v = k0 + 2 * t < nk ? bf16_d(raw[t]) : 0.0;
+                    if (v > 0.0) sp += v; else sm += v;
+                }
             }
-            nb = n_blocks_of(ctx_len[r], NB_max);
+            Qpart[half][0][dim] = sm;
+            Qpart[half][1][dim] = sp;
         }
-        float *out = scores + (size_t)rh * NB_max;
-        const uint4 *base = kminmax + (size_t)rh * NB_max * 32;  // 32 uint4 per block summary
-        const int b0 = chunk * kItemBlocks + tid / kLanesPerBlock;
-        uint4 mn0[kUnroll], mn1[kUnroll], mx0[kUnroll], mx1[kUnroll];
+        __syncthreads();
 #pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int b = b0 + u * kBlocksPerGroup;
-            if (b < nb) {
-                const uint4 *sb = base + (size_t)b * 32;
-                mn0[u] = sb[li];
-                mn1[u] = sb[8 + li];
-                mx0[u] = sb[16 + li];
-                mx1[u] = sb[24 + li];
-            }
+        for (int e = 0; e < 8; e++) {
+            const int d = li * 8 + e;
+            qm[e] = Qpart[0][0][d] + Qpart[1][0][d];
+            qp[e] = Qpart[0][1][d] + Qpart[1][1][d];
         }
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int b = b0 + u * kBlocksPerGroup;
-            if (b >= NB_max) continue;            // the octet skips together
-            if (b >= nb) {
-                if (li == 0) out[b] = -INFINITY;
-                continue;
-            }
-            const uint32_t wmn[8] = {mn0[u].x, mn0[u].y, mn0[u].z, mn0[u].w,
-                                     mn1[u].x, mn1[u].y, mn1[u].z, mn1[u].w};
-            const uint32_t wmx[8] = {mx0[u].x, mx0[u].y, mx0[u].z, mx0[u].w,
-                                     mx1[u].x, mx1[u].y, mx1[u].z, mx1[u].w};
+    };
+
+    // Loads go through a raw buffer resource over the valid blocks of one
+    // (request, KV head) row (base and size in scalar registers): a lane adds
+    // its fixed offset in the group to the chunk's group offset, and a block
+    // past the request's last one reads zeros, so no load sits under a branch
+    // or needs a clamp.
+    // Wave w owns blocks [16 w, 16 w + 16) of each 64-block chunk: group g
+    // covers its blocks 4 g + q, q = lane / 16 (a DPP row per block).  After
+    // the four groups, lane d < 16 holds the score of the wave's block d.
+    // Scores collect in LDS and go out once, after the workgroup's last item:
+    // 64-byte writes scattered through the summary stream cost far more than
+    // their bytes (the DRAM turns from reads to writes for each), about 9% of
+    // the kernel, and the loop then holds no store.
+    const int wave = tid >> 6;
+    const int row_q = lane >> 4;
+    const int lane_voff = (16 * wave + row_q) * kSummaryBytes + li * 16;
+
+    // Segments: the runs of consecutive items of one (request, KV head) in
+    // this workgroup's range.  Qp / Qm are rebuilt at the start of each; the
+    // chunks of a segment then run through the pipeline, whose loop holds no
+    // branch but its exit.
+    int v = v0;
+    int rr = r, hh = 0, chunk = 0;
+    int nb = 0, cr = 0;
+    if (v0 < v1) {
+        nb = uni(n_blocks_of(ctx_r, NB_max));  // from the scan: no second load
+        cr = (nb + kItemBlocks - 1) / kItemBlocks;
+        const int rem = v0 - before;  // item index within request r
+        hh = uni(rem / cr);
+        chunk = uni(rem - hh * cr);
+    }
+    while (v < v1) {
+        const int c1 = uni(min(cr, chunk + (v1 - v)));  // this segment: chunks [chunk, c1)
+        rebuild(rr, hh);
+        const int rh = uni(rr * H_kv + hh);
+        const auto in = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint4 *>(kminmax + (size_t)rh * NB_max * 32), (short)0, nb * kSummaryBytes, kRsrcWord3);
+        // loads of group g of chunk c (its byte offset in the row is uniform)
+        auto load_group = [&](int c, int g, u32x4 &mn, u32x4 &mx) {
+            const int o = lane_voff + uni((c * kItemBlocks + 4 * g) * kSummaryBytes);
+            mn = load16(in, o);               // kmin, dims [8 li, 8 li + 8)
+            mx = load16(in, o + kD * 2);      // kmax, the same dims
+        };
+        // group g of chunk c: its scores go to lanes 4 g + q of `sv`; the
+        // registers are refilled with group g of chunk c_next
+        auto group = [&](int g, u32x4 &mn, u32x4 &mx, int c_next, float &sv) {
+            const uint32_t wmn[4] = {mn.x, mn.y, mn.z, mn.w};
+            const uint32_t wmx[4] = {mx.x, mx.y, mx.z, mx.w};
             double acc = 0.0;
 #pragma unroll
-            for (int w = 0; w < 8; w++) {
-                const int e = (w < 4) ? 2 * w : 8 + 2 * (w - 4);
-                acc = fma(qm[e], bf16_d(wmn[w] & 0xffffu), acc);
-                acc = fma(qm[e + 1], bf16_d(wmn[w] >> 16), acc);
-                acc = fma(qp[e], bf16_d(wmx[w] & 0xffffu), acc);
-                acc = fma(qp[e + 1], bf16_d(wmx[w] >> 16), acc);
+            for (int w = 0; w < 4; w++) {
+                acc = fma(qm[2 * w], bf16_d(wmn[w] & 0xffffu), acc);
+                acc = fma(qm[2 * w + 1], bf16_d(wmn[w] >> 16), acc);
+                acc = fma(qp[2 * w], bf16_d(wmx[w] & 0xffffu), acc);
+                acc = fma(qp[2 * w + 1], bf16_d(wmx[w] >> 16), acc);
             }
-            acc = octet_sum(acc);
-            if (li == 0) out[b] = (float)acc;
+            load_group(c_next, g, mn, mx);
+            acc = row_sum(acc);
+            const float got = __shfl((float)acc, 16 * (lane & 3), 64);  // block 4 g + (lane & 3)
+            if ((lane >> 2) == g) sv = got;
+        };
+        // the wave's 16 scores of chunk c (the workgroup's item k), -inf
+        // past the request's blocks, into LDS
+        auto keep_chunk = [&](int c, int k, float sv) {
+            const int b = c * kItemBlocks + 16 * wave + lane;
+            if (lane < 16) sbuf[k * kItemBlocks + 16 * wave + lane] = b < nb ? sv : -INFINITY;
+        };
+        const int k0 = v - v0;  // the segment's first item, in the workgroup's order
+        for (int i = tid; i < c1 - chunk; i += kThreads) {
+            sdst[k0 + i] = rh * NB_max + (chunk + i) * kItemBlocks;
+            scnt[k0 + i] = min(kItemBlocks, NB_max - (chunk + i) * kItemBlocks);
         }
-        // next item: the next chunk, then the next KV head, then the next
-        // request with any blocks
-        if (++chunk == cr) {
-            chunk = 0;
-            if (++h == H_kv) {
-                h = 0;
-                do {
-                    ++r;
-                    cr = r < B ? __builtin_amdgcn_readfirstlane(valid_chunks(ctx_len, r, NB_max)) : 1;
-                } while (cr == 0);
-            }
+        u32x4 X[kBuf], Y[kBuf];
+        const int last = c1 - 1;
+#pragma unroll
+        for (int g = 0; g < kGroups; g++) load_group(chunk, g, X[2 * g], X[2 * g + 1]);
+#pragma unroll
+        for (int g = 0; g < kGroups; g++) load_group(min(chunk + 1, last), g, Y[2 * g], Y[2 * g + 1]);
+        // X holds chunk c, Y chunk c + 1; using X refills it with c + 2, using
+        // Y with c + 3.  Refills past the segment re-read its last chunk and
+        // go unused, so the loop body is straight-line code.
+        for (int c = chunk;; c += 2) {
+            float sv = 0.f;
+#pragma unroll
+            for (int g = 0; g < kGroups; g++) group(g, X[2 * g], X[2 * g + 1], min(c + 2, last), sv);
+            keep_chunk(c, k0 + c - chunk, sv);
+            if (c + 1 >= c1) break;
+#pragma unroll
+            for (int g = 0; g < kGroups; g++) group(g, Y[2 * g], Y[2 * g + 1], min(c + 3, last), sv);
+            keep_chunk(c + 1, k0 + c + 1 - chunk, sv);
+            if (c + 2 >= c1) break;
         }
+        v += c1 - chunk;
+        // next segment: the next KV head, then the next request with blocks
+        chunk = 0;
+        if (++hh >= H_kv) {
+            hh = 0;
+            do {
+                rr = uni(rr + 1);
+                nb = rr < B ? uni(n_blocks_of(ctx_len[rr], NB_max)) : 1;
+                cr = (nb + kItemBlocks - 1) / kItemBlocks;
+            } while (cr == 0);
+        }
+    }
+
+    // the workgroup's scores: item i's blocks below NB_max go to sdst[i]
+    __syncthreads();
+    for (int idx = tid; idx < (v1 - v0) * kItemBlocks; idx += kThreads) {
+        const int i = idx / kItemBlocks, j = idx - i * kItemBlocks;
+        if (j < scnt[i]) scores[sdst[i] + j] = sbuf[idx];
     }
 
     // -inf past each request's last valid chunk
@@ -218,7 +322,11 @@ int score_grid(int n_items) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, score_kernel, kThreads, 0) != hipSuccess || o < 1) o = 2;
         occ = o;
     }
-    const long g = (long)device_cu_count() * occ;
+    // a persistent grid of the resident workgroups, but at least enough that
+    // no workgroup holds more than kMaxItems items
+    long g = (long)device_cu_count() * occ;
+    const long need = (n_items + kMaxItems - 1) / kMaxItems;
+    if (g < need) g = need;
     return (int)(n_items < g ? n_items : g);
 }
 

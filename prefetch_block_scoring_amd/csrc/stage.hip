@@ -1,10 +1,10 @@
 // KV selection and staging into the HBM working set.
 //
-// OasisKV (arXiv 2608.08097), paperlayer summary, section 4: at most C blocks
-// per KV head are transferred per layer; selection keeps resident predicted
-// blocks and pairs admitted non-resident predicted blocks with
-// least-recently-selected eviction targets; the full cache stays in host
-// memory and the admitted blocks are staged into HBM before the next step.
+// OasisKV (arXiv 2608.08097), paperlayer summary, section 4.  Each step, a
+// (request, KV head) pair's predicted blocks that already sit in its HBM
+// working set stay there; up to C of the others are brought in from the host
+// copy of the cache, each taking the place of the resident block that was
+// predicted longest ago once the budget is full.
 //
 // plan kernel: one workgroup per (request, KV head) updates that pair's slot
 //   table in LDS (the whole state is a few hundred integers) and emits the
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void stage_plan_kernel(PlanArgs a) {
         plan[0] = n_adm;
         plan[1] = need;
         plan[2] = 0;
-        plan[3] = 0;
+        plan[3] = nc - n_adm;  // deferred: predicted, not resident, not admitted
     }
     __syncthreads();
     for (int s = tid; s < S; s += kThreads) {
@@ -252,16 +252,29 @@ __global__ __launch_bounds__(kThreads) void stage_plan_kernel(PlanArgs a) {
 }
 
 // Exclusive prefix of the admit counts over (r, h), written to each row's
-// packed position, and the total after the rows: one workgroup.
-__global__ __launch_bounds__(1024) void stage_prefix_kernel(int32_t *__restrict__ plan, int row, int pairs) {
+// packed position, and the step's totals after the rows: admits, evictions,
+// deferred admits and the pairs with any deferred.  With `accum` (device
+// int64[4]) the same admits, evictions and deferred admits, and 1 for the
+// step, are added to it.  One workgroup.
+__global__ __launch_bounds__(1024) void stage_prefix_kernel(int32_t *__restrict__ plan, int row, int pairs,
+                                                            unsigned long long *__restrict__ accum) {
     __shared__ int tmp[16];
+    __shared__ int red[3][16];
     __shared__ int carry;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) carry = 0;
     __syncthreads();
+    int n_ev = 0, n_def = 0, n_cap = 0;
     for (int base = 0; base < pairs; base += 1024) {
         const int rh = base + tid;
-        const int v = rh < pairs ? plan[(size_t)rh * row] : 0;
+        int v = 0;
+        if (rh < pairs) {
+            const int32_t *p = plan + (size_t)rh * row;
+            v = p[0];
+            n_ev += p[1];
+            n_def += p[3];
+            n_cap += p[3] > 0;
+        }
         int inc = v;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -280,7 +293,37 @@ __global__ __launch_bounds__(1024) void stage_prefix_kernel(int32_t *__restrict_
         if (tid == 0) carry = all;
         __syncthreads();
     }
-    if (tid == 0) plan[(size_t)pairs * row] = carry;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        n_ev += __shfl_xor(n_ev, o, 64);
+        n_def += __shfl_xor(n_def, o, 64);
+        n_cap += __shfl_xor(n_cap, o, 64);
+    }
+    if (lane == 0) {
+        red[0][wave] = n_ev;
+        red[1][wave] = n_def;
+        red[2][wave] = n_cap;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int ev = 0, def = 0, cap = 0;
+        for (int w = 0; w < 16; w++) {
+            ev += red[0][w];
+            def += red[1][w];
+            cap += red[2][w];
+        }
+        int32_t *tail = plan + (size_t)pairs * row;
+        tail[0] = carry;
+        tail[1] = ev;
+        tail[2] = def;
+        tail[3] = cap;
+        if (accum) {
+            atomicAdd(accum + 0, (unsigned long long)carry);
+            atomicAdd(accum + 1, (unsigned long long)ev);
+            atomicAdd(accum + 2, (unsigned long long)def);
+            atomicAdd(accum + 3, 1ull);
+        }
+    }
 }
 
 // Packed positions: the admits of one step, numbered in (pair, admission)
@@ -401,7 +444,8 @@ hipError_t launch_stage_plan(const oasis_dims &d, const oasis_stage_args &a, hip
 }
 
 hipError_t launch_stage_prefix(const oasis_dims &d, const oasis_stage_args &a, hipStream_t s) {
-    hipLaunchKernelGGL(stage_prefix_kernel, dim3(1), dim3(1024), 0, s, a.plan, plan_row(a.C), d.B * d.H_kv);
+    hipLaunchKernelGGL(stage_prefix_kernel, dim3(1), dim3(1024), 0, s, a.plan, plan_row(a.C), d.B * d.H_kv,
+                       reinterpret_cast<unsigned long long *>(a.stats_accum));
     return hipGetLastError();
 }
 

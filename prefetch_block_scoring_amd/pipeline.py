@@ -1,11 +1,11 @@
 """Per-layer decode chain overlapped across layers and decode steps.
 
-The OasisKV pages (arXiv 2608.08097, paperlayer summary, section 4) run, per
-layer, a background chain of top-K prediction, KV selection and KV transfer,
-with independent workers overlapped across layers and decode steps; the
-foreground waits only for the relevant layer's transfer before that layer's
-next-step attention.  The library's native pipeline (oasis_pipeline_* in
-include/oasis.h) schedules that chain on one GPU:
+OasisKV (arXiv 2608.08097), paperlayer summary, section 4.  Prediction,
+selection and the copy of the admitted blocks for a layer run off the
+critical path, so that several layers and decode steps are in flight at once;
+a layer's attention is held back only until its own working set has been
+copied.  The library's native pipeline (oasis_pipeline_* in include/oasis.h)
+lays that out on one GPU's streams:
 
   main stream     attention of (layer l, step t), after the transfer of
                   (l, t - 1) only
@@ -109,7 +109,15 @@ class LayerPipeline:
                  copy_mode: int = oa.OASIS_COPY_KERNEL, host_threads: int = 8, n_split: int = 0, J: int = 1,
                  n_q: int = 1, compute_streams: int = 0):
         B, H_kv, NB, _, bs, D = pool.shape
+        if tuple(summ.shape) != (B, H_kv, NB, 2, D) or summ.dtype != torch.bfloat16 or not summ.is_cuda:
+            raise ValueError(f"summ: expected bf16 device [B][H_kv][NB_max][2][D] = {(B, H_kv, NB, 2, D)}, "
+                             f"got {summ.dtype} {tuple(summ.shape)}")
+        if tuple(ctx.shape) != (B,) or ctx.dtype != torch.int32 or not ctx.is_cuda:
+            raise ValueError(f"ctx: expected int32 device [B] = ({B},), got {ctx.dtype} {tuple(ctx.shape)}")
+        if H_q % H_kv != 0:
+            raise ValueError(f"H_q = {H_q} is not a multiple of H_kv = {H_kv}")
         self.B, self.H_q, self.H_kv, self.NB, self.K_b, self.C = B, H_q, H_kv, NB, K_b, C
+        self.block_bytes = 2 * bs * D * pool.element_size()  # K and V of one block
         self.pool, self.summ, self.ctx = pool, summ, ctx
         self.staged, self.copy_mode = staged, copy_mode
         self.L, self.J, self.n_q = n_layers, J, n_q
@@ -118,13 +126,17 @@ class LayerPipeline:
         self.layers = [_Layer(B, H_q, H_kv, NB, K_b, C, staged, copy_mode, ws, dev, D, bs, n_q)
                        for _ in range(n_layers)]
         self.main = torch.cuda.current_stream()
+        # admits, evictions, deferred admits and staging steps of every layer,
+        # added by the plan kernels on the device
+        self.stats = torch.zeros(4, dtype=torch.int64, device=dev)
         bufs = (oa.oasis_layer_buffers * n_layers)(*[ly.buffers() for ly in self.layers])
         desc = oa.oasis_pipeline_desc(
             n_layers=n_layers, K_b=K_b, C=C if staged else 0, J=J, n_q=n_q, staged=int(staged),
             copy_mode=copy_mode,
             host_threads=host_threads, n_split=n_split, sm_scale=1.0 / math.sqrt(D), pool=pool.data_ptr(),
             kminmax=summ.data_ptr(), ctx_len=ctx.data_ptr(), main_stream=self.main.cuda_stream,
-            layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)), compute_streams=compute_streams)
+            layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)), compute_streams=compute_streams,
+            stage_stats=self.stats.data_ptr() if staged else None)
         self._h = oa.oasis_pipeline_create(oa.dims(B, H_q, H_kv, NB, D, bs), desc)
         self.comp = torch.cuda.ExternalStream(oa.oasis_pipeline_stream(self._h, 1))
         odd = oa.oasis_pipeline_stream(self._h, 4)
@@ -142,8 +154,10 @@ class LayerPipeline:
         D = self.layers[l].out.shape[-1]
         if tuple(q_look.shape) != (self.B, self.J, self.H_q, D):
             raise ValueError(f"q_look shape {tuple(q_look.shape)}: expected [B][J = {self.J}][H_q][D]")
-        if t >= 1 and q_attn.numel() != self.B * self.n_q * self.H_q * D:
-            raise ValueError(f"q_attn shape {tuple(q_attn.shape)}: expected [B][n_q = {self.n_q}][H_q][D]")
+        if t >= 1 and (q_attn is None or q_attn.numel() != self.B * self.n_q * self.H_q * D
+                       or q_attn.dtype != torch.bfloat16 or not q_attn.is_cuda or not q_attn.is_contiguous()):
+            raise ValueError(f"q_attn: expected contiguous bf16 device [B][n_q = {self.n_q}][H_q][D], got "
+                             f"{None if q_attn is None else (q_attn.dtype, tuple(q_attn.shape))}")
         ly = self.layers[l]
         oa.oasis_pipeline_layer_step(self._h, l, t, q_look, q_attn if t >= 1 else None, ly.out, ly.lse)
 
@@ -157,6 +171,21 @@ class LayerPipeline:
         ly = self.layers[l]
         row = 4 + 2 * max(self.K_b if t == 0 else self.C, 1)
         return ly.plans[t % 2][self.B * self.H_kv * row]
+
+    def reset_stage_stats(self):
+        """Clears the staging counters; call it with no layer-step in flight
+        (it synchronises the device, so the clear is done before any later
+        plan kernel adds to them)."""
+        self.stats.zero_()
+        torch.cuda.synchronize(self.stats.device)
+
+    def stage_stats(self) -> dict:
+        """Admits, evictions, deferred admits and staging steps summed over
+        every layer since the last reset (synchronises the device)."""
+        torch.cuda.synchronize(self.stats.device)
+        a, e, d, n = (int(x) for x in self.stats.cpu().tolist())
+        return {"admits": a, "evictions": e, "deferred": d, "steps": n,
+                "bytes": a * self.block_bytes}
 
     def table(self, l: int, t: int):
         """(slot, block, n) tables that the attention of step t reads."""

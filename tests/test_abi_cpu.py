@@ -144,8 +144,10 @@ def stage_args(**kw):
 def test_stage_argument_errors(kw, code):
     dd = d()
     a = stage_args(**kw)
-    assert L.oasis_stage_blocks(ctypes.byref(dd), ctypes.byref(a)) == code
+    st = binding.oasis_stage_stats(admits=7)
+    assert L.oasis_stage_blocks(ctypes.byref(dd), ctypes.byref(a), ctypes.byref(st)) == code
     assert oa.oasis_last_error() != ""
+    assert L.oasis_stage_blocks(ctypes.byref(dd), ctypes.byref(a), None) == code
 
 
 def test_plan_and_staging_sizes():

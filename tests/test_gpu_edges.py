@@ -110,3 +110,43 @@ def test_degenerate_contexts(n_split):
         assert np.all(gn[r] == min(n_blocks(c), K_b))
     o = out.cpu()
     assert torch.all(o[0] == 0)          # empty context
+
+
+@pytest.mark.parametrize("pad", ["nan", "inf", "-inf"])
+@pytest.mark.parametrize("n_q", [1, 2, 3])
+def test_nonfinite_padding_is_never_used(pad, n_q):
+    """Positions past a request's context may hold anything, NaN and Inf
+    included (a pool that appends fill token by token starts from
+    uninitialised memory).  Their weight is 0, and 0 * NaN would still poison
+    the output, so both p . V paths must leave those rows out: with G = 4,
+    n_q = 1 and 2 give 4 and 8 columns (VALU p . V), n_q = 3 gives 12
+    (matrix-core p . V).  Every listed table ends with the partial last
+    block."""
+    m = oa()
+    ctxs = [1, 15, 17, 40, 3000]
+    B, H_q, H_kv, D, T = len(ctxs), 8, 2, 128, 6
+    NB = n_blocks(max(ctxs))
+    g = torch.Generator().manual_seed(94)
+    kv = torch.randn((B, H_kv, NB, 2, 16, D), generator=g).to(torch.bfloat16)
+    for r, c in enumerate(ctxs):
+        for b in range(c // 16, NB):
+            kv[r, :, b, :, max(c - 16 * b, 0):] = float(pad)
+    q = torch.randn((B, n_q, H_q, D), generator=g).to(torch.bfloat16)
+    tbl = torch.full((B, H_kv, T), -1, dtype=torch.int32)
+    n = torch.zeros((B, H_kv), dtype=torch.int32)
+    for r, c in enumerate(ctxs):
+        nb = n_blocks(c)
+        ids = list(range(max(0, nb - T), nb))
+        tbl[r, :, :len(ids)] = torch.tensor(ids, dtype=torch.int32)
+        n[r] = len(ids)
+    ctx_cpu = torch.tensor(ctxs, dtype=torch.int32)
+    sm = 1.0 / math.sqrt(D)
+    for n_split in (1, 2):
+        out = m.oasis_lookahead_attn(q.to(DEV), kv.to(DEV), tbl.to(DEV), tbl.to(DEV), n.to(DEV), ctx_cpu.to(DEV),
+                                     sm_scale=sm, n_split=n_split)
+        torch.cuda.synchronize()
+        o = out.cpu()
+        assert torch.isfinite(o.float()).all(), f"pad {pad}, n_q {n_q}, n_split {n_split}"
+        for j in range(n_q):
+            ref, _ = oracle.attend(u16(q[:, j].contiguous()), u16(kv), ctx_cpu.numpy(), tbl.numpy(), n.numpy(), sm)
+            assert_attn_close(bf16_to_f64(u16(o[:, j].contiguous())), ref)

@@ -255,20 +255,23 @@ def test_stage_matches_oracle(copy_mode, stage_blocks, split, C, turnover):
     stage_dev = torch.empty(sbytes, dtype=torch.uint8, device=DEV)
     ctx = dev(ctx_cpu)
     copy_stream = torch.cuda.Stream()
+    accum = torch.zeros(4, dtype=torch.int64, device=DEV)
     st = oracle.StageState(w.B, w.H_kv, NB)
+    totals = np.zeros(4, dtype=np.int64)
     for s in range(steps):
         Cs = K_b if s == 0 else C
         kw = dict(sel=dev(sels[s]), n_sel=dev(nsels[s]), scores=dev(scores[s]), ctx_len=ctx,
                   K_b=K_b, C=Cs, step=s, slot_block=slot_block, slot_stamp=slot_stamp,
                   host_pool=host, ws_pool=ws, tbl_slot=tbl_slot, tbl_block=tbl_block,
                   tbl_n=tbl_n, plan=plan, host_plan=host_plan, stage_host=stage_host[s % 2],
-                  stage_dev=stage_dev, copy_mode=copy_mode)
+                  stage_dev=stage_dev, copy_mode=copy_mode, stats_accum=accum)
         if split:
             planned = torch.cuda.Event()
             oa().oasis_stage_plan(plan_event=planned, **kw)
             oa().oasis_stage_copy(plan_event=planned, copy_stream=copy_stream, **kw)
+            stats = oa().oasis_stage_read_stats(plan, w.B, w.H_kv, Cs)
         else:
-            oa().oasis_stage_blocks(**kw)
+            stats = oa().oasis_stage_blocks(want_stats=True, **kw)
         torch.cuda.synchronize()
         adm, na, ev, ne = oracle.stage(st, sels[s].numpy(), nsels[s].numpy(), scores[s].numpy(),
                                        ctx_cpu.numpy(), w.bs, K_b, Cs, s)
@@ -281,7 +284,14 @@ def test_stage_matches_oracle(copy_mode, stage_blocks, split, C, turnover):
         np.testing.assert_array_equal(p[:, :, 1], ne)
         # packed positions: running total of admits in (r, h) order
         np.testing.assert_array_equal(p[:, :, 2].ravel(), np.concatenate([[0], np.cumsum(na.ravel())[:-1]]))
-        assert flat[w.B * w.H_kv * row] == na.sum()
+        # deferred admits: predicted blocks the cap held back
+        np.testing.assert_array_equal(p[:, :, 3], st.deferred)
+        tail = flat[w.B * w.H_kv * row: w.B * w.H_kv * row + 4]
+        assert tail.tolist() == [na.sum(), ne.sum(), st.deferred.sum(), (st.deferred > 0).sum()]
+        assert stats == {"admits": na.sum(), "evictions": ne.sum(), "deferred": st.deferred.sum(),
+                         "capped_pairs": (st.deferred > 0).sum(), "bytes": na.sum() * 8192}
+        totals += [na.sum(), ne.sum(), st.deferred.sum(), 1]
+        assert accum.cpu().tolist() == totals.tolist()
         for r in range(w.B):
             for h in range(w.H_kv):
                 k = int(na[r, h])
@@ -305,7 +315,8 @@ def test_stage_matches_oracle(copy_mode, stage_blocks, split, C, turnover):
 
 def run_chain_gpu(w, steps, C, copy_mode=0):
     """score -> select -> stage -> attend for `steps` steps; returns per-step
-    (scores, sel, n_sel, stamps, out) on the CPU."""
+    (scores, sel, n_sel, stamps, out, attended blocks, their count) on the
+    CPU."""
     m = oa()
     ctx_cpu = wl.context_lengths(w)
     ctx = ctx_cpu.to(DEV)
@@ -338,29 +349,8 @@ def run_chain_gpu(w, steps, C, copy_mode=0):
         out = m.oasis_sparse_decode_attn(q, ws, t[0], t[1], t[2], ctx)
         torch.cuda.synchronize()
         hist.append((sc.cpu().numpy(), sel.cpu().numpy(), n.cpu().numpy(),
-                     gpu_stage_state(slot_block, slot_stamp, w.NB_max), u16(out)))
-    return hist
-
-
-def run_chain_oracle(w, steps, C):
-    ctx = wl.context_lengths(w).numpy()
-    kv = u16(wl.kv_pool(w))
-    summ = oracle.build_summaries(kv, ctx, w.bs)
-    st = oracle.StageState(w.B, w.H_kv, w.NB_max)
-    hist = []
-    for s in range(steps):
-        sc = oracle.score(u16(wl.lookahead(w, s)), summ, ctx, w.bs, w.H_kv)
-        sel, n = oracle.select(sc, ctx, w.bs, w.K_b)
-        oracle.stage(st, sel, n, sc, ctx, w.bs, w.K_b, w.K_b if s == 0 else C, s)
-        blocks = np.full((w.B, w.H_kv, w.K_b), -1, dtype=np.int32)
-        nblk = np.zeros((w.B, w.H_kv), dtype=np.int32)
-        for r in range(w.B):
-            for h in range(w.H_kv):
-                res = st.resident(r, h)
-                blocks[r, h, :len(res)] = res
-                nblk[r, h] = len(res)
-        out, _ = oracle.attend(u16(wl.attention_query(w, s + 1)), kv, ctx, blocks, nblk, 1 / math.sqrt(w.D))
-        hist.append((sc, sel, n, st.stamp.copy(), out))
+                     gpu_stage_state(slot_block, slot_stamp, w.NB_max), u16(out),
+                     t[1].cpu().numpy(), t[2].cpu().numpy()))
     return hist
 
 
@@ -368,20 +358,35 @@ def run_chain_oracle(w, steps, C):
                                         ("gqa32b_ragged_b16_staged", 2, (3000, 9000))])
 @pytest.mark.parametrize("copy_mode", [0, 1])
 def test_chain_end_to_end(name, B, ctx, copy_mode):
+    """Every step is compared in full.  Scores and the selection against the
+    oracle's own (the selection up to tied swaps); the staging step by
+    running the oracle's stage on the GPU's selection and scores, so the two
+    states follow the same predictions even after a tied swap; attention
+    against the oracle's attention over the GPU's resident set."""
     w = wl.WORKLOADS[name].shrink(B=B, ctx=ctx)
     C = oracle.fetch_cap_blocks(w.cap, w.K_b)
     steps = 5
     g = run_chain_gpu(w, steps, C, copy_mode)
-    o = run_chain_oracle(w, steps, C)
     ctx_np = wl.context_lengths(w).numpy()
+    kv = u16(wl.kv_pool(w))
+    summ = oracle.build_summaries(kv, ctx_np, w.bs)
+    st = oracle.StageState(w.B, w.H_kv, w.NB_max)
+    compared = 0
     for s in range(steps):
-        gs, gsel, gn, gst, gout = g[s]
-        os_, osel, on, ost, oout = o[s]
+        gs, gsel, gn, gst, gout, gblk, gnblk = g[s]
+        os_ = oracle.score(u16(wl.lookahead(w, s)), summ, ctx_np, w.bs, w.H_kv)
+        osel, on = oracle.select(os_, ctx_np, w.bs, w.K_b)
         assert_scores_close(gs, os_, ctx_np)
         assert_selection_matches(gsel, gn, osel, on, os_)
-        if np.array_equal(gsel, osel):
-            np.testing.assert_array_equal(gst, ost, err_msg=f"step {s}")
-            assert_attn_close(bf16_to_f64(gout), oout)
+        oracle.stage(st, gsel, gn, gs, ctx_np, w.bs, w.K_b, w.K_b if s == 0 else C, s)
+        np.testing.assert_array_equal(gst, st.stamp, err_msg=f"step {s}")
+        for r in range(w.B):
+            for h in range(w.H_kv):
+                assert sorted(gblk[r, h, :gnblk[r, h]].tolist()) == st.resident(r, h).tolist()
+        oout, _ = oracle.attend(u16(wl.attention_query(w, s + 1)), kv, ctx_np, gblk, gnblk, 1 / math.sqrt(w.D))
+        assert_attn_close(bf16_to_f64(gout), oout)
+        compared += 1
+    assert compared == steps
 
 
 # ---------------------------------------------------------------- pipelined layers
