@@ -5,13 +5,12 @@ One layer-step = one pass of the whole path over the batch for one layer:
 block scores from that layer's lookahead queries, top-K under the KV budget,
 staging of the newly selected blocks (fetch-capped, from the pinned host pool
 into the layer's HBM working set) and sparse GQA decode attention over the
-working set.  The OasisKV pages (arXiv 2608.08097, paperlayer summary,
-section 4) run the per-layer chain on background workers overlapped across
-layers and decode steps; the foreground waits only for the relevant layer's
-transfer before that layer's next-step attention.  The benchmark does the
-same with `--layers` layers in flight (default 4): each decode step runs the
-layers in order; a layer's staging overlaps the other layers' work and its
-attention at the next step waits only on its own staging.
+working set.  OasisKV (arXiv 2608.08097, paperlayer summary, section 4) keeps
+prediction, selection and copies off the attention's critical path with
+several layers in flight; the benchmark keeps `--layers` layers in flight
+(default 4): each decode step issues the layers in order, a layer's staging
+overlaps the other layers' work, and its attention at the next step waits
+only on its own copies.
 
 Workload (default): the Qwen3-8B-shaped layer (32 query / 8 KV heads, head dim
 128, 16-token blocks) at batch 128 and 16K context, 2048-token budget, fetch
@@ -95,6 +94,77 @@ def percentiles(values):
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+ROTATION_BYTES = 1 << 30     # bytes a rotation of alone launches cycles through
+
+
+def rotation_count(nbytes, most=64):
+    """Input copies for launches timed alone: at least three, and enough that
+    one round through them reads ROTATION_BYTES (four times the 256 MB
+    Infinity Cache), so a launch never re-reads what the last ones cached."""
+    return int(min(most, max(3, -(-ROTATION_BYTES // max(int(nbytes), 1)))))
+
+
+def time_rotated(torch, fns, n):
+    """Mean microseconds per launch of n launches cycling through fns (one
+    launch per input copy), after one untimed round."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fns[i % len(fns)]()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n * 1e3
+
+
+def alone_entry(nbytes, us, n_rot, how):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"avg_us": round(us, 2), "bytes": int(nbytes), "GBps": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "rotation": n_rot,
+            "note": f"alone on the GPU after the timed steps; consecutive launches cycle through {n_rot} {how}"}
+
+
+def numa_placement(host_tensor, samples=256):
+    """NUMA node of the GPU (sysfs, from its PCI address) and the nodes that
+    hold a sample of a pinned host buffer's pages (move_pages with no target
+    nodes reports where each page lives)."""
+    import ctypes
+    import torch
+    out = {"gpu_node": None, "pool_pages": None}
+    try:
+        p = torch.cuda.get_device_properties(torch.cuda.current_device())
+        addr = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+        with open(f"/sys/bus/pci/devices/{addr}/numa_node") as f:
+            out["gpu_node"] = int(f.read().strip())
+        out["gpu_pci"] = addr
+    except (AttributeError, OSError, ValueError):
+        pass
+    try:
+        libc = ctypes.CDLL(None, use_errno=True)
+        page = os.sysconf("SC_PAGE_SIZE")
+        base = host_tensor.data_ptr()
+        nbytes = host_tensor.numel() * host_tensor.element_size()
+        step = max(page, (nbytes // samples) // page * page)
+        addrs = [(base + i * step) // page * page for i in range(samples) if i * step < nbytes]
+        pages = (ctypes.c_void_p * len(addrs))(*addrs)
+        status = (ctypes.c_int * len(addrs))()
+        SYS_move_pages = 279  # x86_64
+        rc = libc.syscall(SYS_move_pages, 0, ctypes.c_ulong(len(addrs)), pages, None, status, 0)
+        if rc == 0:
+            counts = {}
+            for v in status:
+                key = str(v) if v >= 0 else f"err{-v}"
+                counts[key] = counts.get(key, 0) + 1
+            out["pool_pages"] = counts
+        else:
+            out["pool_pages"] = f"move_pages errno {ctypes.get_errno()}"
+    except (OSError, AttributeError) as e:
+        out["pool_pages"] = f"unavailable: {e}"
+    return out
 
 
 KERNEL_SOURCES = {"attn_kernel": "attn.hip", "score_kernel": "score.hip", "topk_kernel": "topk.hip",
@@ -346,29 +416,27 @@ def main():
                          n_q=n_q, compute_streams=args.compute_streams)
     T = K_b
     splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
-    admitted = torch.zeros((), dtype=torch.int64, device=dev)
 
-    def run(t0, t1, counting=False, step_events=None):
+    def run(t0, t1, step_events=None):
         for t in range(t0, t1):
             for l in range(L):
                 s = t + 3 * l
                 pipe.layer_step(l, t, q_look[s], q_attn[s])
-                if counting and staged and t >= 1:
-                    pipe.drain()
-                    with torch.cuda.stream(pipe.comp_stream(l)):
-                        admitted.add_(pipe.admitted(l, t))
             if step_events is not None:
                 # the main stream passes the step's last attention
                 ev = torch.cuda.Event(enable_timing=True)
                 ev.record(pipe.main)
                 step_events.append(ev)
 
-    # initial fill (step 0) and warm-up; the warm-up steps also count the
-    # admitted blocks per layer-step (a property of the workload's drift), so
-    # that no counting work runs inside the timed steps
-    run(0, 1 + args.warmup, counting=True)
+    # initial fill (step 0) and warm-up
+    run(0, 1 + args.warmup)
     pipe.drain()
     torch.cuda.synchronize()
+    # the staging counters (admits, evictions, deferred admits, steps) that
+    # the plan kernels add up on the device: cleared now, read after the
+    # timed steps, so the H2D bytes are those of the timed steps themselves
+    if staged:
+        pipe.reset_stage_stats()
     # timing events around the attention launches of the timed steps, on
     # their own stream (the roofline's live figure); other kinds only with
     # --kernel-timing all
@@ -382,6 +450,7 @@ def main():
     pipe.drain()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    timed_stats = pipe.stage_stats() if staged else None
     layer_steps = args.steps * L
     ms_per_step = elapsed / layer_steps * 1e3
     value = B * layer_steps / elapsed
@@ -440,7 +509,9 @@ def main():
                               "note": ("host time of a staging call: plan read-back and packing up to the "
                                        "copy's enqueue") if copy_mode != oa.OASIS_COPY_KERNEL
                               else "host time of a staging call (enqueue only)"}
-        adm = int(admitted) / max(args.warmup * L, 1)
+        if timed_stats["steps"] != args.steps * L:
+            raise SystemExit(f"staging counters saw {timed_stats['steps']} steps, {args.steps * L} expected")
+        adm = timed_stats["admits"] / (args.steps * L)
         h2d_bytes = adm * 2 * bs * D * 2
         # reference: one large pinned host -> device copy
         big = oa.oasis_host_empty((256 << 20,), torch.uint8)
@@ -459,47 +530,83 @@ def main():
                "frac_of_nominal": round(step_gbs / PCIE_PEAK_GBS, 3),
                "pinned_memcpy_GBps": round(memcpy_gbs, 2),
                "frac_of_memcpy": round(step_gbs / memcpy_gbs, 3),
-               "copy_engine": args.copy_mode, "drift_frac": round(adm / (B * H_kv) / K_b, 4)}
+               "copy_engine": args.copy_mode, "drift_frac": round(adm / (B * H_kv) / K_b, 4),
+               "deferred_per_layer_step": round(timed_stats["deferred"] / (args.steps * L), 1),
+               "evictions_per_layer_step": round(timed_stats["evictions"] / (args.steps * L), 1),
+               "counted": f"device counters of the plan kernels over the {args.steps * L} timed layer-steps",
+               "numa": numa_placement(pool)}
         del big, dst
 
-    # the same attention launch alone on the GPU (nothing else in flight),
-    # over the last step's working set of layer 0: the kernel's own rate,
-    # beside its rate while sharing the GPU with the pipeline above
+    # The same launches alone on the GPU (nothing else in flight): each
+    # kernel's own rate, beside its rate while sharing the GPU with the
+    # pipeline above.  Consecutive launches read different copies of their
+    # input (rotation), at least 1 GiB apart in total, so no launch finds its
+    # bytes in the 256 MB Infinity Cache that the previous one filled.
     q4 = q_attn[t_last].view(B, n_q, H_q, D)
     out_alone = torch.empty_like(q4)
+    attn_ws = pipe.layers[0].attn_ws
     if staged:
         tb = pipe.table(0, t_last)
-        alone = lambda: oa.oasis_lookahead_attn(
-            q4, pipe.layers[0].ws_pool, tb[0], tb[1], tb[2], ctx, out=out_alone, ws=pipe.layers[0].attn_ws,
-            n_split=args.n_split)
+        wsp = pipe.layers[0].ws_pool
+        n_rot = rotation_count(attn_bytes)
+        pools = [wsp] + [wsp.clone() for _ in range(n_rot - 1)]
+        attn_fns = [lambda p=p_: oa.oasis_lookahead_attn(q4, p, tb[0], tb[1], tb[2], ctx, out=out_alone, ws=attn_ws,
+                                                          n_split=args.n_split) for p_ in pools]
+        rot_how = "copies of the working set"
     else:
         jp = (t_last - 1) % 2
         sel, ns = pipe.layers[0].sel[jp], pipe.layers[0].n_sel[jp]
-        alone = lambda: oa.oasis_lookahead_attn(
-            q4, pool, sel, sel, ns, ctx, out=out_alone, ws=pipe.layers[0].attn_ws, n_split=args.n_split)
-    alone()
-    torch.cuda.synchronize()
+        # the same number of blocks per (r, h), shifted by k * K_b blocks
+        # (mod the request's blocks): other blocks of the same pool
+        nbl = ((ctx + bs - 1) // bs).clamp(min=1).view(B, 1, 1)
+        n_rot = min(rotation_count(attn_bytes), max(1, NB // K_b))
+        sels = [sel] + [torch.where(sel >= 0, (sel + k * K_b) % nbl, sel).to(torch.int32).contiguous()
+                        for k in range(1, n_rot)]
+        attn_fns = [lambda t_=t_: oa.oasis_lookahead_attn(q4, pool, t_, t_, ns, ctx, out=out_alone, ws=attn_ws,
+                                                           n_split=args.n_split) for t_ in sels]
+        rot_how = "tables shifted to other blocks of the pool"
     # attention launches of each phase in launch order, so that a profiled
     # run's kernel trace can be split the same way (--summarize-profile)
+    n_alone = max(20, len(attn_fns))
     log("attention launches: " + json.dumps({"warmup": args.warmup * L, "timed": args.steps * L,
-                                             "extra": n_extra * L if extra else 0, "alone": 21}))
-    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ea.record()
-    for _ in range(20):
-        alone()
-    eb.record()
-    torch.cuda.synchronize()
-    alone_us = ea.elapsed_time(eb) / 20 * 1e3
-    kern["attn_alone"] = {"avg_us": round(alone_us, 2), "bytes": attn_bytes,
-                          "GBps": round(attn_bytes / (alone_us * 1e-6) / 1e9, 1),
-                          "frac_of_peak": round(attn_bytes / (alone_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                          "note": "same launch, alone on the GPU after the timed steps"}
+                                             "extra": n_extra * L if extra else 0,
+                                             "alone": len(attn_fns) + n_alone}))
+    alone_us = time_rotated(torch, attn_fns, n_alone)
+    kern["attn_alone"] = alone_entry(attn_bytes, alone_us, len(attn_fns), rot_how)
+    del attn_fns
+    if staged:
+        del pools
+    else:
+        del sels
+
+    # scores alone, over rotated copies of the summaries
+    sc_out = pipe.layers[0].scores
+    n_rot = rotation_count(score_bytes)
+    summs = [summ] + [summ.clone() for _ in range(n_rot - 1)]
+    ql0 = q_look[t_last]
+    score_fns = [lambda sm_=sm_: oa.oasis_score_blocks(ql0, sm_, ctx, scores=sc_out) for sm_ in summs]
+    kern["score_alone"] = alone_entry(score_bytes, time_rotated(torch, score_fns, max(20, n_rot)), n_rot,
+                                      "copies of the block summaries")
+    del score_fns, summs
+    # top-K alone, over rotated copies of the scores
+    n_rot = rotation_count(topk_bytes)
+    scs = [sc_out] + [sc_out.clone() for _ in range(n_rot - 1)]
+    sel_o, n_o = pipe.layers[0].sel[0], pipe.layers[0].n_sel[0]
+    topk_fns = [lambda x=x: oa.oasis_select_topk(x, ctx, K_b, sel=sel_o, n_sel=n_o) for x in scs]
+    kern["topk_alone"] = alone_entry(topk_bytes, time_rotated(torch, topk_fns, max(20, n_rot)), n_rot,
+                                     "copies of the scores")
+    del topk_fns, scs
+    torch.cuda.empty_cache()
 
     if args.attn_sweep:
         # look-ahead attention alone over the same blocks for n_q = 1, 2, ...
         # query vectors per request (K / V read once for all of them)
         sweep = {}
         gq = torch.Generator(device=dev).manual_seed(17)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if not staged:
+            jp = (t_last - 1) % 2
+            sel, ns = pipe.layers[0].sel[jp], pipe.layers[0].n_sel[jp]
         for nq in range(1, 16 // (H_q // H_kv) + 1):
             qs = torch.randn((B, nq, H_q, D), generator=gq, device=dev).to(torch.bfloat16)
             o_s = torch.empty_like(qs)
@@ -677,8 +784,9 @@ def agreement_run(args):
 
 def cpu_baseline(w, pool, ctx_cpu, q_look, seconds, C):
     """The CPU oracle, unchanged, on the same inputs: full-batch layer-steps
-    (score, select, staging bookkeeping, attention over the resident blocks
-    read from the host pool) until about `seconds` of work are done."""
+    (score, select, staging bookkeeping and a host copy of the admitted
+    blocks into a staging buffer, attention over the resident blocks read
+    from the host pool) until about `seconds` of work are done."""
     import numpy as np
     import torch
     import oracle
@@ -690,7 +798,10 @@ def cpu_baseline(w, pool, ctx_cpu, q_look, seconds, C):
     summ = oracle.build_summaries(kv_np, ctx, w.bs)
     st = oracle.StageState(w.B, w.H_kv, w.NB_max)
     sm = 1.0 / math.sqrt(w.D)
-    n_steps, t_total = 0, 0.0
+    # host staging buffer for the admitted blocks of one step (as many as the
+    # uncapped first step admits)
+    stage_buf = np.empty((w.B * w.H_kv * w.K_b,) + kv_np.shape[3:], dtype=np.uint16) if w.staged else None
+    n_steps, t_total, copied = 0, 0.0, 0
     s = 0
     while True:
         ql = q_look[s % len(q_look)].cpu().view(torch.int16).numpy().view(np.uint16)
@@ -699,7 +810,11 @@ def cpu_baseline(w, pool, ctx_cpu, q_look, seconds, C):
         sc = oracle.score(ql, summ, ctx, w.bs, w.H_kv)
         sel, n = oracle.select(sc, ctx, w.bs, w.K_b)
         if w.staged:
-            oracle.stage(st, sel, n, sc, ctx, w.bs, w.K_b, w.K_b if s == 0 else C, s)
+            adm, na, _, _ = oracle.stage(st, sel, n, sc, ctx, w.bs, w.K_b, w.K_b if s == 0 else C, s)
+            # the admitted blocks, copied out of the host pool in (r, h, admission) order
+            rr, hh, kk = np.nonzero(np.arange(adm.shape[2])[None, None, :] < na[:, :, None])
+            stage_buf[:len(rr)] = kv_np[rr, hh, adm[rr, hh, kk]]
+            copied += len(rr)
             blocks = np.full((w.B, w.H_kv, w.K_b), -1, dtype=np.int32)
             nb = np.zeros((w.B, w.H_kv), dtype=np.int32)
             for r in range(w.B):
@@ -720,8 +835,11 @@ def cpu_baseline(w, pool, ctx_cpu, q_look, seconds, C):
     return {"value": round(w.B * n_steps / t_total, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{n_steps} full-batch layer-steps (B={w.B}) of score+select+"
-                      f"{'stage bookkeeping+' if w.staged else ''}attend, fp64 C oracle, "
-                      f"{t_total:.1f}s of CPU time",
+                      f"{'stage bookkeeping+host copy of the admitted blocks+' if w.staged else ''}attend, "
+                      f"fp64 C oracle, {t_total:.1f}s of CPU time"
+                      + (f"; {copied} blocks copied ({copied * 2 * w.bs * w.D * 2 / 1e6:.1f} MB)" if w.staged
+                         else ""),
+            "threads": oracle.num_threads(), "nproc": os.cpu_count(),
             "cpu_model": _cpu_model()}
 
 
