@@ -396,6 +396,28 @@ int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q,
                              void *ws, size_t ws_bytes, int32_t n_split,
                              void *stream);
 
+/* oasis_sparse_decode_attn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation with the same arguments except the
+ * workspace, whose split-K partials go to a fixed array in device memory
+ * that the library holds, oasis_sparse_decode_attn_static_bytes() bytes
+ * (8 MiB) on each device it runs on, until the process ends.  The call
+ * allocates nothing.  It fails with OASIS_ENOSPACE when the partials
+ * (B * H_q * splits * (D + 2) * 4 bytes, 0 without splitting) exceed the
+ * array.  Every call on a device uses that device's one array: calls that
+ * overlap on one device (on different streams, or from different threads)
+ * race and must be ordered by the caller.  Each call writes every partial it
+ * reads, so nothing needs clearing between calls. */
+size_t oasis_sparse_decode_attn_static_bytes(void);
+int oasis_sparse_decode_attn_static(const oasis_dims *dims, const uint16_t *q,
+                                    const uint16_t *kv_pool, int32_t P,
+                                    const int32_t *tbl_slot,
+                                    const int32_t *tbl_block,
+                                    const int32_t *tbl_n, int32_t T,
+                                    const int32_t *ctx_len, float sm_scale,
+                                    uint16_t *out, float *lse,
+                                    int32_t n_split, void *stream);
+
 /* Look-ahead attention (section 4: the normal query and the draft queries
  * are computed together over the resident KV).  Exactly
  * oasis_sparse_decode_attn applied to each of n_q query vectors per request

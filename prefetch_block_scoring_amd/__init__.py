@@ -12,5 +12,6 @@ from .binding import (  # noqa: F401
     oasis_pipeline_copy_host_seconds, oasis_pipeline_create, oasis_pipeline_desc, oasis_pipeline_destroy,
     oasis_pipeline_drain, oasis_pipeline_layer_step, oasis_pipeline_stream, oasis_pipeline_timing,
     oasis_pipeline_timing_read, oasis_pipeline_timing_values, oasis_score_blocks, oasis_select_topk, oasis_sparse_decode_attn,
+    oasis_sparse_decode_attn_static, oasis_sparse_decode_attn_static_bytes,
     oasis_stage_blocks, oasis_stage_buffer_bytes, oasis_stage_copy, oasis_stage_plan, oasis_stage_plan_bytes,
     oasis_stage_read_stats, oasis_stage_stats, oasis_version)

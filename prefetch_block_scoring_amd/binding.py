@@ -103,6 +103,9 @@ _SIGNATURES = {
     "oasis_sparse_decode_attn": (ctypes.c_int, [
         ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
         ctypes.c_size_t, _I32, _P]),
+    "oasis_sparse_decode_attn_static_bytes": (ctypes.c_size_t, []),
+    "oasis_sparse_decode_attn_static": (ctypes.c_int, [
+        ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _I32, _P]),
     "oasis_block_mass_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims)]),
     "oasis_block_attention_mass": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _P, _P, _P, ctypes.c_float, _P, _P,
                                                   ctypes.c_size_t, _P]),
@@ -563,6 +566,50 @@ def oasis_sparse_decode_attn(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: t
         ctypes.byref(d), _ptr(q), _ptr(kv_pool), int(P), _ptr(tbl_slot), _ptr(tbl_block), _ptr(tbl_n),
         int(T), _ptr(ctx_len), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), int(n_split), _stream(stream)))
+    return (out, lse) if want_lse or lse is not None else out
+
+
+def oasis_sparse_decode_attn_static_bytes() -> int:
+    """Bytes of the fixed split-K scratch of oasis_sparse_decode_attn_static."""
+    return int(_lib.oasis_sparse_decode_attn_static_bytes())
+
+
+def oasis_sparse_decode_attn_static(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: torch.Tensor,
+                                    tbl_block: torch.Tensor, tbl_n: torch.Tensor, ctx_len: torch.Tensor,
+                                    sm_scale: Optional[float] = None, out=None, lse=None, n_split: int = 0,
+                                    want_lse: bool = False, stream=None):
+    """oasis_sparse_decode_attn without a workspace: the split-K partials go
+    to the library's fixed device scratch, so the call allocates nothing
+    (pass `out` / `lse` to allocate nothing here either).  Calls that overlap
+    on one device race on that scratch."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 6)
+    _need(tbl_slot, "tbl_slot", torch.int32, 3)
+    _need(tbl_block, "tbl_block", torch.int32, 3)
+    _need(tbl_n, "tbl_n", torch.int32, 2)
+    _need(ctx_len, "ctx_len", torch.int32, 1)
+    B, H_q, D = q.shape
+    H_kv, P, bs = kv_pool.shape[1], kv_pool.shape[2], kv_pool.shape[4]
+    _group(H_q, H_kv)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 6, shape=(B, H_kv, P, 2, bs, D))
+    T = tbl_slot.shape[2]
+    _need(tbl_slot, "tbl_slot", torch.int32, 3, shape=(B, H_kv, T))
+    _need(tbl_block, "tbl_block", torch.int32, 3, shape=(B, H_kv, T))
+    _need(tbl_n, "tbl_n", torch.int32, 2, shape=(B, H_kv))
+    _need(ctx_len, "ctx_len", torch.int32, 1, shape=(B,))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3, shape=(B, H_q, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, shape=(B, H_q))
+    d = dims(B, H_q, H_kv, max(P, 1), D, bs)
+    _check(_lib.oasis_sparse_decode_attn_static(
+        ctypes.byref(d), _ptr(q), _ptr(kv_pool), int(P), _ptr(tbl_slot), _ptr(tbl_block), _ptr(tbl_n),
+        int(T), _ptr(ctx_len), float(sm_scale), _ptr(out), _ptr(lse), int(n_split), _stream(stream)))
     return (out, lse) if want_lse or lse is not None else out
 
 

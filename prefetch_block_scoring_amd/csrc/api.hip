@@ -475,6 +475,44 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
     return OASIS_OK;
 }
 
+size_t oasis_sparse_decode_attn_static_bytes(void) { return attn_static_scratch_bytes(); }
+
+int oasis_sparse_decode_attn_static(const oasis_dims *dims, const uint16_t *q, const uint16_t *kv_pool, int32_t P,
+                                    const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n,
+                                    int32_t T, const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse,
+                                    int32_t n_split, void *stream) {
+    clear_error();
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (P < 1) FAIL(OASIS_EINVAL, "P = %d < 1", P);
+    if (T < 0) FAIL(OASIS_EINVAL, "T = %d < 0", T);
+    if (n_split < 0 || n_split > 64) FAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", n_split);
+    if (!std::isfinite(sm_scale)) FAIL(OASIS_EINVAL, "sm_scale is not finite");
+    if (dims->B == 0) return OASIS_OK;
+    NEED(q);
+    NEED(kv_pool);
+    NEED(tbl_n);
+    NEED(ctx_len);
+    NEED(out);
+    if (T > 0) {
+        NEED(tbl_slot);
+        NEED(tbl_block);
+    }
+    const int splits = attn_splits(*dims, 1, T, n_split);
+    const size_t need = attn_ws_bytes(*dims, 1, T, n_split);
+    const size_t have = attn_static_scratch_bytes();
+    if (need > have)
+        FAIL(OASIS_ENOSPACE,
+             "split-K partials need %zu bytes, more than the %zu bytes of fixed scratch (B * H_q * splits * "
+             "(D + 2) * 4); use oasis_sparse_decode_attn with a workspace, or fewer splits",
+             need, have);
+    void *ws = nullptr;
+    if (need > 0) OASIS_HIP(attn_static_scratch(&ws));
+    OASIS_HIP(launch_attn(*dims, 1, q, kv_pool, P, tbl_slot, tbl_block, tbl_n, T, ctx_len, sm_scale, out, lse,
+                          static_cast<float *>(ws), splits, static_cast<hipStream_t>(stream)));
+    return OASIS_OK;
+}
+
 int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q, const uint16_t *kv_pool, int32_t P,
                              const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n, int32_t T,
                              const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,

@@ -41,6 +41,7 @@
 #include "oasis_internal.h"
 
 #include <cmath>
+#include <mutex>
 
 namespace oasis {
 namespace {
@@ -590,6 +591,37 @@ hipError_t launch_g(const oasis_dims &d, const AttnArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Split-K partials of oasis_sparse_decode_attn_static: a fixed array in
+// device memory for callers that cannot allocate.  Each device the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device array: kernels get the address
+// that hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+size_t attn_static_scratch_bytes() { return kStaticScratchBytes; }
+
+// Device address of this device's `scratch`, looked up once per device (with
+// that device current) and kept.
+hipError_t attn_static_scratch(void **ptr) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int attn_splits(const oasis_dims &d, int n_q, int T, int n_split) {
     if (n_split > 0) return n_split < 64 ? n_split : 64;

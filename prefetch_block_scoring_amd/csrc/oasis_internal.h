@@ -85,6 +85,12 @@ int attn_splits(const oasis_dims &d, int n_q, int T, int n_split);
 // split-K workspace for n_q queries per request
 size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split);
 
+// The fixed split-K scratch of oasis_sparse_decode_attn_static: its size, and
+// its address on the current device (looked up once per device).
+constexpr int kMaxDevices = 64;
+size_t attn_static_scratch_bytes();
+hipError_t attn_static_scratch(void **ptr);
+
 // n_q queries per request, q / out [B][n_q][H_q][D]; n_q * G <= kMaxG
 hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q,
                        const uint16_t *kv_pool, int P, const int32_t *tbl_slot,

@@ -264,3 +264,17 @@ def test_timing_values_rejects_bad_arguments():
     lib = binding.library()
     n = ctypes.c_int32()
     assert lib.oasis_pipeline_timing_values(None, 0, None, 0, ctypes.byref(n)) == oa.OASIS_EINVAL
+
+
+def test_static_attention_scratch_limit_is_checked_on_the_host():
+    """The allocation-free attention entry point refuses split-K partials
+    larger than its fixed scratch before any device call (fake pointers are
+    never dereferenced)."""
+    assert L.oasis_sparse_decode_attn_static_bytes() == 8 << 20
+    dd = d(B=512, H_q=64, H_kv=4, NB_max=64)
+    p = ctypes.c_void_p(16)
+    assert L.oasis_sparse_decode_attn_static(ctypes.byref(dd), p, p, 64, p, p, p, 128, p, 0.1, p, None, 16,
+                                             None) == oa.OASIS_ENOSPACE
+    assert "fixed scratch" in oa.oasis_last_error()
+    assert L.oasis_sparse_decode_attn_static(ctypes.byref(dd), p, p, 0, p, p, p, 128, p, 0.1, p, None, 16,
+                                             None) == oa.OASIS_EINVAL
