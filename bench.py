@@ -50,8 +50,9 @@ def parse():
     p.add_argument("--copy-mode", choices=["kernel", "dma", "mixed"], default="kernel")
     p.add_argument("--host-threads", type=int, default=8, help="packing threads of the DMA copy engine")
     p.add_argument("--n-split", type=int, default=0)
-    p.add_argument("--compute-streams", type=int, default=0, choices=[0, 1, 2],
-                   help="streams for scores, top-K and plan (0 = the library's automatic choice)")
+    p.add_argument("--compute-streams", type=int, default=0, choices=[-1, 0, 1, 2],
+                   help="streams for scores, top-K and plan (0 = the library's automatic choice, "
+                        "-1 = the main stream, after each layer's attention)")
     p.add_argument("--joint", action="store_true",
                    help="look-ahead attention: the normal query and the step's J draft queries attend together")
     p.add_argument("--attn-sweep", action="store_true",

@@ -455,7 +455,9 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
  *   compute streams (owned)      scores and top-K of (l, t), staging plan;
  *                                without staging, even and odd layers
  *                                alternate two, so one layer's top-K
- *                                overlaps the next layer's scores
+ *                                overlaps the next layer's scores; or none:
+ *                                the main stream runs them after the
+ *                                layer's attention (compute_streams)
  *   copy streams (owned)         the copies of (l, t); the zero-copy engine
  *                                alternates two by layer so that one
  *                                layer's gather tail overlaps the next
@@ -527,20 +529,25 @@ typedef struct oasis_pipeline_desc {
     int32_t compute_streams;  /* streams for scores, top-K and the plan: 1,
                                  or 2 (even and odd layers alternate, so one
                                  layer's top-K overlaps the next layer's
-                                 scores); 0 = automatic: 2 when nothing is
-                                 staged or when B * H_kv is below the device's
-                                 compute-unit count (top-K and the plan run
-                                 one workgroup per (request, KV head) and
-                                 would leave most compute units idle), else 1.
-                                 Copy streams: OASIS_COPY_KERNEL with one
-                                 compute stream, two (even and odd layers),
-                                 so one gather's tail overlaps the next one's
-                                 start; OASIS_COPY_MIXED, two (the DMA layers
-                                 and the gather layers); otherwise one.  With
-                                 one compute stream that keeps to four
-                                 streams, the hardware queues of a process;
+                                 scores); -1: none, the chain runs on the
+                                 main stream after each layer's attention
+                                 (the kernels that read HBM never overlap
+                                 each other, only the copies); 0 =
+                                 automatic: 2 when nothing is staged or when
+                                 B * H_kv is below the device's compute-unit
+                                 count (top-K and the plan run one workgroup
+                                 per (request, KV head) and would leave most
+                                 compute units idle), else -1 (a staged step
+                                 with many pairs is bound by the link).
+                                 Copy streams: OASIS_COPY_KERNEL with at
+                                 most one compute stream, two (even and odd
+                                 layers), so one gather's tail overlaps the
+                                 next one's start; OASIS_COPY_MIXED, two
+                                 (the DMA layers and the gather layers);
+                                 otherwise one.  That keeps to four streams,
+                                 the hardware queues of a process, except
                                  two compute streams with the mixed engine
-                                 make five. */
+                                 (five). */
     int64_t *stage_stats;     /* optional, device int64[4]: every staging
                                  step of every layer adds its admits,
                                  evictions, deferred admits and 1 (see

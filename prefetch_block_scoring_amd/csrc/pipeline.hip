@@ -47,6 +47,7 @@ struct oasis_pipeline {
     int device = 0;
     int S = 0;
     hipStream_t main = nullptr, comp[2] = {nullptr, nullptr}, copy[2] = {nullptr, nullptr};
+    bool comp_on_main = false;  // compute_streams = -1: the chain runs on the main stream
     std::vector<hipEvent_t> ev;  // [kind][layer][kRing]
 
     // timing
@@ -212,8 +213,9 @@ void release(oasis_pipeline *p) {
     for (auto &v : p->t_ev)
         for (hipEvent_t e : v)
             if (e) (void)hipEventDestroy(e);
-    for (hipStream_t c : p->comp)
-        if (c) (void)hipStreamDestroy(c);
+    if (!p->comp_on_main)
+        for (hipStream_t c : p->comp)
+            if (c) (void)hipStreamDestroy(c);
     for (hipStream_t c : p->copy)
         if (c) (void)hipStreamDestroy(c);
     delete p;
@@ -239,8 +241,8 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
         PFAIL(OASIS_EINVAL, "copy_mode = %d", ds.copy_mode);
     if (!ds.pool || !ds.kminmax || !ds.ctx_len || !ds.layers) PFAIL(OASIS_EINVAL, "pool, kminmax, ctx_len or layers is NULL");
     if (ds.n_split < 0 || ds.n_split > 64) PFAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", ds.n_split);
-    if (ds.compute_streams < 0 || ds.compute_streams > 2)
-        PFAIL(OASIS_EINVAL, "compute_streams = %d outside [0, 2]", ds.compute_streams);
+    if (ds.compute_streams < -1 || ds.compute_streams > 2)
+        PFAIL(OASIS_EINVAL, "compute_streams = %d outside [-1, 2]", ds.compute_streams);
     int rc0 = check_dims(dims);
     if (rc0) return rc0;
     if ((int64_t)ds.n_q * (dims->H_q / dims->H_kv) > kMaxG)
@@ -273,12 +275,20 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     // layer's latency-bound top-K and plan overlap the next layer's scores.
     // That pays when those kernels leave compute units idle: always without
     // staging, and with staging when there are fewer (request, KV head)
-    // pairs than compute units.  With more pairs a staged step is bound by
-    // the link, and the hardware queue is worth more to a second gather
-    // stream (the 32B-class ragged layer, 128 pairs: 104k -> 160k tok/s with
-    // two; the Qwen3-8B layer at batch 128, 1024 pairs: 159k -> 151k).
+    // pairs than compute units (the 32B-class ragged layer, 128 pairs: 104k
+    // -> 160k tok/s with two).  With more pairs a staged step is bound by the
+    // link: the chain then runs on the main stream behind each attention
+    // (compute_streams = -1), so the kernels that read HBM never run beside
+    // one another, only beside the copies, and the hardware queues go to two
+    // gather streams (the Qwen3-8B layer at batch 128, 1024 pairs: 160.3k
+    // tok/s, attention 484 us live, against 159.7k and 750 us with its own
+    // compute stream, whose score kernel then takes HBM bandwidth from it).
     int n_comp = ds.compute_streams;
-    if (n_comp == 0) n_comp = (!ds.staged || (int64_t)dims->B * dims->H_kv < device_cu_count()) ? 2 : 1;
+    if (n_comp == 0) n_comp = (!ds.staged || (int64_t)dims->B * dims->H_kv < device_cu_count()) ? 2 : -1;
+    if (n_comp < 0) {
+        p->comp_on_main = true;
+        p->comp[0] = p->main;
+    }
     for (int c = 0; c < n_comp; c++)
         if ((e = hipStreamCreateWithFlags(&p->comp[c], hipStreamNonBlocking)) != hipSuccess)
             return fail(e, "hipStreamCreateWithFlags");
@@ -290,7 +300,7 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     // DMA layers and one for the gather layers.
     const int n_copy = !ds.staged                           ? 0
                        : ds.copy_mode == OASIS_COPY_MIXED    ? 2
-                       : ds.copy_mode == OASIS_COPY_KERNEL && n_comp == 1 ? 2
+                       : ds.copy_mode == OASIS_COPY_KERNEL && n_comp <= 1 ? 2
                                                               : 1;
     for (int c = 0; c < n_copy; c++)
         if ((e = hipStreamCreateWithFlags(&p->copy[c], hipStreamNonBlocking)) != hipSuccess)

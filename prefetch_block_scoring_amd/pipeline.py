@@ -12,7 +12,8 @@ lays that out on one GPU's streams:
   compute stream  scores and top-K of (l, t), then the staging plan of (l, t)
                   (two streams by layer parity when nothing is staged or
                   when there are fewer (request, KV head) pairs than compute
-                  units; `compute_streams` overrides)
+                  units; otherwise the main stream itself, behind each
+                  attention; `compute_streams` overrides)
   copy streams    the copies of (l, t) (gather kernels, on two streams by
                   layer parity when there is one compute stream, or DMA
                   copy + scatter on the pipeline's worker thread, or, mixed,
@@ -138,10 +139,14 @@ class LayerPipeline:
             layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)), compute_streams=compute_streams,
             stage_stats=self.stats.data_ptr() if staged else None)
         self._h = oa.oasis_pipeline_create(oa.dims(B, H_q, H_kv, NB, D, bs), desc)
-        self.comp = torch.cuda.ExternalStream(oa.oasis_pipeline_stream(self._h, 1))
+        c1 = oa.oasis_pipeline_stream(self._h, 1)
         odd = oa.oasis_pipeline_stream(self._h, 4)
+        # -1: the chain shares the main stream (whose handle is NULL when it
+        # is the default stream)
+        on_main = c1 == self.main.cuda_stream or not c1
+        self.comp = self.main if on_main else torch.cuda.ExternalStream(c1)
         self._comp_odd = torch.cuda.ExternalStream(odd) if odd else self.comp
-        self.compute_streams = 2 if odd else 1
+        self.compute_streams = -1 if on_main else (2 if odd else 1)
         self.copy = [torch.cuda.ExternalStream(c) for c in
                      (oa.oasis_pipeline_stream(self._h, k) for k in (2, 3)) if c]
 

@@ -394,7 +394,7 @@ def test_chain_end_to_end(name, B, ctx, copy_mode):
 
 @pytest.mark.parametrize("copy_mode,joint,compute_streams",
                          [(0, False, 0), (1, False, 0), (0, True, 0), (0, False, 1), (1, False, 1),
-                          (2, False, 0), (2, False, 1)])
+                          (2, False, 0), (2, False, 1), (0, False, -1), (1, False, -1)])
 def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams):
     """Three layers in flight on separate streams (the schedule the benchmark
     times): every layer's attention output at every step equals the oracle
@@ -402,7 +402,8 @@ def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams):
     normal query and the step's draft queries (n_q = 1 + J), each query
     against the oracle's attention for it alone.  compute_streams 0 is the
     automatic choice (two here: 16 (request, KV head) pairs); 1 puts every
-    layer's scores, top-K and plan on one stream beside two copy streams.
+    layer's scores, top-K and plan on one stream beside two copy streams;
+    -1 runs them on the main stream after each layer's attention.
     copy_mode 2 (mixed): layers 0 and 2 stage through the DMA engine, layer 1
     through the gather kernel."""
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
