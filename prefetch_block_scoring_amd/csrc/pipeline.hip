@@ -8,14 +8,13 @@
 // schedule through the library's own entry points, so a decode step costs a
 // few microseconds of host time per layer instead of a round of interpreter
 // calls per launch.  The dependency rules are stated in include/oasis.h.
+#include "copy_queue.h"
 #include "oasis_internal.h"
 
 #include <chrono>
-#include <condition_variable>
 #include <cstdio>
-#include <deque>
 #include <mutex>
-#include <thread>
+#include <string>
 #include <vector>
 
 namespace oasis {
@@ -59,15 +58,8 @@ struct oasis_pipeline {
     int copy_calls = 0;
     std::mutex t_mu;  // copy-host totals (written by the worker)
 
-    // DMA worker
-    std::thread worker;
-    std::mutex mu;
-    std::condition_variable cv_job, cv_done;
-    std::deque<Job> jobs;
-    std::vector<long> done;  // per layer: last step whose copies are enqueued
-    bool stop = false;
-    int err = OASIS_OK;
-    std::string err_msg;
+    // DMA worker: runs the copy halves in submission order
+    CopyQueue<Job> copies;
 
     hipEvent_t event(int kind, int l, int t) const {
         return ev[((size_t)kind * desc.n_layers + l) * kRing + (t % kRing)];
@@ -108,44 +100,11 @@ int run_copy(oasis_pipeline *p, const Job &j) {
     return rc;
 }
 
-void worker_loop(oasis_pipeline *p) {
-    (void)hipSetDevice(p->device);
-    for (;;) {
-        Job j;
-        {
-            std::unique_lock<std::mutex> lk(p->mu);
-            p->cv_job.wait(lk, [&] { return p->stop || !p->jobs.empty(); });
-            if (p->jobs.empty()) return;
-            j = p->jobs.front();
-        }
-        int rc = OASIS_OK;
-        std::string msg;
-        {
-            std::lock_guard<std::mutex> lk(p->mu);
-            rc = p->err;  // after an error, later copies are not issued
-        }
-        if (rc == OASIS_OK) {
-            rc = run_copy(p, j);
-            if (rc != OASIS_OK) msg = oasis_last_error();
-        }
-        {
-            std::lock_guard<std::mutex> lk(p->mu);
-            p->jobs.pop_front();
-            if (rc != OASIS_OK && p->err == OASIS_OK) {
-                p->err = rc;
-                p->err_msg = "staging copy of layer " + std::to_string(j.layer) + " step " +
-                             std::to_string(j.step) + ": " + msg;
-            }
-            p->done[j.layer] = j.step;
-        }
-        p->cv_done.notify_all();
-    }
-}
-
 int worker_error(oasis_pipeline *p) {
-    std::lock_guard<std::mutex> lk(p->mu);
-    if (p->err != OASIS_OK) set_error(p->err_msg);
-    return p->err;
+    std::string msg;
+    const int rc = p->copies.error(&msg);
+    if (rc != OASIS_OK) set_error(msg);
+    return rc;
 }
 
 // The copy engine of layer l's staging.
@@ -195,14 +154,7 @@ int check_layer(const oasis_pipeline_desc &ds, const oasis_layer_buffers &b, int
 }
 
 void release(oasis_pipeline *p) {
-    if (p->worker.joinable()) {
-        {
-            std::lock_guard<std::mutex> lk(p->mu);
-            p->stop = true;
-        }
-        p->cv_job.notify_all();
-        p->worker.join();
-    }
+    p->copies.stop();
     for (hipStream_t c : p->comp)
         if (c) (void)hipStreamSynchronize(c);
     for (hipStream_t c : p->copy)
@@ -261,7 +213,6 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     p->layers.assign(ds.layers, ds.layers + ds.n_layers);
     p->desc.layers = nullptr;
     p->next_step.assign(ds.n_layers, 0);
-    p->done.assign(ds.n_layers, -1);
     p->S = ds.K_b + (ds.staged ? ds.C : 0);
     p->main = static_cast<hipStream_t>(ds.main_stream);
     auto fail = [&](hipError_t e, const char *what) {
@@ -309,7 +260,18 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     for (auto &x : p->ev)
         if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess)
             return fail(e, "hipEventCreateWithFlags");
-    if (ds.staged && ds.copy_mode != OASIS_COPY_KERNEL) p->worker = std::thread(worker_loop, p);
+    if (ds.staged && ds.copy_mode != OASIS_COPY_KERNEL) {
+        p->copies.start(
+            ds.n_layers,
+            [p](const Job &j, std::string *msg) {
+                const int rc = run_copy(p, j);
+                if (rc != OASIS_OK)
+                    *msg = "staging copy of layer " + std::to_string(j.layer) + " step " + std::to_string(j.step) +
+                           ": " + oasis_last_error();
+                return rc;
+            },
+            [p] { (void)hipSetDevice(p->device); });
+    }
     *out = p;
     return OASIS_OK;
 }
@@ -334,10 +296,7 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     // foreground: attention of step t
     if (t >= 1) {
         if (ds.staged) {
-            if (mode == OASIS_COPY_DMA) {
-                std::unique_lock<std::mutex> lk(p->mu);
-                p->cv_done.wait(lk, [&] { return p->done[l] >= t - 1 || p->err != OASIS_OK; });
-            }
+            if (mode == OASIS_COPY_DMA) (void)p->copies.wait_done(l, t - 1);
             if ((rc = worker_error(p))) return rc;
             OASIS_HIP(hipStreamWaitEvent(p->main, p->event(kEvStage, l, t - 1), 0));
             const int k = t % 3;
@@ -421,11 +380,7 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     if ((rc = oasis_stage_plan(d, &a))) return rc;
     timed_end(p, 3, cs);
     if (mode == OASIS_COPY_DMA) {
-        {
-            std::lock_guard<std::mutex> lk(p->mu);
-            p->jobs.push_back(job);
-        }
-        p->cv_job.notify_one();
+        p->copies.push(job);
     } else if ((rc = run_copy(p, job))) {
         return rc;
     }
@@ -436,10 +391,7 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
 int oasis_pipeline_drain(oasis_pipeline *p) {
     clear_error();
     if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
-    {
-        std::unique_lock<std::mutex> lk(p->mu);
-        p->cv_done.wait(lk, [&] { return p->jobs.empty(); });
-    }
+    (void)p->copies.drain();
     return worker_error(p);
 }
 

@@ -13,12 +13,10 @@
 // DMA engines do not use the compute units or their memory path, so the
 // HBM-bound kernels of the same step keep their bandwidth.
 #include "oasis_internal.h"
+#include "worker_pool.h"
 
 #include <atomic>
-#include <condition_variable>
 #include <cstring>
-#include <functional>
-#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -28,85 +26,8 @@ namespace {
 
 // ------------------------------------------------------------ worker pool
 
-class Workers {
-  public:
-    ~Workers() {
-        {
-            std::lock_guard<std::mutex> lk(mu_);
-            stop_ = true;
-        }
-        cv_.notify_all();
-        for (auto &t : threads_) t.join();
-    }
-
-    // Run fn(i) for i in [0, n) on up to `want` threads, the caller included.
-    void run(int want, int n, const std::function<void(int)> &fn) {
-        if (n <= 0) return;
-        std::lock_guard<std::mutex> run_lk(run_mu_);  // one job at a time
-        if (want < 1) want = 1;
-        ensure(want - 1);
-        const int helpers = std::min<int>(want - 1, (int)threads_.size());
-        {
-            std::lock_guard<std::mutex> lk(mu_);
-            fn_ = &fn;
-            n_ = n;
-            next_.store(0);
-            active_ = helpers;
-            helpers_ = helpers;
-            gen_++;
-        }
-        cv_.notify_all();
-        drain();
-        std::unique_lock<std::mutex> lk(mu_);
-        done_cv_.wait(lk, [&] { return active_ == 0; });
-        fn_ = nullptr;
-    }
-
-  private:
-    void ensure(int k) {
-        std::lock_guard<std::mutex> lk(mu_);
-        while ((int)threads_.size() < k) {
-            const int id = (int)threads_.size();
-            threads_.emplace_back([this, id] { loop(id); });
-        }
-    }
-
-    void drain() {
-        for (int i = next_.fetch_add(1); i < n_; i = next_.fetch_add(1)) (*fn_)(i);
-    }
-
-    void loop(int id) {
-        uint64_t seen = 0;
-        for (;;) {
-            {
-                std::unique_lock<std::mutex> lk(mu_);
-                cv_.wait(lk, [&] { return stop_ || (gen_ != seen && id < helpers_); });
-                if (stop_) return;
-                seen = gen_;
-            }
-            drain();
-            {
-                std::lock_guard<std::mutex> lk(mu_);
-                if (--active_ == 0) done_cv_.notify_all();
-            }
-        }
-    }
-
-    std::mutex run_mu_;
-    std::mutex mu_;
-    std::condition_variable cv_, done_cv_;
-    std::vector<std::thread> threads_;
-    const std::function<void(int)> *fn_ = nullptr;
-    std::atomic<int> next_{0};
-    int n_ = 0;
-    int active_ = 0;
-    int helpers_ = 0;
-    uint64_t gen_ = 0;
-    bool stop_ = false;
-};
-
-Workers &workers() {
-    static Workers w;
+WorkerPool &workers() {
+    static WorkerPool w;
     return w;
 }
 
