@@ -59,5 +59,38 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_usage(names=("score.hip", "attn.hip", "topk.hip", "stage.hip")) -> str:
+    """The compiler's register, LDS, scratch and occupancy figures of each
+    kernel in the named sources (device pass only, nothing is written)."""
+    flags = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "--cuda-device-only",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE, "-I", CSRC, "-o", os.devnull, "-c"]
+    import re
+    keys = (("TotalSGPRs", "sgpr"), ("VGPRs", "vgpr"), ("AGPRs", "agpr"), ("ScratchSize [bytes/lane]", "scratch"),
+            ("Occupancy [waves/SIMD]", "waves/SIMD"), ("SGPRs Spill", "sgpr spill"),
+            ("VGPRs Spill", "vgpr spill"), ("LDS Size [bytes/block]", "LDS bytes"))
+    out = [f"{'source':11s} {'kernel':34s} " + " ".join(f"{lab:>10s}" for _, lab in keys)]
+    for name in names:
+        r = subprocess.run([hipcc()] + flags + [os.path.join(CSRC, name)], capture_output=True, text=True)
+        kern, vals = None, {}
+        for line in r.stderr.splitlines() + ["remark: Function Name: <end>"]:
+            if "remark:" not in line:
+                continue
+            body = line.split("remark:", 1)[1].split(" [-Rpass")[0].strip()
+            field, _, value = body.partition(": ")
+            if field == "Function Name":
+                if kern is not None:
+                    m = re.search(r"\d([a-z][a-z0-9_]*_kernel)(ILi(\d+)E)?", kern)
+                    label = (m.group(1) + (f"<{m.group(3)}>" if m.group(3) else "")) if m else kern
+                    out.append(f"{name:11s} {label:34s} " + " ".join(f"{vals.get(k, '-'):>10s}" for k, _ in keys))
+                kern, vals = value, {}
+            else:
+                vals[field] = value
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
+    if "--resource-usage" in sys.argv:
+        print(resource_usage())
+    else:
+        build(verbose="-q" not in sys.argv)
