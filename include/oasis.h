@@ -533,12 +533,15 @@ typedef struct oasis_pipeline_desc {
                                  main stream after each layer's attention
                                  (the kernels that read HBM never overlap
                                  each other, only the copies); 0 =
-                                 automatic: 2 when nothing is staged or when
-                                 B * H_kv is below the device's compute-unit
-                                 count (top-K and the plan run one workgroup
-                                 per (request, KV head) and would leave most
-                                 compute units idle), else -1 (a staged step
-                                 with many pairs is bound by the link).
+                                 automatic: -1 for a staged step that is
+                                 bound by the link (C blocks of 8 KiB at
+                                 57 GB/s take over 2.5 times as long as the
+                                 pair's K_b blocks and NB_max summaries of
+                                 512 B at 6 TB/s) and has at least as many
+                                 (request, KV head) pairs as the device has
+                                 compute units; else 2 (top-K and the plan
+                                 run one workgroup per pair and, with few
+                                 pairs, leave compute units idle).
                                  Copy streams: OASIS_COPY_KERNEL with at
                                  most one compute stream, two (even and odd
                                  layers), so one gather's tail overlaps the
