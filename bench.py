@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--compute-streams", type=int, default=0, choices=[-1, 0, 1, 2],
                    help="streams for scores, top-K and plan (0 = the library's automatic choice, "
                         "-1 = the main stream, after each layer's attention)")
+    p.add_argument("--issue-threads", type=int, default=0, choices=[-1, 0, 1],
+                   help="worker threads that enqueue each layer-step's chain and copies (0 = the library's "
+                        "automatic choice, 1 = on, -1 = off: the calling thread enqueues everything)")
     p.add_argument("--joint", action="store_true",
                    help="look-ahead attention: the normal query and the step's J draft queries attend together")
     p.add_argument("--attn-sweep", action="store_true",
@@ -493,7 +496,7 @@ def main():
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
     pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=H_q, K_b=K_b, C=C, n_layers=L, staged=staged,
                          copy_mode=copy_mode, host_threads=args.host_threads, n_split=args.n_split, J=w.J,
-                         n_q=n_q, compute_streams=args.compute_streams)
+                         n_q=n_q, compute_streams=args.compute_streams, issue_threads=args.issue_threads)
     T = K_b
     splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
 
@@ -767,6 +770,7 @@ def main():
                    "copy_engine": args.copy_mode if staged else None,
                    "host_threads": args.host_threads if staged and copy_mode != oa.OASIS_COPY_KERNEL else None,
                    "attn_splits": splits, "compute_streams": pipe.compute_streams,
+                   "issue_threads": pipe.issue_threads,
                    "copy_streams": len(pipe.copy) if staged else None},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -465,10 +465,13 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
  *
  * Per layer the buffers rotate: the attention of step t reads table t % 3,
  * the plan of step t writes table (t + 1) % 3 and uses selection and plan
- * buffer t % 2.  So the plan of step t waits for the attention and the copies
- * of step t - 2, and the copies of step t wait for the attention of step
- * t - 1, whose slots they may refill.  Unstaged pipelines (K/V in HBM)
- * attend at step t over the selection of step t - 1 in the full pool.  With
+ * buffer t % 2, and the copies of step t may refill slots that the
+ * attention of step t - 1 still reads.  So the top-K of step t waits for the
+ * attention of step t - 1, which itself waited for the copies of step t - 2
+ * (the last readers of plan buffer t % 2); the plan and the copies of step t
+ * follow that top-K, and the attention of step t waits for the copies of
+ * step t - 1.  Unstaged pipelines (K/V in HBM) attend at step t over the
+ * selection of step t - 1 in the full pool.  With
  * OASIS_COPY_DMA the copy half, which blocks on host packing, runs on one
  * worker thread owned by the pipeline, in submission order; with
  * OASIS_COPY_KERNEL it is enqueued by the calling thread.  Streams are
@@ -556,12 +559,26 @@ typedef struct oasis_pipeline_desc {
                                  evictions, deferred admits and 1 (see
                                  oasis_stage_args.stats_accum); the caller
                                  clears it */
+    int32_t issue_threads;    /* staged pipelines whose chain has compute
+                                 streams of its own: 0 or 1 = one worker
+                                 thread enqueues each layer-step's scores,
+                                 top-K and plan, another its copies, both
+                                 in submission order, and the calling
+                                 thread only the attention (a stream wait
+                                 on a pending event costs the enqueuing
+                                 thread 8-24 us, and a staged layer-step
+                                 needs three); -1 = the calling thread
+                                 enqueues everything.  Unstaged pipelines
+                                 and a chain on the main stream
+                                 (compute_streams = -1) always use the
+                                 calling thread. */
 } oasis_pipeline_desc;
 
 typedef struct oasis_pipeline oasis_pipeline;
 
 /* Checks the description, creates the compute and copy streams, the events
- * and (DMA) the worker thread; *out receives the handle. */
+ * and the worker threads (DMA copies; issue threads); *out receives the
+ * handle. */
 int oasis_pipeline_create(const oasis_dims *dims,
                           const oasis_pipeline_desc *desc,
                           oasis_pipeline **out);
@@ -580,8 +597,10 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t layer, int32_t step,
                               const uint16_t *q_look, const uint16_t *q_attn,
                               uint16_t *out, float *lse);
 
-/* Waits until the DMA worker has enqueued every submitted copy (no device
- * synchronisation). */
+/* Waits until the worker threads (DMA copies, issue threads) have enqueued
+ * everything submitted so far (no device synchronisation): after it, work
+ * the caller enqueues on a pipeline stream follows every earlier
+ * layer-step's work on that stream. */
 int oasis_pipeline_drain(oasis_pipeline *p);
 
 /* The pipeline's streams: which = 0 main, 1 compute (of even layers with

@@ -77,7 +77,7 @@ class oasis_pipeline_desc(ctypes.Structure):
         ("copy_mode", _I32),
         ("host_threads", _I32), ("n_split", _I32), ("sm_scale", ctypes.c_float), ("pool", _P),
         ("kminmax", _P), ("ctx_len", _P), ("main_stream", _P), ("layers", ctypes.POINTER(oasis_layer_buffers)),
-        ("compute_streams", _I32), ("stage_stats", _P)]
+        ("compute_streams", _I32), ("stage_stats", _P), ("issue_threads", _I32)]
 
 
 # name -> (restype, argtypes)

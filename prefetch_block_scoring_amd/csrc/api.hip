@@ -355,8 +355,8 @@ static int stage_copy_phase(const oasis_dims *dims, const oasis_stage_args *a, c
         OASIS_HIP(hipEventRecord(plan_ready, s));
     }
     if (a->copy_mode == OASIS_COPY_KERNEL) {
-        OASIS_HIP(hipStreamWaitEvent(cs, plan_ready, 0));
-        if (a->wait_event) OASIS_HIP(hipStreamWaitEvent(cs, static_cast<hipEvent_t>(a->wait_event), 0));
+        OASIS_HIP(stream_wait(cs, plan_ready));
+        if (a->wait_event) OASIS_HIP(stream_wait(cs, static_cast<hipEvent_t>(a->wait_event)));
         OASIS_HIP(launch_stage_gather(*dims, *a, pool_dev, cs));
     } else {
         if ((rc = stage_dma(*dims, *a, plan_ready, cs))) return rc;

@@ -1,13 +1,16 @@
-// An in-order queue of staging copies served by one host thread.
+// An in-order queue of jobs served by one host thread.
 //
-// With the DMA copy engine, the copy half of a layer's staging step blocks
-// its thread (plan read-back, packing, the memcpy), so the layer pipeline
-// hands it to this worker and goes on issuing the next layers (OasisKV,
-// paperlayer summary, section 4: the per-layer chain runs in the background,
-// the foreground waits only for the copies its own attention needs).  Jobs
-// run in submission order; after the first failure the rest are dropped and
-// every waiter returns.  Plain C++ (no HIP), so that the same code is built
-// and checked under ThreadSanitizer on a machine with no GPU.
+// The layer pipeline hands work that would hold up the thread enqueuing a
+// layer's attention to such workers: the copy half of a staging step (with
+// the DMA engine it blocks on the plan read-back, the packing and the
+// memcpy) and, for layers with few (request, KV head) pairs, the whole
+// background chain, whose cross-stream waits cost the enqueuing thread
+// microseconds each (OasisKV, paperlayer summary, section 4: the per-layer
+// chain runs in the background, the foreground waits only for what its own
+// attention needs).  Jobs run in submission order; after the first failure
+// the rest are dropped and every waiter returns.  Plain C++ (no HIP), so
+// that the same code is built and checked under ThreadSanitizer on a
+// machine with no GPU.
 #pragma once
 
 #include <condition_variable>
@@ -57,6 +60,7 @@ class CopyQueue {
     // run, or a job has failed.  Returns the first error code (0 if none).
     int wait_done(int layer, int step) {
         std::unique_lock<std::mutex> lk(mu_);
+        if (layer < 0 || layer >= (int)done_.size()) return err_;  // not started, or no such layer
         cv_done_.wait(lk, [&] { return done_[layer] >= step || err_ != 0; });
         return err_;
     }
@@ -66,6 +70,19 @@ class CopyQueue {
         std::unique_lock<std::mutex> lk(mu_);
         cv_done_.wait(lk, [&] { return jobs_.empty(); });
         return err_;
+    }
+
+    // Record a failure from outside the queue (unless one is recorded):
+    // later jobs are dropped and every waiter returns.
+    void fail(int code, const std::string &msg) {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            if (err_ == 0) {
+                err_ = code;
+                err_msg_ = msg;
+            }
+        }
+        cv_done_.notify_all();
     }
 
     // The first error code (0 if none) and its message.

@@ -124,6 +124,11 @@ int stage_dma(const oasis_dims &d, const oasis_stage_args &a, hipEvent_t plan_re
 // per-thread ring of ordering events on the current device
 int ring_event(hipEvent_t *ev);
 
+// Make stream s wait for event e unless e has already completed (or was never
+// recorded).  A wait on a pending event costs the calling thread 8-24 us, and
+// its barrier packet delays the stream even when the event is done by then.
+hipError_t stream_wait(hipStream_t s, hipEvent_t e);
+
 // Map every page of a fresh pinned host allocation into the process (one
 // write per page, on the worker threads) so that later CPU accesses, such as
 // the DMA engine's packing, do not take a page fault per new page.

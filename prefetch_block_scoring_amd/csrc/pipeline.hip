@@ -40,6 +40,13 @@ struct Job {
     oasis_stage_args args{};
 };
 
+// The background half of one layer-step: scores, top-K and staging plan
+// from the lookahead queries (and the copies that follow).
+struct ChainJob {
+    int layer = 0, step = 0;
+    const uint16_t *q_look = nullptr;
+};
+
 }  // namespace
 }  // namespace oasis
 
@@ -65,8 +72,11 @@ struct oasis_pipeline {
     int copy_calls = 0;
     std::mutex t_mu;  // copy-host totals (written by the worker)
 
-    // DMA worker: runs the copy halves in submission order
+    // worker threads, each in submission order: the copy halves (DMA engine,
+    // or any engine when `threaded`), and with `threaded` the chain halves
+    bool threaded = false;
     CopyQueue<Job> copies;
+    CopyQueue<ChainJob> chain;
 
     hipEvent_t event(int kind, int l, int t) const {
         return ev[((size_t)kind * desc.n_layers + l) * kRing + (t % kRing)];
@@ -109,7 +119,8 @@ int run_copy(oasis_pipeline *p, const Job &j) {
 
 int worker_error(oasis_pipeline *p) {
     std::string msg;
-    const int rc = p->copies.error(&msg);
+    int rc = p->chain.error(&msg);
+    if (rc == OASIS_OK) rc = p->copies.error(&msg);
     if (rc != OASIS_OK) set_error(msg);
     return rc;
 }
@@ -161,6 +172,7 @@ int check_layer(const oasis_pipeline_desc &ds, const oasis_layer_buffers &b, int
 }
 
 void release(oasis_pipeline *p) {
+    p->chain.stop();  // its last jobs may still hand copies on
     p->copies.stop();
     for (hipStream_t c : p->comp)
         if (c) (void)hipStreamSynchronize(c);
@@ -184,6 +196,8 @@ void release(oasis_pipeline *p) {
 
 extern "C" {
 
+static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look);
+
 int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *desc, oasis_pipeline **out) {
     clear_error();
     if (!out) PFAIL(OASIS_EINVAL, "out is NULL");
@@ -200,6 +214,8 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
         PFAIL(OASIS_EINVAL, "copy_mode = %d", ds.copy_mode);
     if (!ds.pool || !ds.kminmax || !ds.ctx_len || !ds.layers) PFAIL(OASIS_EINVAL, "pool, kminmax, ctx_len or layers is NULL");
     if (ds.n_split < 0 || ds.n_split > 64) PFAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", ds.n_split);
+    if (ds.issue_threads < -1 || ds.issue_threads > 1)
+        PFAIL(OASIS_EINVAL, "issue_threads = %d outside [-1, 1]", ds.issue_threads);
     if (ds.compute_streams < -1 || ds.compute_streams > 2)
         PFAIL(OASIS_EINVAL, "compute_streams = %d outside [-1, 2]", ds.compute_streams);
     int rc0 = check_dims(dims);
@@ -277,7 +293,29 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     for (auto &x : p->ev)
         if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess)
             return fail(e, "hipEventCreateWithFlags");
-    if (ds.staged && ds.copy_mode != OASIS_COPY_KERNEL) {
+    // issue threads: the chain and the copies are enqueued by two worker
+    // threads of their own, so that the calling thread enqueues only the
+    // attention.  A stream wait on an event that is still pending costs the
+    // thread that enqueues it 8 to 24 us on MI355X (ROCm 7.2), and a staged
+    // layer-step makes three of them (for the attention, before the top-K,
+    // before the copies): with all of them on the calling thread, a layer with
+    // few (request, KV head) pairs is bound by that thread.
+    p->threaded = ds.staged && !p->comp_on_main && ds.issue_threads >= 0;
+    if (p->threaded) {
+        p->chain.start(
+            ds.n_layers,
+            [p](const ChainJob &j, std::string *msg) {
+                const int rc = issue_chain(p, j.layer, j.step, j.q_look);
+                if (rc != OASIS_OK) {
+                    *msg = "scores, top-K or plan of layer " + std::to_string(j.layer) + " step " +
+                           std::to_string(j.step) + ": " + oasis_last_error();
+                    p->copies.fail(rc, *msg);  // its copies never come: release whoever waits for them
+                }
+                return rc;
+            },
+            [p] { (void)hipSetDevice(p->device); });
+    }
+    if (ds.staged && (ds.copy_mode != OASIS_COPY_KERNEL || p->threaded)) {
         p->copies.start(
             ds.n_layers,
             [p](const Job &j, std::string *msg) {
@@ -293,66 +331,38 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     return OASIS_OK;
 }
 
-int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uint16_t *q_look,
-                              const uint16_t *q_attn, uint16_t *out, float *lse) {
-    clear_error();
-    if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
+// The background half of layer-step (l, t): scores, top-K and (staged) the
+// staging plan for step t + 1 from the lookahead queries, then the copies
+// (handed to the copy worker when there is one).  Runs on the calling thread,
+// or on the chain worker in submission order.
+static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look) {
     const oasis_pipeline_desc &ds = p->desc;
-    if (l < 0 || l >= ds.n_layers) PFAIL(OASIS_EINVAL, "layer = %d outside [0, %d)", l, ds.n_layers);
-    if (t != p->next_step[l]) PFAIL(OASIS_EINVAL, "layer %d: step %d issued, step %d expected", l, t, p->next_step[l]);
-    if (!q_look) PFAIL(OASIS_EINVAL, "q_look is NULL");
-    if (t >= 1 && (!q_attn || !out)) PFAIL(OASIS_EINVAL, "q_attn or out is NULL at step %d", t);
-    int rc;
-    if ((rc = worker_error(p))) return rc;
     const oasis_layer_buffers &b = p->layers[l];
     const oasis_dims *d = &p->d;
     const int K_b = ds.K_b;
     const int j = t % 2;
     const int mode = layer_copy_mode(ds, l);
-
-    // foreground: attention of step t
-    if (t >= 1) {
-        if (ds.staged) {
-            if (mode == OASIS_COPY_DMA) (void)p->copies.wait_done(l, t - 1);
-            if ((rc = worker_error(p))) return rc;
-            OASIS_HIP(hipStreamWaitEvent(p->main, p->event(kEvStage, l, t - 1), 0));
-            const int k = t % 3;
-            timed_begin(p, 0, p->main);
-            rc = oasis_lookahead_attn(d, ds.n_q, q_attn, b.ws_pool, p->S, b.tbl_slot[k], b.tbl_block[k],
-                                      b.tbl_n[k], K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws,
-                                      b.attn_ws_bytes, ds.n_split, p->main);
-        } else {
-            const int jp = (t - 1) % 2;
-            OASIS_HIP(hipStreamWaitEvent(p->main, p->event(kEvSel, l, t - 1), 0));
-            timed_begin(p, 0, p->main);
-            rc = oasis_lookahead_attn(d, ds.n_q, q_attn, ds.pool, d->NB_max, b.sel[jp], b.sel[jp], b.n_sel[jp],
-                                      K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes,
-                                      ds.n_split, p->main);
-        }
-        if (rc) return rc;
-        timed_end(p, 0, p->main);
-        OASIS_HIP(hipEventRecord(p->event(kEvAttn, l, t), p->main));
-    }
-
-    // background: prediction and staging plan for step t + 1
+    int rc;
     hipStream_t cs = p->comp[p->comp[1] ? (l & 1) : 0];
     timed_begin(p, 1, cs);
     if ((rc = oasis_score_blocks(d, q_look, ds.J, ds.kminmax, ds.ctx_len, b.scores, cs))) return rc;
     timed_end(p, 1, cs);
     if (t >= 2) {
-        // sel[j] (unstaged: read by the attention of step t - 1) and table
-        // (t + 1) % 3 (staged: read by the attention of step t - 2)
-        OASIS_HIP(hipStreamWaitEvent(cs, p->event(kEvAttn, l, ds.staged ? t - 2 : t - 1), 0));
+        // unstaged: sel[j], read by the attention of step t - 1.  Staged: the
+        // attention of step t - 1 covers every later reuse: table
+        // (t + 1) % 3 (read by the attention of step t - 2, earlier on the
+        // main stream), plan[j] (read by the copies of step t - 2, which
+        // that attention waited for) and the slots this step's copies may
+        // refill (read by that attention itself)
+        OASIS_HIP(stream_wait(cs, p->event(kEvAttn, l, t - 1)));
     }
     timed_begin(p, 2, cs);
     if ((rc = oasis_select_topk(d, b.scores, ds.ctx_len, K_b, b.sel[j], b.n_sel[j], cs))) return rc;
     timed_end(p, 2, cs);
     if (!ds.staged) {
         OASIS_HIP(hipEventRecord(p->event(kEvSel, l, t), cs));
-        p->next_step[l] = t + 1;
         return OASIS_OK;
     }
-    if (t >= 2) OASIS_HIP(hipStreamWaitEvent(cs, p->event(kEvStage, l, t - 2), 0));  // plan[j]'s last reader
 
     Job job;
     job.layer = l;
@@ -389,25 +399,75 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     // mixed: copy[0] carries the DMA (even) layers, copy[1] the gathers (odd);
     // otherwise the layers alternate over the copy streams there are
     a.copy_stream = p->copy[p->copy[1] ? (l & 1) : 0];
-    a.wait_event = t >= 1 ? p->event(kEvAttn, l, t - 1) : nullptr;
+    // the copies follow the plan, which followed the attention of step t - 1
+    a.wait_event = nullptr;
     a.done_event = p->event(kEvStage, l, t);
     a.plan_event = p->event(kEvPlan, l, t);
     a.stats_accum = ds.stage_stats;
     timed_begin(p, 3, cs);
     if ((rc = oasis_stage_plan(d, &a))) return rc;
     timed_end(p, 3, cs);
-    if (mode == OASIS_COPY_DMA) {
+    if (mode == OASIS_COPY_DMA || p->threaded) {
         p->copies.push(job);
     } else if ((rc = run_copy(p, job))) {
         return rc;
     }
-    p->next_step[l] = t + 1;
     return OASIS_OK;
+}
+
+int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uint16_t *q_look,
+                              const uint16_t *q_attn, uint16_t *out, float *lse) {
+    clear_error();
+    if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
+    const oasis_pipeline_desc &ds = p->desc;
+    if (l < 0 || l >= ds.n_layers) PFAIL(OASIS_EINVAL, "layer = %d outside [0, %d)", l, ds.n_layers);
+    if (t != p->next_step[l]) PFAIL(OASIS_EINVAL, "layer %d: step %d issued, step %d expected", l, t, p->next_step[l]);
+    if (!q_look) PFAIL(OASIS_EINVAL, "q_look is NULL");
+    if (t >= 1 && (!q_attn || !out)) PFAIL(OASIS_EINVAL, "q_attn or out is NULL at step %d", t);
+    int rc;
+    if ((rc = worker_error(p))) return rc;
+    const oasis_layer_buffers &b = p->layers[l];
+    const oasis_dims *d = &p->d;
+    const int K_b = ds.K_b;
+    const int mode = layer_copy_mode(ds, l);
+
+    // foreground: attention of step t
+    if (t >= 1) {
+        if (ds.staged) {
+            // the copy worker has recorded the copies of step t - 1
+            if (mode == OASIS_COPY_DMA || p->threaded) (void)p->copies.wait_done(l, t - 1);
+            if ((rc = worker_error(p))) return rc;
+            OASIS_HIP(stream_wait(p->main, p->event(kEvStage, l, t - 1)));
+            const int k = t % 3;
+            timed_begin(p, 0, p->main);
+            rc = oasis_lookahead_attn(d, ds.n_q, q_attn, b.ws_pool, p->S, b.tbl_slot[k], b.tbl_block[k],
+                                      b.tbl_n[k], K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws,
+                                      b.attn_ws_bytes, ds.n_split, p->main);
+        } else {
+            const int jp = (t - 1) % 2;
+            OASIS_HIP(stream_wait(p->main, p->event(kEvSel, l, t - 1)));
+            timed_begin(p, 0, p->main);
+            rc = oasis_lookahead_attn(d, ds.n_q, q_attn, ds.pool, d->NB_max, b.sel[jp], b.sel[jp], b.n_sel[jp],
+                                      K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes,
+                                      ds.n_split, p->main);
+        }
+        if (rc) return rc;
+        timed_end(p, 0, p->main);
+        OASIS_HIP(hipEventRecord(p->event(kEvAttn, l, t), p->main));
+    }
+
+    p->next_step[l] = t + 1;
+    if (p->threaded) {
+        p->chain.push(ChainJob{l, t, q_look});
+        return OASIS_OK;
+    }
+    return issue_chain(p, l, t, q_look);
 }
 
 int oasis_pipeline_drain(oasis_pipeline *p) {
     clear_error();
     if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
+    (void)p->chain.drain();  // before the copies: its jobs hand copies on
     (void)p->copies.drain();
     return worker_error(p);
 }

@@ -143,6 +143,13 @@ int ring_event(hipEvent_t *ev) {
     return OASIS_OK;
 }
 
+hipError_t stream_wait(hipStream_t s, hipEvent_t e) {
+    const hipError_t q = hipEventQuery(e);
+    if (q == hipSuccess) return hipSuccess;
+    if (q != hipErrorNotReady) return q;
+    return hipStreamWaitEvent(s, e, 0);
+}
+
 int stage_dma(const oasis_dims &d, const oasis_stage_args &a, hipEvent_t plan_ready, hipStream_t cs) {
     const int pairs = d.B * d.H_kv;
     const int row = plan_row(a.C);
@@ -208,7 +215,7 @@ int stage_dma(const oasis_dims &d, const oasis_stage_args &a, hipEvent_t plan_re
                                  hipMemcpyHostToDevice, cs));
         if (!waited && a.wait_event) {
             // only the scatter touches working-set slots
-            OASIS_HIP(hipStreamWaitEvent(cs, static_cast<hipEvent_t>(a.wait_event), 0));
+            OASIS_HIP(stream_wait(cs, static_cast<hipEvent_t>(a.wait_event)));
             waited = true;
         }
         OASIS_HIP(launch_stage_scatter(d, a, lo, hi, cs));

@@ -108,7 +108,7 @@ class LayerPipeline:
 
     def __init__(self, *, pool, summ, ctx, H_q: int, K_b: int, C: int, n_layers: int, staged: bool,
                  copy_mode: int = oa.OASIS_COPY_KERNEL, host_threads: int = 8, n_split: int = 0, J: int = 1,
-                 n_q: int = 1, compute_streams: int = 0):
+                 n_q: int = 1, compute_streams: int = 0, issue_threads: int = 0):
         B, H_kv, NB, _, bs, D = pool.shape
         if tuple(summ.shape) != (B, H_kv, NB, 2, D) or summ.dtype != torch.bfloat16 or not summ.is_cuda:
             raise ValueError(f"summ: expected bf16 device [B][H_kv][NB_max][2][D] = {(B, H_kv, NB, 2, D)}, "
@@ -137,6 +137,7 @@ class LayerPipeline:
             host_threads=host_threads, n_split=n_split, sm_scale=1.0 / math.sqrt(D), pool=pool.data_ptr(),
             kminmax=summ.data_ptr(), ctx_len=ctx.data_ptr(), main_stream=self.main.cuda_stream,
             layers=ctypes.cast(bufs, ctypes.POINTER(oa.oasis_layer_buffers)), compute_streams=compute_streams,
+            issue_threads=issue_threads,
             stage_stats=self.stats.data_ptr() if staged else None)
         self._h = oa.oasis_pipeline_create(oa.dims(B, H_q, H_kv, NB, D, bs), desc)
         c1 = oa.oasis_pipeline_stream(self._h, 1)
@@ -147,6 +148,9 @@ class LayerPipeline:
         self.comp = self.main if on_main else torch.cuda.ExternalStream(c1)
         self._comp_odd = torch.cuda.ExternalStream(odd) if odd else self.comp
         self.compute_streams = -1 if on_main else (2 if odd else 1)
+        # whether worker threads enqueue the chain and the copies (the
+        # library's rule for issue_threads)
+        self.issue_threads = bool(staged and not on_main and issue_threads >= 0)
         self.copy = [torch.cuda.ExternalStream(c) for c in
                      (oa.oasis_pipeline_stream(self._h, k) for k in (2, 3)) if c]
 
@@ -217,6 +221,8 @@ class LayerPipeline:
         return oa.oasis_pipeline_copy_host_seconds(self._h)
 
     def drain(self):
+        """Returns once the worker threads have enqueued every layer-step
+        submitted so far (no device synchronisation)."""
         oa.oasis_pipeline_drain(self._h)
 
     def close(self):

@@ -194,6 +194,8 @@ def _pipeline_desc(L=2, staged=1, copy_mode=0, **kw):
     ({"n_split": 65}, oa.OASIS_EINVAL),
     ({"compute_streams": 3}, oa.OASIS_EINVAL),
     ({"compute_streams": -2}, oa.OASIS_EINVAL),
+    ({"issue_threads": 2}, oa.OASIS_EINVAL),
+    ({"issue_threads": -2}, oa.OASIS_EINVAL),
     ({"n_q": 0}, oa.OASIS_EINVAL),
     ({"n_q": 5}, oa.OASIS_EUNSUPPORTED),     # 5 queries x 4 heads > 16 columns
 ])

@@ -70,10 +70,12 @@ def run_gpu(w, copy_mode, rs):
         for l in range(LAYERS):
             s = t + PHASE * l
             pipe.layer_step(l, t, q_look[s], q_attn[s])
+            # the issue threads have enqueued this layer-step's chain (no
+            # device wait: the streams keep running ahead of each other)
+            pipe.drain()
             ly = pipe.layers[l]
             snap = {}
-            # stream-ordered snapshots of the sampled requests; no host wait,
-            # so the streams keep running ahead of each other as in the bench
+            # stream-ordered snapshots of the sampled requests
             with torch.cuda.stream(pipe.comp_stream(l)):
                 snap["scores"] = ly.scores.index_select(0, idx)
                 snap["sel"] = ly.sel[t % 2].index_select(0, idx)

@@ -392,10 +392,11 @@ def test_chain_end_to_end(name, B, ctx, copy_mode):
 # ---------------------------------------------------------------- pipelined layers
 
 
-@pytest.mark.parametrize("copy_mode,joint,compute_streams",
-                         [(0, False, 0), (1, False, 0), (0, True, 0), (0, False, 1), (1, False, 1),
-                          (2, False, 0), (2, False, 1), (0, False, -1), (1, False, -1)])
-def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams):
+@pytest.mark.parametrize("copy_mode,joint,compute_streams,issue_threads",
+                         [(0, False, 0, 0), (1, False, 0, 0), (0, True, 0, 0), (0, False, 1, 0), (1, False, 1, 0),
+                          (2, False, 0, 0), (2, False, 1, 0), (0, False, -1, 0), (1, False, -1, 0),
+                          (0, False, 0, -1), (1, False, 0, -1), (2, False, 0, -1)])
+def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams, issue_threads):
     """Three layers in flight on separate streams (the schedule the benchmark
     times): every layer's attention output at every step equals the oracle
     chain run serially for that layer.  joint: look-ahead attention of the
@@ -404,6 +405,8 @@ def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams):
     automatic choice (two here: 16 (request, KV head) pairs); 1 puts every
     layer's scores, top-K and plan on one stream beside two copy streams;
     -1 runs them on the main stream after each layer's attention.
+    issue_threads 0: with compute streams of their own, worker threads
+    enqueue the chain and the copies; -1: the calling thread enqueues all.
     copy_mode 2 (mixed): layers 0 and 2 stage through the DMA engine, layer 1
     through the gather kernel."""
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
@@ -422,8 +425,10 @@ def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams):
         attn_q = [torch.cat([attn_q[s][:, None], looks[s]], dim=1).contiguous() for s in range(steps + 2 * L)]
     n_q = 1 + w.J if joint else 1
     pipe = LayerPipeline(pool=host, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=True, J=w.J,
-                         copy_mode=copy_mode, host_threads=4, n_q=n_q, compute_streams=compute_streams)
+                         copy_mode=copy_mode, host_threads=4, n_q=n_q, compute_streams=compute_streams,
+                         issue_threads=issue_threads)
     assert pipe.compute_streams == (compute_streams or 2)
+    assert pipe.issue_threads == (compute_streams != -1 and issue_threads == 0)
     outs = {}
     for t in range(steps):
         for l in range(L):

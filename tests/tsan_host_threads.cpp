@@ -11,7 +11,9 @@
 //   issues layer-steps in the pipeline's order, waits for step t - 1 of a
 //   layer before reading what that job wrote (plain memory again), drains,
 //   and in a second round one job fails: later jobs must not run, every
-//   waiter must return, and the first error must be the one reported.
+//   waiter must return, and the first error must be the one reported.  Two
+//   queues chained as the pipeline's issue threads chain them: a failure in
+//   the first releases the producer waiting on the second.
 //
 // Exit status 0 when every check holds; ThreadSanitizer itself exits with 66
 // when it reported anything.
@@ -141,6 +143,56 @@ static void queue_stop_with_pending() {
     CHECK(n.load() == 50);
 }
 
+// The layer pipeline's issue threads: the producer enqueues each
+// layer-step's chain job on one queue, whose runner hands a copy job on to a
+// second queue; before the job of (layer, t) the producer waits until the
+// copy of (layer, t - 1) has run.  A chain job that fails marks the copy
+// queue failed, so that the producer's wait returns.
+static void two_queue_handoff(int layers, int steps, int fail_layer, int fail_step) {
+    oasis::CopyQueue<Job> copies, chain;
+    std::vector<std::vector<long>> issued(layers, std::vector<long>(steps, -1));  // written by the copy worker
+    copies.start(layers, [&](const Job &j, std::string *) {
+        issued[j.layer][j.step] = 7L * j.layer + j.step;
+        return 0;
+    });
+    chain.start(layers, [&](const Job &j, std::string *msg) {
+        if (j.layer == fail_layer && j.step == fail_step) {
+            *msg = "chain failed";
+            copies.fail(5, *msg);
+            return 5;
+        }
+        copies.push(j);
+        return 0;
+    });
+    bool stopped = false;
+    for (int t = 0; t < steps && !stopped; t++) {
+        for (int l = 0; l < layers; l++) {
+            if (t >= 1) {
+                if (copies.wait_done(l, t - 1) != 0) {
+                    stopped = true;
+                    break;
+                }
+                CHECK(issued[l][t - 1] == 7L * l + t - 1);
+            }
+            chain.push(Job{l, t});
+        }
+    }
+    (void)chain.drain();
+    (void)copies.drain();
+    std::string msg;
+    if (fail_layer < 0) {
+        CHECK(!stopped && chain.error(&msg) == 0 && copies.error(&msg) == 0);
+        for (int l = 0; l < layers; l++)
+            for (int t = 0; t < steps; t++) CHECK(issued[l][t] == 7L * l + t);
+    } else {
+        CHECK(stopped);
+        CHECK(chain.error(&msg) == 5 && msg == "chain failed");
+        CHECK(copies.error(&msg) == 5);
+    }
+    chain.stop();
+    copies.stop();
+}
+
 int main() {
     pool_stress();
     for (int rep = 0; rep < 20; rep++) queue_round(4, 40, -1, -1);
@@ -148,6 +200,9 @@ int main() {
     queue_round(3, 10, 0, 1);
     queue_round(1, 5, 0, 4);
     queue_stop_with_pending();
+    for (int rep = 0; rep < 10; rep++) two_queue_handoff(4, 30, -1, -1);
+    two_queue_handoff(4, 30, 1, 9);
+    two_queue_handoff(2, 5, 0, 0);
     std::printf("host threads: all checks passed\n");
     return 0;
 }
