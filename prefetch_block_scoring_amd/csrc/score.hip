@@ -29,8 +29,10 @@
 // load instruction reads four consecutive blocks' halves, 1 KiB in whole
 // 128-byte lines, and a lane keeps only 16 of the 256 Qp / Qm values (32
 // registers).  The sixteen partial sums meet through four DPP steps.  A wave
-// owns 16 consecutive blocks of each 64-block chunk and writes their 16
-// scores with one 64-byte store.
+// owns 16 consecutive blocks of each 64-block chunk; their scores go to an
+// LDS buffer, and the workgroup writes the scores of all its items once its
+// loads are done (a store between the loads of a streaming read turns the
+// memory around and cost ~9% alone at batch 128).
 //
 // Software pipeline: the registers hold two items' load groups (eight groups,
 // 16 KiB per wave).  As each group of the current item is used, the same
