@@ -152,25 +152,15 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     // Q^T as the MFMA B operand: lane (col, grp) brings column `col`, dims
     // kk * 32 + grp * 8 + [0, 8) for k-step kk; staged once in LDS (columns
     // past n_q * G are zero) and read back per block, which keeps registers
-    // for the loads in flight.
-    {
-        const int c = tid >> 4, chunk = tid & 15;  // 256 threads = 16 columns x 16 chunks
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (c < NC) {
-            const int qi = c / G, g = c - qi * G;
-            v = reinterpret_cast<const uint4 *>(
-                a.q + (((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + g) * kD)[chunk];
-        }
-        q_lds[c][chunk] = v;
+    // for the loads in flight.  The query load, the table load and the first
+    // block's loads are all issued before the query goes to LDS, so their
+    // latencies overlap (183 against 190 us alone at batch 128 / 16K).
+    const int qc = tid >> 4, qchunk = tid & 15;  // 256 threads = 16 columns x 16 chunks
+    uint4 qv = make_uint4(0, 0, 0, 0);
+    if (qc < NC) {
+        const int qi = qc / G, g = qc - qi * G;
+        qv = reinterpret_cast<const uint4 *>(a.q + (((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + g) * kD)[qchunk];
     }
-    __syncthreads();
-
-    float acc[GP][8];
-#pragma unroll
-    for (int g = 0; g < GP; g++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) acc[g][e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
 
     const int32_t *ts = a.tbl_slot + (size_t)rh * a.T;
     const int32_t *tb = a.tbl_block + (size_t)rh * a.T;
@@ -195,6 +185,16 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     const uint4 *src_c = next_valid(blk_c);
     uint4 kc[4], vc[4];
     if (src_c) load(src_c, kc, vc);
+
+    q_lds[qc][qchunk] = qv;
+    __syncthreads();
+
+    float acc[GP][8];
+#pragma unroll
+    for (int g = 0; g < GP; g++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[g][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
 
     float(*pl)[16] = p_lds[wave];
     while (src_c) {
@@ -381,26 +381,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
     // Q^T as the MFMA B operand: lane (col, grp) brings column `col`, dims
     // kk * 32 + grp * 8 + [0, 8) for k-step kk; staged once in LDS (columns
     // past n_q * G are zero) and read back per block, which keeps registers
-    // for the loads in flight.
-    {
-        const int c = tid >> 4, chunk = tid & 15;  // 256 threads = 16 columns x 16 chunks
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (c < NC) {
-            const int qi = c / G, g = c - qi * G;
-            v = reinterpret_cast<const uint4 *>(
-                a.q + (((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + g) * kD)[chunk];
-        }
-        q_lds[c][chunk] = v;
+    // for the loads in flight.  As in attn_kernel, the query, table and first
+    // block loads are issued together before the query goes to LDS.
+    const int qc = tid >> 4, qchunk = tid & 15;  // 256 threads = 16 columns x 16 chunks
+    uint4 qv = make_uint4(0, 0, 0, 0);
+    if (qc < NC) {
+        const int qi = qc / G, g = qc - qi * G;
+        qv = reinterpret_cast<const uint4 *>(a.q + (((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + g) * kD)[qchunk];
     }
-    __syncthreads();
-
-    // output accumulator in the MFMA C layout: acc[tt][e] = O^T[dim tt * 16 +
-    // 4 * grp + e][column col], so every value of a lane belongs to its own
-    // column and the rescale needs no exchange
-    f32x4 acc[8];
-#pragma unroll
-    for (int tt = 0; tt < 8; tt++) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
 
     const int32_t *ts = a.tbl_slot + (size_t)rh * a.T;
     const int32_t *tb = a.tbl_block + (size_t)rh * a.T;
@@ -426,6 +414,17 @@ __global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
     const uint4 *src_c = next_valid(blk_c);
     uint4 kc[4], vc[4];
     if (src_c) load(src_c, kc, vc);
+
+    q_lds[qc][qchunk] = qv;
+    __syncthreads();
+
+    // output accumulator in the MFMA C layout: acc[tt][e] = O^T[dim tt * 16 +
+    // 4 * grp + e][column col], so every value of a lane belongs to its own
+    // column and the rescale needs no exchange
+    f32x4 acc[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; tt++) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
 
     while (src_c) {
         int blk_n = 0;
