@@ -32,12 +32,17 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
 // Workgroups of one zero-copy gather.  Its PCIe reads wait microseconds and,
-// while they wait, slow the HBM-bound kernels that run beside them.  The layer
-// pipeline runs the gathers of consecutive layers on two streams, so up to two
-// run at once; 24 workgroups each (up to 384 KiB of reads in flight) keep the
-// link at ~95% of the pinned-memcpy rate, and over a pipelined decode step
-// 16 to 32 measured the same while 48 was 20% slower.
+// while they wait, slow the kernels that run beside them.  When a step can
+// admit thousands of blocks (the Qwen3-8B layer at batch 128: 1024 pairs x C)
+// the layer pipeline runs two gathers at once, and 24 workgroups each keep
+// the link at the pinned-memcpy rate (12 or 16: 1-2% slower; at a cap of two
+// blocks 16 is 17% slower).  With at most kFewAdmits admits per step, 16
+// leave more compute units to the latency-bound kernels beside them: the
+// ragged 32B-class layer (128 pairs, C = 6) runs at 154k tok/s against 149k
+// with 24 (12: 140k, 20: 154k).
 constexpr int kGatherWgs = 24;
+constexpr int kGatherWgsFew = 16;
+constexpr long kFewAdmits = 1024;
 
 __device__ __forceinline__ int wg_exclusive_scan(int v, int *tmp, int *total) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
@@ -381,7 +386,7 @@ __device__ void copy_positions(const int32_t *__restrict__ plan, int row, int pa
     }
 }
 
-// Zero-copy engine: kGatherWgs workgroups split the step's packed positions
+// Zero-copy engine: kGatherWgs (kGatherWgsFew) workgroups split the step's packed positions
 // into contiguous ranges; each thread keeps two 16-byte PCIe reads in flight
 // per block.
 __global__ __launch_bounds__(256) void stage_gather_kernel(
@@ -464,7 +469,8 @@ hipError_t launch_stage_gather(const oasis_dims &d, const oasis_stage_args &a,
                                const void *host_pool_dev, hipStream_t s) {
     if (a.C <= 0) return hipSuccess;
     const long most = (long)d.B * d.H_kv * a.C;  // admits of the step are at most this many
-    const int wgs = most < kGatherWgs ? (int)most : kGatherWgs;
+    const int want = most <= kFewAdmits ? kGatherWgsFew : kGatherWgs;
+    const int wgs = most < want ? (int)most : want;
     hipLaunchKernelGGL(stage_gather_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a.plan, plan_row(a.C),
                        d.B * d.H_kv, a.C, reinterpret_cast<const uint4 *>(host_pool_dev),
                        reinterpret_cast<uint4 *>(a.ws_pool), d.NB_max, a.S);
