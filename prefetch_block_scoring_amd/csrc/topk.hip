@@ -59,6 +59,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     const int r = rh / H_kv;
     const int tid = threadIdx.x;
     const int wave = tid / 64;
+    const float *row = scores + (size_t)rh * NB_max;
+    // Scores are read kBatch per thread at a time, every load issued before
+    // any is used; the first batch goes out with the context length (the row
+    // holds NB_max scores, so the reads stay inside it whatever the length).
+    constexpr int kBatch = 8;
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) v[u] = row[min(tid + u * kThreads, NB_max - 1)];
     const int nb = n_blocks_of(ctx_len[r], NB_max);
     int32_t *out = sel + (size_t)rh * K_b;
 
@@ -68,13 +76,21 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         return;
     }
 
-    const float *row = scores + (size_t)rh * NB_max;
     uint32_t k_and = 0xffffffffu, k_or = 0u;
-    for (int b = tid; b < nb; b += kThreads) {
-        const uint32_t key = rank_key(row[b]);
-        keys[b] = key;
-        k_and &= key;
-        k_or |= key;
+    for (int b0 = tid;; b0 += kBatch * kThreads) {
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const int b = b0 + u * kThreads;
+            if (b < nb) {
+                const uint32_t key = rank_key(v[u]);
+                keys[b] = key;
+                k_and &= key;
+                k_or |= key;
+            }
+        }
+        if (b0 + kBatch * kThreads >= nb) break;
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) v[u] = row[min(b0 + (kBatch + u) * kThreads, nb - 1)];
     }
     // bits every key shares: the leading digits made of them need no pass
     // (the scores of one row usually share sign and most of the exponent)
