@@ -30,6 +30,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+// the plan's bounds (checked at the entry points): K_sel <= 1024 predicted
+// ids and S <= 2048 slots per (request, KV head)
+constexpr int kMaxIdsPerThread = 1024 / kThreads;
+constexpr int kMaxSlotsPerThread = 2048 / kThreads;
 
 // Workgroups of one zero-copy gather.  Its PCIe reads wait microseconds and,
 // while they wait, slow the kernels that run beside them.  When a step can
@@ -116,40 +120,64 @@ __global__ __launch_bounds__(kThreads) void stage_plan_kernel(PlanArgs a) {
     const int rh = blockIdx.x;
     const int r = rh / a.H_kv;
     const int tid = threadIdx.x;
-    const int nb = n_blocks_of(a.ctx_len[r], a.NB_max);
     const int32_t *P = a.sel + (size_t)rh * K;
-    int np = a.n_sel[rh];
-    np = np < 0 ? 0 : (np > K ? K : np);
     int32_t *slot_block = a.slot_block + (size_t)rh * S;
     int32_t *slot_stamp = a.slot_stamp + (size_t)rh * S;
     const float *sc = a.scores + (size_t)rh * a.NB_max;
+
+    // Every read that needs nothing else is issued first, so their latencies
+    // overlap: the context length, the selection count, this thread's
+    // predicted ids (a contiguous range of the K, with the one before it) and
+    // its slots of the table.  Indices are clamped into the rows; the copies
+    // past their ends are never used.
+    const int ctx = a.ctx_len[r];
+    int np = a.n_sel[rh];
+    const int per = (K + kThreads - 1) / kThreads;  // <= kMaxIdsPerThread
+    const int lo = min(K, tid * per);
+    int pid[kMaxIdsPerThread + 1];  // P[lo - 1 + u]
+#pragma unroll
+    for (int u = 0; u <= kMaxIdsPerThread; u++) pid[u] = P[min(max(lo - 1 + u, 0), K - 1)];
+    int sbr[kMaxSlotsPerThread], str[kMaxSlotsPerThread];  // slot tid + u * kThreads
+#pragma unroll
+    for (int u = 0; u < kMaxSlotsPerThread; u++) {
+        const int sl = min(tid + u * kThreads, S - 1);
+        sbr[u] = slot_block[sl];
+        str[u] = slot_stamp[sl];
+    }
+    const int nb = n_blocks_of(ctx, a.NB_max);
+    np = np < 0 ? 0 : (np > K ? K : np);
 
     // 1. predicted ids: keep those in range and strictly ascending (rows from
     //    top-K are), compacted into pv in order
     int npv;
     {
-        const int per = (np + kThreads - 1) / kThreads;
-        const int lo = min(np, tid * per), hi = min(np, lo + per);
+        const int hi = min(np, lo + per);
         int c = 0;
-        for (int i = lo; i < hi; i++) {
-            const int p = P[i];
-            c += (p >= 0 && p < nb && (i == 0 || p > P[i - 1])) ? 1 : 0;
+#pragma unroll
+        for (int u = 0; u < kMaxIdsPerThread; u++) {
+            const int i = lo + u, p = pid[u + 1];
+            c += (i < hi && p >= 0 && p < nb && (i == 0 || p > pid[u])) ? 1 : 0;
         }
         int pos = wg_exclusive_scan(c, tmp, &npv);
-        for (int i = lo; i < hi; i++) {
-            const int p = P[i];
-            if (p >= 0 && p < nb && (i == 0 || p > P[i - 1])) pv[pos++] = p;
+#pragma unroll
+        for (int u = 0; u < kMaxIdsPerThread; u++) {
+            const int i = lo + u, p = pid[u + 1];
+            if (i < hi && p >= 0 && p < nb && (i == 0 || p > pid[u])) pv[pos++] = p;
         }
     }
     for (int k = tid; k < npv; k += kThreads) res_of[k] = -1;
     // 2. slot table; anything outside [0, nb) counts as free
-    for (int s = tid; s < S; s += kThreads) {
-        int b = slot_block[s];
-        if (b < 0 || b >= nb) b = -1;
-        sb[s] = b;
-        st[s] = b >= 0 ? slot_stamp[s] : -1;
-        in_p[s] = 0;
-        victim[s] = 0;
+#pragma unroll
+    for (int u = 0; u < kMaxSlotsPerThread; u++) {
+        const int sl = tid + u * kThreads;
+        if (sl < S) {
+            int b = sbr[u];
+            if (b < 0 || b >= nb) b = -1;
+            sb[sl] = b;
+            st[sl] = b >= 0 ? str[u] : -1;
+            in_p[sl] = 0;
+            victim[sl] = 0;
+        }
     }
     __syncthreads();
     // 3. resident predicted blocks: binary search of each held block in pv
