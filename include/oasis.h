@@ -536,15 +536,18 @@ typedef struct oasis_pipeline_desc {
                                  main stream after each layer's attention
                                  (the kernels that read HBM never overlap
                                  each other, only the copies); 0 =
-                                 automatic: -1 for a staged step that is
-                                 bound by the link (C blocks of 8 KiB at
-                                 57 GB/s take over 2.5 times as long as the
-                                 pair's K_b blocks and NB_max summaries of
-                                 512 B at 6 TB/s) and has at least as many
-                                 (request, KV head) pairs as the device has
-                                 compute units; else 2 (top-K and the plan
-                                 run one workgroup per pair and, with few
-                                 pairs, leave compute units idle).
+                                 automatic: 1 without staging (a second
+                                 stream only adds a second score kernel
+                                 beside the attention on HBM); staged, -1
+                                 for a step that is bound by the link (C
+                                 blocks of 8 KiB at 57 GB/s take over 2.5
+                                 times as long as the pair's K_b blocks
+                                 and NB_max summaries of 512 B at 6 TB/s)
+                                 and has at least as many (request, KV
+                                 head) pairs as the device has compute
+                                 units; else 2 (top-K and the plan run one
+                                 workgroup per pair and, with few pairs,
+                                 leave compute units idle).
                                  Copy streams: OASIS_COPY_KERNEL with at
                                  most one compute stream, two (even and odd
                                  layers), so one gather's tail overlaps the

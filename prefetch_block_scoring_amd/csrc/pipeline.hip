@@ -247,27 +247,32 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     if (e != hipSuccess) return fail(e, "hipGetDevice");
     // compute streams: with two, even and odd layers alternate, so that one
     // layer's latency-bound top-K and plan overlap the next layer's scores.
-    // That pays when those kernels leave compute units idle (fewer (request,
-    // KV head) pairs than compute units: the 32B-class ragged layer, 128
-    // pairs, 104k -> 160k tok/s with two), and whenever the step is bound by
-    // HBM rather than by the link.  A staged step whose admits can take the
-    // link much longer than its HBM kernels take HBM is link-bound: the chain
-    // then runs on the main stream behind each attention (compute_streams =
-    // -1), so the kernels that read HBM never run beside one another, only
-    // beside the copies, and the hardware queues go to two gather streams.
-    // The Qwen3-8B layer at batch 128 (1024 pairs, K_b 128, 1024 blocks of
-    // context), fetch cap C blocks per pair per step, tok/s with the chain on
-    // the main stream / two compute streams: C = 3: 205k / 268k, C = 4: 175k /
-    // 205k, C = 6: 160k / 151k.  The link time of C blocks per pair over the
-    // HBM time of the pair's attention and score bytes is 2.2 at C = 4 and
-    // 3.3 at C = 6; the rule below switches at 2.5.
+    // That pays for a staged step with fewer (request, KV head) pairs than
+    // compute units (the 32B-class ragged layer, 128 pairs: 154k against
+    // 142k tok/s with one) and for a staged step that HBM binds (the Qwen3-8B
+    // layer at batch 128 with a fetch cap of one or two blocks: 393k / 360k
+    // against 343k / 320k).  Without staging one compute stream is better:
+    // its scores and the attention are the step's HBM traffic, and a second
+    // stream only adds a second score kernel taking bandwidth from the
+    // attention (Qwen3-8B in HBM at batch 32: 361k against 354k; the
+    // reasoning layer: 355k against 345k).  A staged step whose admits can
+    // take the link much longer than its HBM kernels take HBM is link-bound:
+    // the chain then runs on the main stream behind each attention
+    // (compute_streams = -1), so the kernels that read HBM never run beside
+    // one another, only beside the copies, and the hardware queues go to two
+    // gather streams.  The Qwen3-8B layer at batch 128 (1024 pairs, K_b 128,
+    // 1024 blocks of context), fetch cap C blocks per pair per step, tok/s
+    // with the chain on the main stream / two compute streams: C = 3: 205k /
+    // 268k, C = 4: 175k / 205k, C = 6: 160k / 151k.  The link time of C blocks
+    // per pair over the HBM time of the pair's attention and score bytes is
+    // 2.2 at C = 4 and 3.3 at C = 6; the rule below switches at 2.5.
     int n_comp = ds.compute_streams;
     if (n_comp == 0) {
         const int64_t pairs = (int64_t)dims->B * dims->H_kv;
         const double link_s = (double)ds.C * kBlockBytes / kLinkBytesPerS;
         const double hbm_s = ((double)ds.K_b * kBlockBytes + (double)dims->NB_max * kSummaryBytes) / kHbmBytesPerS;
         const bool link_bound = ds.staged && link_s > 2.5 * hbm_s;
-        n_comp = (pairs < device_cu_count() || !link_bound) ? 2 : -1;
+        n_comp = !ds.staged ? 1 : (pairs < device_cu_count() || !link_bound) ? 2 : -1;
     }
     if (n_comp < 0) {
         p->comp_on_main = true;
