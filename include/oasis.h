@@ -452,12 +452,13 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
  * launch, event record and stream wait made from native code: *
  *   main stream (the caller's)   attention of (l, t) over the working set
  *                                staged at (l, t - 1)
- *   compute streams (owned)      scores and top-K of (l, t), staging plan;
- *                                without staging, even and odd layers
- *                                alternate two, so one layer's top-K
- *                                overlaps the next layer's scores; or none:
- *                                the main stream runs them after the
- *                                layer's attention (compute_streams)
+ *   compute streams (owned)      scores and top-K of (l, t), staging plan:
+ *                                one without staging; two for a staged
+ *                                step that the link does not bind (even
+ *                                and odd layers alternate, so one layer's
+ *                                top-K overlaps the next layer's scores);
+ *                                or none: the main stream runs them after
+ *                                the layer's attention (compute_streams)
  *   copy streams (owned)         the copies of (l, t); the zero-copy engine
  *                                alternates two by layer so that one
  *                                layer's gather tail overlaps the next

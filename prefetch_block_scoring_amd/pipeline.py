@@ -10,14 +10,18 @@ lays that out on one GPU's streams:
   main stream     attention of (layer l, step t), after the transfer of
                   (l, t - 1) only
   compute stream  scores and top-K of (l, t), then the staging plan of (l, t)
-                  (two streams by layer parity when nothing is staged or
-                  when there are fewer (request, KV head) pairs than compute
-                  units; otherwise the main stream itself, behind each
-                  attention; `compute_streams` overrides)
+                  (one stream when nothing is staged; two by layer parity for
+                  a staged step that the link does not bind; otherwise the
+                  main stream itself, behind each attention;
+                  `compute_streams` overrides)
   copy streams    the copies of (l, t) (gather kernels, on two streams by
-                  layer parity when there is one compute stream, or DMA
-                  copy + scatter on the pipeline's worker thread, or, mixed,
-                  DMA for even layers and gathers for odd layers)
+                  layer parity when the chain is on the main stream, or DMA
+                  copy + scatter, or, mixed, DMA for even layers and gathers
+                  for odd layers)
+
+With staging and compute streams of its own, the chain and the copies of a
+layer-step are enqueued by the pipeline's two issue threads, and the calling
+thread enqueues only the attention (`issue_threads`).
 
 `LayerPipeline` allocates the per-layer buffers the native pipeline works in
 (three attention tables, two selections and two plan buffers per layer, the
