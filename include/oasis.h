@@ -571,7 +571,11 @@ typedef struct oasis_pipeline_desc {
                                  thread only the attention (a stream wait
                                  on a pending event costs the enqueuing
                                  thread 8-24 us, and a staged layer-step
-                                 needs three); -1 = the calling thread
+                                 needs three).  The workers make their
+                                 waits (the top-K's on the attention of
+                                 step t - 1, the copies' on their plan) on
+                                 the host, so those streams carry no
+                                 barrier packets.  -1 = the calling thread
                                  enqueues everything.  Unstaged pipelines
                                  and a chain on the main stream
                                  (compute_streams = -1) always use the
