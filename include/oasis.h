@@ -178,8 +178,9 @@ int oasis_select_topk(const oasis_dims *dims, const float *scores,
  * written by the previous call, but may refill slots listed in the table
  * written two calls earlier (blocks the previous call evicted): `wait_event`
  * must mark the end of every attention that read that older table.
- * `done_event` (if not NULL) is recorded on `copy_stream` after the last
- * copy: make the next attention wait on it.
+ * `done_event` (if not NULL) completes on `copy_stream` with the last copy
+ * (with OASIS_COPY_KERNEL it is bound to the gather kernel itself, so it adds
+ * no marker to the queue): make the next attention wait on it.
  *
  * Copy engines:
  *  - OASIS_COPY_DMA reads the plan back into `host_plan` (pinned host, at
@@ -236,7 +237,8 @@ typedef struct oasis_stage_args {
     void *copy_stream;
     void *wait_event;
     void *done_event;
-    void *plan_event;       /* optional: recorded after the plan kernels */
+    void *plan_event;       /* optional: completes with the plan kernels
+                               (bound to the last one) */
     int64_t *stats_accum;   /* optional, device int64[4]: the plan kernels add
                                this step's admits, evictions and deferred
                                admits (oasis_stage_stats) to [0], [1], [2] and
@@ -346,7 +348,8 @@ int oasis_stage_read_stats(const oasis_dims *dims, int32_t C,
 
 /* The two halves of oasis_stage_blocks, for callers that overlap staging
  * across layers: oasis_stage_plan enqueues the plan kernels (steps 1-4 and
- * the table) on `stream`, records `plan_event` if given, and never blocks.
+ * the table) on `stream`, binds `plan_event` if given to the last of them,
+ * and never blocks.
  * oasis_stage_copy performs step 5 for the plan in `plan`: it orders the
  * copies after `plan_event` if given, else after everything enqueued on
  * `stream` so far, and otherwise behaves as the copy part of
@@ -621,9 +624,11 @@ int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
  * `capacity` launches of each kind whose bit is set in `kinds` and clears
  * the totals; capacity 0 or kinds 0 disables it.  Kinds: 0 attention (main
  * stream), 1 scores, 2 top-K, 3 staging plan (compute stream); each interval
- * starts once the stream's earlier waits are satisfied.  Every timed launch
- * records two timing events on its stream.  timing_read synchronises on the
- * recorded events and returns their total milliseconds and count. */
+ * runs from the start of the launch's first kernel to the end of its last.
+ * The two timing events of a launch are bound to those kernels, so timing
+ * adds nothing to the queues.  Re-arming first waits for everything the
+ * pipeline has enqueued to finish.  timing_read synchronises on the events
+ * and returns their total milliseconds and count. */
 int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity,
                           uint32_t kinds);
 int oasis_pipeline_timing_read(oasis_pipeline *p, int32_t kind,

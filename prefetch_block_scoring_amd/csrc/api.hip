@@ -153,6 +153,20 @@ int oasis_build_summaries(const oasis_dims *dims, const uint16_t *kv, const int3
 
 int oasis_score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J,
                        const uint16_t *kminmax, const int32_t *ctx_len, float *scores, void *stream) {
+    return score_blocks(dims, q_look, J, kminmax, ctx_len, scores, stream, {});
+}
+
+int oasis_select_topk(const oasis_dims *dims, const float *scores, const int32_t *ctx_len, int32_t K_b,
+                      int32_t *sel, int32_t *n_sel, void *stream) {
+    return select_topk(dims, scores, ctx_len, K_b, sel, n_sel, stream, {});
+}
+
+}  // extern "C"
+
+namespace oasis {
+
+int score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J, const uint16_t *kminmax,
+                 const int32_t *ctx_len, float *scores, void *stream, const LaunchEvents &ev) {
     clear_error();
     int rc = check_dims(dims);
     if (rc) return rc;
@@ -160,29 +174,41 @@ int oasis_score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J
     if (J > 64) FAIL(OASIS_EUNSUPPORTED, "J = %d (at most 64)", J);
     if ((int64_t)dims->B * dims->H_kv * ((dims->NB_max + 63) / 64) > INT32_MAX)
         FAIL(OASIS_EUNSUPPORTED, "B * H_kv * ceil(NB_max / 64) exceeds 2^31 - 1");
-    if (dims->B == 0) return OASIS_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dims->B == 0) {
+        OASIS_HIP(record_events(ev, s));
+        return OASIS_OK;
+    }
     NEED(q_look);
     NEED(kminmax);
     NEED(ctx_len);
     NEED(scores);
-    OASIS_HIP(launch_score(*dims, q_look, J, kminmax, ctx_len, scores, static_cast<hipStream_t>(stream)));
+    OASIS_HIP(launch_score(*dims, q_look, J, kminmax, ctx_len, scores, s, ev));
     return OASIS_OK;
 }
 
-int oasis_select_topk(const oasis_dims *dims, const float *scores, const int32_t *ctx_len, int32_t K_b,
-                      int32_t *sel, int32_t *n_sel, void *stream) {
+int select_topk(const oasis_dims *dims, const float *scores, const int32_t *ctx_len, int32_t K_b, int32_t *sel,
+                int32_t *n_sel, void *stream, const LaunchEvents &ev) {
     clear_error();
     int rc = check_dims(dims);
     if (rc) return rc;
     if (K_b < 1) FAIL(OASIS_EINVAL, "K_b = %d < 1", K_b);
-    if (dims->B == 0) return OASIS_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dims->B == 0) {
+        OASIS_HIP(record_events(ev, s));
+        return OASIS_OK;
+    }
     NEED(scores);
     NEED(ctx_len);
     NEED(sel);
     NEED(n_sel);
-    OASIS_HIP(launch_topk(*dims, scores, ctx_len, K_b, sel, n_sel, static_cast<hipStream_t>(stream)));
+    OASIS_HIP(launch_topk(*dims, scores, ctx_len, K_b, sel, n_sel, s, ev));
     return OASIS_OK;
 }
+
+}  // namespace oasis
+
+extern "C" {
 
 int oasis_append_kv(const oasis_dims *dims, const uint16_t *k_new, const uint16_t *v_new, int32_t *ctx_len,
                     uint16_t *kminmax, void *pool, uint16_t *ws_pool, const int32_t *slot_block, int32_t S,
@@ -317,11 +343,12 @@ static int check_copy_args(const oasis_dims *dims, const oasis_stage_args *a) {
     return OASIS_OK;
 }
 
-static int stage_plan_phase(const oasis_dims *dims, const oasis_stage_args *a) {
+// `start` (optional) completes as the plan kernel starts; `plan_event`
+// completes with the prefix kernel.
+static int stage_plan_phase(const oasis_dims *dims, const oasis_stage_args *a, hipEvent_t start = nullptr) {
     hipStream_t s = static_cast<hipStream_t>(a->stream);
-    OASIS_HIP(launch_stage_plan(*dims, *a, s));
-    OASIS_HIP(launch_stage_prefix(*dims, *a, s));
-    if (a->plan_event) OASIS_HIP(hipEventRecord(static_cast<hipEvent_t>(a->plan_event), s));
+    OASIS_HIP(launch_stage_plan(*dims, *a, s, {start, nullptr}));
+    OASIS_HIP(launch_stage_prefix(*dims, *a, s, {nullptr, static_cast<hipEvent_t>(a->plan_event)}));
     return OASIS_OK;
 }
 
@@ -349,28 +376,41 @@ static int stage_copy_phase(const oasis_dims *dims, const oasis_stage_args *a, c
     hipStream_t s = static_cast<hipStream_t>(a->stream);
     hipStream_t cs = a->copy_stream ? static_cast<hipStream_t>(a->copy_stream) : s;
     // the plan this copy uses: `plan_event` if given, else everything on `stream` so far
+    // (a gather on that same stream follows it in stream order)
+    const bool in_order = cs == s && a->copy_mode == OASIS_COPY_KERNEL;
     hipEvent_t plan_ready = static_cast<hipEvent_t>(a->plan_event);
-    if (!plan_ready) {
+    if (!plan_ready && !in_order) {
         if ((rc = ring_event(&plan_ready))) return rc;
         OASIS_HIP(hipEventRecord(plan_ready, s));
     }
+    hipEvent_t done = static_cast<hipEvent_t>(a->done_event);
     if (a->copy_mode == OASIS_COPY_KERNEL) {
-        OASIS_HIP(stream_wait(cs, plan_ready));
+        if (!in_order) OASIS_HIP(stream_wait(cs, plan_ready));
         if (a->wait_event) OASIS_HIP(stream_wait(cs, static_cast<hipEvent_t>(a->wait_event)));
-        OASIS_HIP(launch_stage_gather(*dims, *a, pool_dev, cs));
+        OASIS_HIP(launch_stage_gather(*dims, *a, pool_dev, cs, {nullptr, done}));
     } else {
         if ((rc = stage_dma(*dims, *a, plan_ready, cs))) return rc;
+        if (done) OASIS_HIP(hipEventRecord(done, cs));
     }
-    if (a->done_event) OASIS_HIP(hipEventRecord(static_cast<hipEvent_t>(a->done_event), cs));
     return OASIS_OK;
 }
 
-int oasis_stage_plan(const oasis_dims *dims, const oasis_stage_args *a) {
+int oasis_stage_plan(const oasis_dims *dims, const oasis_stage_args *a) { return stage_plan(dims, a, nullptr); }
+
+}  // extern "C"
+
+int oasis::stage_plan(const oasis_dims *dims, const oasis_stage_args *a, hipEvent_t start) {
     clear_error();
     int rc = check_plan_args(dims, a);
-    if (rc || dims->B == 0) return rc;
-    return stage_plan_phase(dims, a);
+    if (rc) return rc;
+    if (dims->B == 0) {
+        OASIS_HIP(record_events({start, static_cast<hipEvent_t>(a->plan_event)}, static_cast<hipStream_t>(a->stream)));
+        return OASIS_OK;
+    }
+    return stage_plan_phase(dims, a, start);
 }
+
+extern "C" {
 
 int oasis_stage_copy(const oasis_dims *dims, const oasis_stage_args *a) {
     clear_error();
@@ -443,6 +483,16 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
                          int32_t P, const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n,
                          int32_t T, const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,
                          size_t ws_bytes, int32_t n_split, void *stream) {
+    return lookahead_attn(dims, n_q, q, kv_pool, P, tbl_slot, tbl_block, tbl_n, T, ctx_len, sm_scale, out, lse, ws,
+                          ws_bytes, n_split, stream, {});
+}
+
+}  // extern "C"
+
+int oasis::lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q, const uint16_t *kv_pool, int32_t P,
+                          const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n, int32_t T,
+                          const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,
+                          size_t ws_bytes, int32_t n_split, void *stream, const LaunchEvents &ev) {
     clear_error();
     int rc = check_dims(dims);
     if (rc) return rc;
@@ -454,7 +504,11 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
     if (T < 0) FAIL(OASIS_EINVAL, "T = %d < 0", T);
     if (n_split < 0 || n_split > 64) FAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", n_split);
     if (!std::isfinite(sm_scale)) FAIL(OASIS_EINVAL, "sm_scale is not finite");
-    if (dims->B == 0) return OASIS_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dims->B == 0) {
+        OASIS_HIP(record_events(ev, s));
+        return OASIS_OK;
+    }
     NEED(q);
     NEED(kv_pool);
     NEED(tbl_n);
@@ -471,9 +525,11 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
         if (ws_bytes < need) FAIL(OASIS_ENOSPACE, "attention workspace %zu bytes < %zu", ws_bytes, need);
     }
     OASIS_HIP(launch_attn(*dims, n_q, q, kv_pool, P, tbl_slot, tbl_block, tbl_n, T, ctx_len, sm_scale, out, lse,
-                          static_cast<float *>(ws), splits, static_cast<hipStream_t>(stream)));
+                          static_cast<float *>(ws), splits, s, ev));
     return OASIS_OK;
 }
+
+extern "C" {
 
 size_t oasis_sparse_decode_attn_static_bytes(void) { return attn_static_scratch_bytes(); }
 

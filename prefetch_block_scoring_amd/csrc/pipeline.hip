@@ -11,6 +11,7 @@
 #include "copy_queue.h"
 #include "oasis_internal.h"
 
+#include <algorithm>
 #include <chrono>
 #include <cstdio>
 #include <mutex>
@@ -41,10 +42,12 @@ struct Job {
 };
 
 // The background half of one layer-step: scores, top-K and staging plan
-// from the lookahead queries (and the copies that follow).
+// from the lookahead queries (and the copies that follow).  attn_prev
+// completes with the attention of step - 1.
 struct ChainJob {
     int layer = 0, step = 0;
     const uint16_t *q_look = nullptr;
+    hipEvent_t attn_prev = nullptr;
 };
 
 }  // namespace
@@ -62,6 +65,10 @@ struct oasis_pipeline {
     hipStream_t main = nullptr, comp[2] = {nullptr, nullptr}, copy[2] = {nullptr, nullptr};
     bool comp_on_main = false;  // compute_streams = -1: the chain runs on the main stream
     std::vector<hipEvent_t> ev;  // [kind][layer][kRing]
+    // per layer, written by the calling thread: the event that completes with
+    // the layer's latest attention, and (unstaged) with its latest top-K; the
+    // ring's event, or the timing event bound to the same kernel
+    std::vector<hipEvent_t> attn_last, sel_last;
 
     // timing
     int t_cap = 0;
@@ -93,16 +100,14 @@ namespace {
         return (code);                                    \
     } while (0)
 
-void timed_begin(oasis_pipeline *p, int kind, hipStream_t s) {
-    if ((p->t_kinds >> kind & 1u) && p->t_n[kind] < p->t_cap)
-        (void)hipEventRecord(p->t_ev[kind][2 * p->t_n[kind]], s);
-}
-
-void timed_end(oasis_pipeline *p, int kind, hipStream_t s) {
-    if ((p->t_kinds >> kind & 1u) && p->t_n[kind] < p->t_cap) {
-        (void)hipEventRecord(p->t_ev[kind][2 * p->t_n[kind] + 1], s);
-        p->t_n[kind]++;
-    }
+// The timing events of the next launch of `kind`, bound to its kernels, or
+// none when that kind is not timed (or its capacity is used up).  Kind 0 is
+// taken by the calling thread, kinds 1-3 by whichever thread issues the
+// chain.
+LaunchEvents timed(oasis_pipeline *p, int kind) {
+    if (!(p->t_kinds >> kind & 1u) || p->t_n[kind] >= p->t_cap) return {};
+    const int i = p->t_n[kind]++;
+    return {p->t_ev[kind][2 * i], p->t_ev[kind][2 * i + 1]};
 }
 
 // The copy half of staging for one job; called by the calling thread
@@ -204,7 +209,7 @@ void release(oasis_pipeline *p) {
 
 extern "C" {
 
-static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look);
+static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look, hipEvent_t attn_prev);
 
 int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *desc, oasis_pipeline **out) {
     clear_error();
@@ -244,6 +249,8 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     p->layers.assign(ds.layers, ds.layers + ds.n_layers);
     p->desc.layers = nullptr;
     p->next_step.assign(ds.n_layers, 0);
+    p->attn_last.assign(ds.n_layers, nullptr);
+    p->sel_last.assign(ds.n_layers, nullptr);
     p->S = ds.K_b + (ds.staged ? ds.C : 0);
     p->main = static_cast<hipStream_t>(ds.main_stream);
     auto fail = [&](hipError_t e, const char *what) {
@@ -318,7 +325,7 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
         p->chain.start(
             ds.n_layers,
             [p](const ChainJob &j, std::string *msg) {
-                const int rc = issue_chain(p, j.layer, j.step, j.q_look);
+                const int rc = issue_chain(p, j.layer, j.step, j.q_look, j.attn_prev);
                 if (rc != OASIS_OK) {
                     *msg = "scores, top-K or plan of layer " + std::to_string(j.layer) + " step " +
                            std::to_string(j.step) + ": " + oasis_last_error();
@@ -348,7 +355,7 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
 // staging plan for step t + 1 from the lookahead queries, then the copies
 // (handed to the copy worker when there is one).  Runs on the calling thread,
 // or on the chain worker in submission order.
-static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look) {
+static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look, hipEvent_t attn_prev) {
     const oasis_pipeline_desc &ds = p->desc;
     const oasis_layer_buffers &b = p->layers[l];
     const oasis_dims *d = &p->d;
@@ -357,9 +364,7 @@ static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look) 
     const int mode = layer_copy_mode(ds, l);
     int rc;
     hipStream_t cs = p->comp[p->comp[1] ? (l & 1) : 0];
-    timed_begin(p, 1, cs);
-    if ((rc = oasis_score_blocks(d, q_look, ds.J, ds.kminmax, ds.ctx_len, b.scores, cs))) return rc;
-    timed_end(p, 1, cs);
+    if ((rc = score_blocks(d, q_look, ds.J, ds.kminmax, ds.ctx_len, b.scores, cs, timed(p, 1)))) return rc;
     if (t >= 2) {
         // unstaged: sel[j], read by the attention of step t - 1.  Staged: the
         // attention of step t - 1 covers every later reuse: table
@@ -373,14 +378,19 @@ static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look) 
         // the compute stream gets no barrier packet, each of which holds its
         // queue ~10 us after the event has completed (the ragged 32B-class
         // layer: 159k against 155k tok/s).
-        if (p->threaded) OASIS_HIP(hipEventSynchronize(p->event(kEvAttn, l, t - 1)));
-        else OASIS_HIP(stream_wait(cs, p->event(kEvAttn, l, t - 1)));
+        // (no event: timing was re-armed since, after everything finished)
+        if (!attn_prev) {
+        } else if (p->threaded) {
+            OASIS_HIP(hipEventSynchronize(attn_prev));
+        } else {
+            OASIS_HIP(stream_wait(cs, attn_prev));
+        }
     }
-    timed_begin(p, 2, cs);
-    if ((rc = oasis_select_topk(d, b.scores, ds.ctx_len, K_b, b.sel[j], b.n_sel[j], cs))) return rc;
-    timed_end(p, 2, cs);
+    LaunchEvents tk = timed(p, 2);
+    if (!ds.staged && !tk.stop) tk.stop = p->event(kEvSel, l, t);
+    if ((rc = select_topk(d, b.scores, ds.ctx_len, K_b, b.sel[j], b.n_sel[j], cs, tk))) return rc;
     if (!ds.staged) {
-        OASIS_HIP(hipEventRecord(p->event(kEvSel, l, t), cs));
+        p->sel_last[l] = tk.stop;  // unstaged chains run on the calling thread
         return OASIS_OK;
     }
 
@@ -422,11 +432,10 @@ static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look) 
     // the copies follow the plan, which followed the attention of step t - 1
     a.wait_event = nullptr;
     a.done_event = p->event(kEvStage, l, t);
-    a.plan_event = p->event(kEvPlan, l, t);
+    const LaunchEvents pe = timed(p, 3);
+    a.plan_event = pe.stop ? pe.stop : p->event(kEvPlan, l, t);
     a.stats_accum = ds.stage_stats;
-    timed_begin(p, 3, cs);
-    if ((rc = oasis_stage_plan(d, &a))) return rc;
-    timed_end(p, 3, cs);
+    if ((rc = stage_plan(d, &a, pe.start))) return rc;
     if (mode == OASIS_COPY_DMA || p->threaded) {
         p->copies.push(job);
     } else if ((rc = run_copy(p, job))) {
@@ -452,36 +461,36 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     const int mode = layer_copy_mode(ds, l);
 
     // foreground: attention of step t
+    const hipEvent_t attn_prev = p->attn_last[l];
     if (t >= 1) {
+        LaunchEvents ev = timed(p, 0);
+        if (!ev.stop) ev.stop = p->event(kEvAttn, l, t);
         if (ds.staged) {
             // the copy worker has recorded the copies of step t - 1
             if (mode == OASIS_COPY_DMA || p->threaded) (void)p->copies.wait_done(l, t - 1);
             if ((rc = worker_error(p))) return rc;
             OASIS_HIP(stream_wait(p->main, p->event(kEvStage, l, t - 1)));
             const int k = t % 3;
-            timed_begin(p, 0, p->main);
-            rc = oasis_lookahead_attn(d, ds.n_q, q_attn, b.ws_pool, p->S, b.tbl_slot[k], b.tbl_block[k],
-                                      b.tbl_n[k], K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws,
-                                      b.attn_ws_bytes, ds.n_split, p->main);
+            rc = lookahead_attn(d, ds.n_q, q_attn, b.ws_pool, p->S, b.tbl_slot[k], b.tbl_block[k], b.tbl_n[k], K_b,
+                                ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes, ds.n_split, p->main,
+                                ev);
         } else {
             const int jp = (t - 1) % 2;
-            OASIS_HIP(stream_wait(p->main, p->event(kEvSel, l, t - 1)));
-            timed_begin(p, 0, p->main);
-            rc = oasis_lookahead_attn(d, ds.n_q, q_attn, ds.pool, d->NB_max, b.sel[jp], b.sel[jp], b.n_sel[jp],
-                                      K_b, ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes,
-                                      ds.n_split, p->main);
+            if (p->sel_last[l]) OASIS_HIP(stream_wait(p->main, p->sel_last[l]));
+            rc = lookahead_attn(d, ds.n_q, q_attn, ds.pool, d->NB_max, b.sel[jp], b.sel[jp], b.n_sel[jp], K_b,
+                                ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes, ds.n_split, p->main,
+                                ev);
         }
         if (rc) return rc;
-        timed_end(p, 0, p->main);
-        OASIS_HIP(hipEventRecord(p->event(kEvAttn, l, t), p->main));
+        p->attn_last[l] = ev.stop;
     }
 
     p->next_step[l] = t + 1;
     if (p->threaded) {
-        p->chain.push(ChainJob{l, t, q_look});
+        p->chain.push(ChainJob{l, t, q_look, attn_prev});
         return OASIS_OK;
     }
-    return issue_chain(p, l, t, q_look);
+    return issue_chain(p, l, t, q_look, attn_prev);
 }
 
 int oasis_pipeline_drain(oasis_pipeline *p) {
@@ -510,6 +519,13 @@ int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity, uint32_t kinds) {
     if (kinds >> kTimedKinds) PFAIL(OASIS_EINVAL, "kinds = 0x%x (bits 0 .. %d)", kinds, kTimedKinds - 1);
     int rc = oasis_pipeline_drain(p);
     if (rc) return rc;
+    // The timing events are bound to launches again from the first one on, so
+    // no wait still to be issued may name one: let everything enqueued
+    // finish, after which the next steps need no wait on earlier launches.
+    for (hipStream_t c : {p->main, p->comp[0], p->comp[1], p->copy[0], p->copy[1]})
+        if (c) OASIS_HIP(hipStreamSynchronize(c));
+    std::fill(p->attn_last.begin(), p->attn_last.end(), nullptr);
+    std::fill(p->sel_last.begin(), p->sel_last.end(), nullptr);
     for (int k = 0; k < kTimedKinds; k++) {
         auto &v = p->t_ev[k];
         while ((int)v.size() < 2 * capacity) {

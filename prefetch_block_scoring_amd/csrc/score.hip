@@ -342,12 +342,12 @@ int score_grid(int n_items) {
 
 hipError_t launch_score(const oasis_dims &d, const uint16_t *q_look, int J,
                         const uint16_t *kminmax, const int32_t *ctx_len,
-                        float *scores, hipStream_t s) {
+                        float *scores, hipStream_t s, const LaunchEvents &ev) {
     const int chunks = (d.NB_max + kItemBlocks - 1) / kItemBlocks;
     const int n_items = d.B * d.H_kv * chunks;  // at most this many items hold blocks
-    hipLaunchKernelGGL(score_kernel, dim3((unsigned)score_grid(n_items)), dim3(kThreads), 0, s, q_look, J,
-                       d.H_q, d.H_kv, reinterpret_cast<const uint4 *>(kminmax), ctx_len, scores, d.NB_max,
-                       d.B);
+    hipExtLaunchKernelGGL(score_kernel, dim3((unsigned)score_grid(n_items)), dim3(kThreads), 0, s, ev.start,
+                          ev.stop, 0, q_look, J, d.H_q, d.H_kv, reinterpret_cast<const uint4 *>(kminmax), ctx_len,
+                          scores, d.NB_max, d.B);
     return hipGetLastError();
 }
 
