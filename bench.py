@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--kernel-timing", default="attn", choices=["all", "attn"],
                    help="launches of the timed steps that get timing events (two event records each, which "
                         "slow a pipeline bound by the GPU); the others are timed in an extra pass afterwards")
+    p.add_argument("--timing-every", type=int, default=1,
+                   help="time one launch in every N of each timed kind during the timed steps (a timed launch "
+                        "carries a start event, which holds its queue ~5 us)")
     p.add_argument("--cap", type=float, default=None,
                    help="override the staged workload's fetch cap (fraction of the budget; >= 1 = fetch-all)")
     p.add_argument("--drift", type=float, default=None,
@@ -525,7 +528,9 @@ def main():
     # --kernel-timing all
     all_kinds = ("attn", "score", "topk", "plan") if staged else ("attn", "score", "topk")
     timed_kinds = all_kinds if args.kernel_timing == "all" else ("attn",)
-    pipe.enable_timing(args.steps * L, timed_kinds)
+    every = max(1, args.timing_every)
+    n_timed = -(-args.steps * L // every)
+    pipe.enable_timing(n_timed, timed_kinds, every=every)
     step_events = []
     t0 = time.perf_counter()
     run(1 + args.warmup, n_steps, step_events=step_events)
@@ -544,10 +549,11 @@ def main():
             raise SystemExit(f"timing of {name}: {n} launches recorded, {n_expect} expected")
         return us
 
-    live = {k: read_us(k, args.steps * L) for k in timed_kinds}
+    live = {k: read_us(k, n_timed) for k in timed_kinds}
+    live_note = "live, timed steps" + (f", one launch in {every}" if every > 1 else "")
     # distributions: each timed launch, and each decode step (intervals
     # between the main stream's passes of consecutive steps), per layer-step
-    spread = {k: pipe.timing_values(k, args.steps * L) for k in timed_kinds}
+    spread = {k: pipe.timing_values(k, n_timed) for k in timed_kinds}
     step_us = [step_events[i - 1].elapsed_time(step_events[i]) * 1e3 / L for i in range(1, len(step_events))]
     copy_s, copy_n = pipe.copy_host_seconds()
     # the kinds not timed above: an extra pass of n_extra steps with events on
@@ -581,12 +587,12 @@ def main():
         us = avg_us(name)
         kern[name] = {"avg_us": round(us, 2), "bytes": nbytes,
                       "GBps": round(nbytes / (us * 1e-6) / 1e9, 1) if us > 0 else None,
-                      "timed": "live, timed steps" if name in live else f"extra pass of {n_extra} steps",
+                      "timed": live_note if name in live else f"extra pass of {n_extra} steps",
                       **percentiles(spread.get(name, []))}
     h2d = None
     if staged:
         kern["plan"] = {"avg_us": round(avg_us("plan"), 2), "note": "plan and prefix kernels",
-                        "timed": "live, timed steps" if "plan" in live else f"extra pass of {n_extra} steps",
+                        "timed": live_note if "plan" in live else f"extra pass of {n_extra} steps",
                         **percentiles(spread.get("plan", []))}
         kern["copy_host"] = {"avg_us": round(copy_s / max(copy_n, 1) * 1e6, 2),
                               "note": ("host time of a staging call: plan read-back and packing up to the "

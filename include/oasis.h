@@ -622,7 +622,9 @@ int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
 
 /* Event timing of the steps: capacity > 0 (re)arms timing of up to
  * `capacity` launches of each kind whose bit is set in `kinds` and clears
- * the totals; capacity 0 or kinds 0 disables it.  Kinds: 0 attention (main
+ * the totals; capacity 0 or kinds 0 disables it.  Of each kind, one launch
+ * in every `every` (>= 1) is timed, the first launch after arming
+ * included.  Kinds: 0 attention (main
  * stream), 1 scores, 2 top-K, 3 staging plan (compute stream); each interval
  * runs from the start of the launch's first kernel to the end of its last.
  * The two timing events of a launch are bound to those kernels, so timing
@@ -630,7 +632,7 @@ int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
  * pipeline has enqueued to finish.  timing_read synchronises on the events
  * and returns their total milliseconds and count. */
 int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity,
-                          uint32_t kinds);
+                          uint32_t kinds, int32_t every);
 int oasis_pipeline_timing_read(oasis_pipeline *p, int32_t kind,
                                double *total_ms, int32_t *count);
 

@@ -120,7 +120,7 @@ _SIGNATURES = {
     "oasis_pipeline_layer_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P]),
     "oasis_pipeline_drain": (ctypes.c_int, [_P]),
     "oasis_pipeline_stream": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_void_p)]),
-    "oasis_pipeline_timing": (ctypes.c_int, [_P, _I32, ctypes.c_uint32]),
+    "oasis_pipeline_timing": (ctypes.c_int, [_P, _I32, ctypes.c_uint32, _I32]),
     "oasis_pipeline_timing_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(_I32)]),
     "oasis_pipeline_timing_values": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_float), _I32,
@@ -696,8 +696,8 @@ def oasis_pipeline_stream(h: int, which: int) -> Optional[int]:
     return s.value
 
 
-def oasis_pipeline_timing(h: int, capacity: int, kinds: int = 0xF):
-    _check(_lib.oasis_pipeline_timing(h, int(capacity), int(kinds)))
+def oasis_pipeline_timing(h: int, capacity: int, kinds: int = 0xF, every: int = 1):
+    _check(_lib.oasis_pipeline_timing(h, int(capacity), int(kinds), int(every)))
 
 
 def oasis_pipeline_timing_read(h: int, kind: int):

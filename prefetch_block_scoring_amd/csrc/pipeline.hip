@@ -72,6 +72,8 @@ struct oasis_pipeline {
 
     // timing
     int t_cap = 0;
+    int t_every = 1;       // one launch in every t_every of a kind is timed
+    int t_seen[kTimedKinds] = {0, 0, 0, 0};  // launches of each kind since arming
     uint32_t t_kinds = 0;  // bit k: kind k is timed
     std::vector<hipEvent_t> t_ev[kTimedKinds];  // 2 * t_cap each
     int t_n[kTimedKinds] = {0, 0, 0, 0};
@@ -106,6 +108,7 @@ namespace {
 // chain.
 LaunchEvents timed(oasis_pipeline *p, int kind) {
     if (!(p->t_kinds >> kind & 1u) || p->t_n[kind] >= p->t_cap) return {};
+    if (p->t_seen[kind]++ % p->t_every != 0) return {};
     const int i = p->t_n[kind]++;
     return {p->t_ev[kind][2 * i], p->t_ev[kind][2 * i + 1]};
 }
@@ -512,10 +515,11 @@ int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream) {
     return OASIS_OK;
 }
 
-int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity, uint32_t kinds) {
+int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity, uint32_t kinds, int32_t every) {
     clear_error();
     if (!p) PFAIL(OASIS_EINVAL, "pipeline is NULL");
     if (capacity < 0 || capacity > (1 << 20)) PFAIL(OASIS_EINVAL, "capacity = %d", capacity);
+    if (every < 1) PFAIL(OASIS_EINVAL, "every = %d < 1", every);
     if (kinds >> kTimedKinds) PFAIL(OASIS_EINVAL, "kinds = 0x%x (bits 0 .. %d)", kinds, kTimedKinds - 1);
     int rc = oasis_pipeline_drain(p);
     if (rc) return rc;
@@ -534,8 +538,10 @@ int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity, uint32_t kinds) {
             v.push_back(e);
         }
         p->t_n[k] = 0;
+        p->t_seen[k] = 0;
     }
     p->t_cap = capacity;
+    p->t_every = every;
     p->t_kinds = kinds;
     std::lock_guard<std::mutex> lk(p->t_mu);
     p->copy_host_s = 0.0;

@@ -204,11 +204,11 @@ class LayerPipeline:
         """(slot, block, n) tables that the attention of step t reads."""
         return self.layers[l].tbls[t % 3]
 
-    def enable_timing(self, capacity: int, kinds=("attn", "score", "topk", "plan")):
+    def enable_timing(self, capacity: int, kinds=("attn", "score", "topk", "plan"), every: int = 1):
         """Time up to `capacity` launches of each of `kinds` (attn, score,
-        topk, plan) with events on their own streams; clears earlier
-        totals."""
-        oa.oasis_pipeline_timing(self._h, capacity, sum(1 << TIMING_KINDS[k] for k in kinds))
+        topk, plan), one in every `every` of them, with events bound to
+        their kernels; clears earlier totals."""
+        oa.oasis_pipeline_timing(self._h, capacity, sum(1 << TIMING_KINDS[k] for k in kinds), every)
 
     def timing(self, kind: str):
         """(average microseconds, count) of the timed launches of `kind`."""

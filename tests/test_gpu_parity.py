@@ -499,3 +499,59 @@ def test_pipeline_timing_values_match_totals():
         assert abs(sum(vals) / count - avg) <= 1e-3 * avg + 1e-3, kind
     assert len(pipe.timing_values("attn", 2)) == 2
     pipe.close()
+
+
+@pytest.mark.parametrize("staged", [True, False])
+def test_pipeline_timing_rearm_keeps_results(staged):
+    """The timing events are bound to the launches they time, and re-arming
+    the timers binds them to later launches again.  Re-arming mid-run (with
+    one launch in every 2, then every 3, timed) changes no result: every
+    layer-step's attention output equals that of the same run without
+    timing, bit for bit, and each kind counts the launches its stride
+    picks."""
+    from prefetch_block_scoring_amd.pipeline import LayerPipeline
+    m = oa()
+    name = "qwen3_8b_16k_b128_staged" if staged else "qwen3_8b_16k_b32_hbm"
+    w = wl.WORKLOADS[name].shrink(B=3, ctx=(3000, 9000))
+    C = oracle.fetch_cap_blocks(w.cap, w.K_b) if staged else 0
+    L, steps = 3, 8
+    kinds = ("attn", "score", "topk", "plan") if staged else ("attn", "score", "topk")
+    ctx = wl.context_lengths(w).to(DEV)
+    if staged:
+        pool = m.oasis_host_empty((w.B, w.H_kv, w.NB_max, 2, w.bs, w.D))
+        pool.copy_(wl.kv_pool(w))
+    else:
+        pool = wl.kv_pool(w, device=DEV)
+    summ = m.oasis_build_summaries(pool, ctx)
+    looks = [wl.lookahead(w, s).to(DEV) for s in range(steps)]
+    attn_q = [looks[max(s - 1, 0)][:, 0].contiguous() for s in range(steps)]
+
+    def run(timing):
+        pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=staged,
+                             J=w.J)
+        outs, counts = [], None
+        if timing:
+            pipe.enable_timing(64, kinds)
+        for t in range(steps):
+            if timing and t in (3, 5):
+                pipe.enable_timing(64, kinds, every=2 if t == 3 else 3)
+            for l in range(L):
+                pipe.layer_step(l, t, looks[t], attn_q[t])
+                if t >= 1:
+                    # in stream order after the attention, without a host wait
+                    with torch.cuda.stream(pipe.main):
+                        outs.append(pipe.layers[l].out.clone())
+        if timing:
+            counts = {k: pipe.timing(k)[1] for k in kinds}
+        pipe.drain()
+        torch.cuda.synchronize()
+        pipe.close()
+        return outs, counts
+
+    timed_outs, counts = run(True)
+    plain_outs, _ = run(False)
+    assert len(timed_outs) == len(plain_outs) == (steps - 1) * L
+    for i, (a, b) in enumerate(zip(timed_outs, plain_outs)):
+        assert torch.equal(a, b), f"layer-step {i}"
+    # armed at step 5 with every = 3: steps 5..7 launch 3 * L of each kind
+    assert counts == {k: -(-(steps - 5) * L // 3) for k in kinds}
