@@ -64,11 +64,12 @@ def parse():
                    help="instead of the throughput run: the lookahead-agreement analogue (top-K overlap of the "
                         "draft-based selection with the next query's exact attention top-K, against drafting noise)")
     p.add_argument("--kernel-timing", default="attn", choices=["all", "attn"],
-                   help="launches of the timed steps that get timing events (two event records each, which "
-                        "slow a pipeline bound by the GPU); the others are timed in an extra pass afterwards")
+                   help="launches of the timed steps that get timing events (a start event recorded on the "
+                        "stream, which holds it ~3 us, and a stop event bound to the last kernel); the others "
+                        "are timed in an extra pass afterwards")
     p.add_argument("--timing-every", type=int, default=1,
-                   help="time one launch in every N of each timed kind during the timed steps (a timed launch "
-                        "carries a start event, which holds its queue ~5 us)")
+                   help="time one launch in every N of each timed kind during the timed steps (a timed launch's "
+                        "start event holds its queue ~3 us)")
     p.add_argument("--cap", type=float, default=None,
                    help="override the staged workload's fetch cap (fraction of the budget; >= 1 = fetch-all)")
     p.add_argument("--drift", type=float, default=None,

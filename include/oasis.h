@@ -566,23 +566,31 @@ typedef struct oasis_pipeline_desc {
                                  evictions, deferred admits and 1 (see
                                  oasis_stage_args.stats_accum); the caller
                                  clears it */
-    int32_t issue_threads;    /* staged pipelines whose chain has compute
-                                 streams of its own: 0 or 1 = one worker
+    int32_t issue_threads;    /* pipelines whose chain has compute streams
+                                 of its own: with issue threads one worker
                                  thread enqueues each layer-step's scores,
-                                 top-K and plan, another its copies, both
-                                 in submission order, and the calling
-                                 thread only the attention (a stream wait
-                                 on a pending event costs the enqueuing
-                                 thread 8-24 us, and a staged layer-step
-                                 needs three).  The workers make their
-                                 waits (the top-K's on the attention of
-                                 step t - 1, the copies' on their plan) on
-                                 the host, so those streams carry no
-                                 barrier packets.  -1 = the calling thread
-                                 enqueues everything.  Unstaged pipelines
-                                 and a chain on the main stream
-                                 (compute_streams = -1) always use the
-                                 calling thread. */
+                                 top-K and plan, another (staged) its
+                                 copies, both in submission order, and the
+                                 calling thread only the attention.  The
+                                 chain's cross-stream waits (the top-K's on
+                                 the attention of step t - 1, a gather's on
+                                 its plan) and, without staging, the
+                                 attention's on the selection of step t - 1
+                                 are then made on the host by the thread
+                                 that enqueues the waiting work, once what
+                                 it waits for is enqueued, so those queues
+                                 carry no barrier packets; without staging
+                                 THE CALLING THREAD MAY BLOCK in
+                                 oasis_pipeline_layer_step until the
+                                 selection of (layer, step - 1) is done.
+                                 0 = automatic: on for staged steps and for
+                                 unstaged steps whose attention and score
+                                 bytes take HBM at least 40 us; 1 = on;
+                                 -1 = off, the calling thread enqueues
+                                 everything, with stream waits.  A chain on
+                                 the main stream (compute_streams = -1)
+                                 always uses the calling thread
+                                 (oasis_pipeline_issue_threads tells). */
 } oasis_pipeline_desc;
 
 typedef struct oasis_pipeline oasis_pipeline;
@@ -601,8 +609,10 @@ int oasis_pipeline_create(const oasis_dims *dims,
  * staging for step t + 1 from q_look [B][J][H_q][D] bf16, device.  Steps of one layer must be
  * issued in order 0, 1, 2, ... (OASIS_EINVAL otherwise); layers may
  * interleave freely.  Inputs must stay valid until the work completes.
- * Blocks the caller only while the DMA worker has not yet enqueued the
- * copies of (layer, step - 1).  An error of the DMA worker is returned by
+ * It blocks the caller while a worker thread has not yet enqueued the
+ * copies (DMA engine; issue threads) or the selection (issue threads) of
+ * (layer, step - 1), and with issue threads and no staging until that
+ * selection has run on the GPU.  An error of a worker thread is returned by
  * the next call. */
 int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t layer, int32_t step,
                               const uint16_t *q_look, const uint16_t *q_attn,
@@ -620,17 +630,22 @@ int oasis_pipeline_drain(oasis_pipeline *p);
  * stream of odd layers (NULL where not used). */
 int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
 
+/* *on = 1 if the pipeline's chain and copies are enqueued by issue threads
+ * (the automatic choice, or issue_threads = 1), else 0. */
+int oasis_pipeline_issue_threads(oasis_pipeline *p, int32_t *on);
+
 /* Event timing of the steps: capacity > 0 (re)arms timing of up to
  * `capacity` launches of each kind whose bit is set in `kinds` and clears
  * the totals; capacity 0 or kinds 0 disables it.  Of each kind, one launch
  * in every `every` (>= 1) is timed, the first launch after arming
- * included.  Kinds: 0 attention (main
- * stream), 1 scores, 2 top-K, 3 staging plan (compute stream); each interval
- * runs from the start of the launch's first kernel to the end of its last.
- * The two timing events of a launch are bound to those kernels, so timing
- * adds nothing to the queues.  Re-arming first waits for everything the
- * pipeline has enqueued to finish.  timing_read synchronises on the events
- * and returns their total milliseconds and count. */
+ * included.  Kinds: 0 attention (main stream), 1 scores, 2 top-K, 3 staging
+ * plan (compute stream); each interval starts once the stream's earlier
+ * work and waits are done (a start event recorded on the stream, which
+ * holds it ~3 us) and ends with the launch's last kernel (a stop event
+ * bound to that kernel, which costs the queue nothing).  Re-arming first
+ * waits for everything the pipeline has enqueued to finish.  timing_read
+ * synchronises on the events and returns their total milliseconds and
+ * count. */
 int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity,
                           uint32_t kinds, int32_t every);
 int oasis_pipeline_timing_read(oasis_pipeline *p, int32_t kind,

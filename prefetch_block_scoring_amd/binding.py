@@ -120,6 +120,7 @@ _SIGNATURES = {
     "oasis_pipeline_layer_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P]),
     "oasis_pipeline_drain": (ctypes.c_int, [_P]),
     "oasis_pipeline_stream": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_void_p)]),
+    "oasis_pipeline_issue_threads": (ctypes.c_int, [_P, ctypes.POINTER(_I32)]),
     "oasis_pipeline_timing": (ctypes.c_int, [_P, _I32, ctypes.c_uint32, _I32]),
     "oasis_pipeline_timing_read": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(_I32)]),
@@ -694,6 +695,13 @@ def oasis_pipeline_stream(h: int, which: int) -> Optional[int]:
     s = ctypes.c_void_p()
     _check(_lib.oasis_pipeline_stream(h, int(which), ctypes.byref(s)))
     return s.value
+
+
+def oasis_pipeline_issue_threads(h: int) -> bool:
+    """Whether the pipeline's chain and copies are enqueued by issue threads."""
+    on = _I32()
+    _check(_lib.oasis_pipeline_issue_threads(h, ctypes.byref(on)))
+    return bool(on.value)
 
 
 def oasis_pipeline_timing(h: int, capacity: int, kinds: int = 0xF, every: int = 1):

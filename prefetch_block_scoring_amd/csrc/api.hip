@@ -153,12 +153,12 @@ int oasis_build_summaries(const oasis_dims *dims, const uint16_t *kv, const int3
 
 int oasis_score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J,
                        const uint16_t *kminmax, const int32_t *ctx_len, float *scores, void *stream) {
-    return score_blocks(dims, q_look, J, kminmax, ctx_len, scores, stream, {});
+    return score_blocks(dims, q_look, J, kminmax, ctx_len, scores, stream, nullptr);
 }
 
 int oasis_select_topk(const oasis_dims *dims, const float *scores, const int32_t *ctx_len, int32_t K_b,
                       int32_t *sel, int32_t *n_sel, void *stream) {
-    return select_topk(dims, scores, ctx_len, K_b, sel, n_sel, stream, {});
+    return select_topk(dims, scores, ctx_len, K_b, sel, n_sel, stream, nullptr);
 }
 
 }  // extern "C"
@@ -166,7 +166,7 @@ int oasis_select_topk(const oasis_dims *dims, const float *scores, const int32_t
 namespace oasis {
 
 int score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J, const uint16_t *kminmax,
-                 const int32_t *ctx_len, float *scores, void *stream, const LaunchEvents &ev) {
+                 const int32_t *ctx_len, float *scores, void *stream, hipEvent_t done) {
     clear_error();
     int rc = check_dims(dims);
     if (rc) return rc;
@@ -176,33 +176,33 @@ int score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J, cons
         FAIL(OASIS_EUNSUPPORTED, "B * H_kv * ceil(NB_max / 64) exceeds 2^31 - 1");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dims->B == 0) {
-        OASIS_HIP(record_events(ev, s));
+        OASIS_HIP(record_done(done, s));
         return OASIS_OK;
     }
     NEED(q_look);
     NEED(kminmax);
     NEED(ctx_len);
     NEED(scores);
-    OASIS_HIP(launch_score(*dims, q_look, J, kminmax, ctx_len, scores, s, ev));
+    OASIS_HIP(launch_score(*dims, q_look, J, kminmax, ctx_len, scores, s, done));
     return OASIS_OK;
 }
 
 int select_topk(const oasis_dims *dims, const float *scores, const int32_t *ctx_len, int32_t K_b, int32_t *sel,
-                int32_t *n_sel, void *stream, const LaunchEvents &ev) {
+                int32_t *n_sel, void *stream, hipEvent_t done) {
     clear_error();
     int rc = check_dims(dims);
     if (rc) return rc;
     if (K_b < 1) FAIL(OASIS_EINVAL, "K_b = %d < 1", K_b);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dims->B == 0) {
-        OASIS_HIP(record_events(ev, s));
+        OASIS_HIP(record_done(done, s));
         return OASIS_OK;
     }
     NEED(scores);
     NEED(ctx_len);
     NEED(sel);
     NEED(n_sel);
-    OASIS_HIP(launch_topk(*dims, scores, ctx_len, K_b, sel, n_sel, s, ev));
+    OASIS_HIP(launch_topk(*dims, scores, ctx_len, K_b, sel, n_sel, s, done));
     return OASIS_OK;
 }
 
@@ -343,12 +343,11 @@ static int check_copy_args(const oasis_dims *dims, const oasis_stage_args *a) {
     return OASIS_OK;
 }
 
-// `start` (optional) completes as the plan kernel starts; `plan_event`
-// completes with the prefix kernel.
-static int stage_plan_phase(const oasis_dims *dims, const oasis_stage_args *a, hipEvent_t start = nullptr) {
+// `plan_event` is bound to the prefix kernel that ends the plan.
+static int stage_plan_phase(const oasis_dims *dims, const oasis_stage_args *a) {
     hipStream_t s = static_cast<hipStream_t>(a->stream);
-    OASIS_HIP(launch_stage_plan(*dims, *a, s, {start, nullptr}));
-    OASIS_HIP(launch_stage_prefix(*dims, *a, s, {nullptr, static_cast<hipEvent_t>(a->plan_event)}));
+    OASIS_HIP(launch_stage_plan(*dims, *a, s));
+    OASIS_HIP(launch_stage_prefix(*dims, *a, s, static_cast<hipEvent_t>(a->plan_event)));
     return OASIS_OK;
 }
 
@@ -387,7 +386,7 @@ static int stage_copy_phase(const oasis_dims *dims, const oasis_stage_args *a, c
     if (a->copy_mode == OASIS_COPY_KERNEL) {
         if (!in_order) OASIS_HIP(stream_wait(cs, plan_ready));
         if (a->wait_event) OASIS_HIP(stream_wait(cs, static_cast<hipEvent_t>(a->wait_event)));
-        OASIS_HIP(launch_stage_gather(*dims, *a, pool_dev, cs, {nullptr, done}));
+        OASIS_HIP(launch_stage_gather(*dims, *a, pool_dev, cs, done));
     } else {
         if ((rc = stage_dma(*dims, *a, plan_ready, cs))) return rc;
         if (done) OASIS_HIP(hipEventRecord(done, cs));
@@ -395,22 +394,16 @@ static int stage_copy_phase(const oasis_dims *dims, const oasis_stage_args *a, c
     return OASIS_OK;
 }
 
-int oasis_stage_plan(const oasis_dims *dims, const oasis_stage_args *a) { return stage_plan(dims, a, nullptr); }
-
-}  // extern "C"
-
-int oasis::stage_plan(const oasis_dims *dims, const oasis_stage_args *a, hipEvent_t start) {
+int oasis_stage_plan(const oasis_dims *dims, const oasis_stage_args *a) {
     clear_error();
     int rc = check_plan_args(dims, a);
     if (rc) return rc;
     if (dims->B == 0) {
-        OASIS_HIP(record_events({start, static_cast<hipEvent_t>(a->plan_event)}, static_cast<hipStream_t>(a->stream)));
+        OASIS_HIP(record_done(static_cast<hipEvent_t>(a->plan_event), static_cast<hipStream_t>(a->stream)));
         return OASIS_OK;
     }
-    return stage_plan_phase(dims, a, start);
+    return stage_plan_phase(dims, a);
 }
-
-extern "C" {
 
 int oasis_stage_copy(const oasis_dims *dims, const oasis_stage_args *a) {
     clear_error();
@@ -484,7 +477,7 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
                          int32_t T, const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,
                          size_t ws_bytes, int32_t n_split, void *stream) {
     return lookahead_attn(dims, n_q, q, kv_pool, P, tbl_slot, tbl_block, tbl_n, T, ctx_len, sm_scale, out, lse, ws,
-                          ws_bytes, n_split, stream, {});
+                          ws_bytes, n_split, stream, nullptr);
 }
 
 }  // extern "C"
@@ -492,7 +485,7 @@ int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q,
 int oasis::lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q, const uint16_t *kv_pool, int32_t P,
                           const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n, int32_t T,
                           const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,
-                          size_t ws_bytes, int32_t n_split, void *stream, const LaunchEvents &ev) {
+                          size_t ws_bytes, int32_t n_split, void *stream, hipEvent_t done) {
     clear_error();
     int rc = check_dims(dims);
     if (rc) return rc;
@@ -506,7 +499,7 @@ int oasis::lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q
     if (!std::isfinite(sm_scale)) FAIL(OASIS_EINVAL, "sm_scale is not finite");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dims->B == 0) {
-        OASIS_HIP(record_events(ev, s));
+        OASIS_HIP(record_done(done, s));
         return OASIS_OK;
     }
     NEED(q);
@@ -525,7 +518,7 @@ int oasis::lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q
         if (ws_bytes < need) FAIL(OASIS_ENOSPACE, "attention workspace %zu bytes < %zu", ws_bytes, need);
     }
     OASIS_HIP(launch_attn(*dims, n_q, q, kv_pool, P, tbl_slot, tbl_block, tbl_n, T, ctx_len, sm_scale, out, lse,
-                          static_cast<float *>(ws), splits, s, ev));
+                          static_cast<float *>(ws), splits, s, done));
     return OASIS_OK;
 }
 

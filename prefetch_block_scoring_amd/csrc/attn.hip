@@ -583,9 +583,9 @@ __global__ __launch_bounds__(kD) void attn_combine_kernel(const float *__restric
 }
 
 template <int GP>
-hipError_t launch_g(const oasis_dims &d, const AttnArgs &a, hipStream_t s, const LaunchEvents &ev) {
+hipError_t launch_g(const oasis_dims &d, const AttnArgs &a, hipStream_t s, hipEvent_t done) {
     dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)a.n_split);
-    hipExtLaunchKernelGGL(attn_kernel<GP>, grid, dim3(kThreads), 0, s, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL(attn_kernel<GP>, grid, dim3(kThreads), 0, s, nullptr, done, 0, a);
     return hipGetLastError();
 }
 
@@ -650,7 +650,7 @@ size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split) {
 hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q, const uint16_t *kv_pool, int P,
                        const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n,
                        int T, const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse,
-                       float *ws, int n_split, hipStream_t s, const LaunchEvents &ev) {
+                       float *ws, int n_split, hipStream_t s, hipEvent_t done) {
     AttnArgs a;
     a.q = q;
     a.kv = kv_pool;
@@ -669,8 +669,8 @@ hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q, const ui
     a.lse = lse;
     a.ws = ws;
     const int NC = n_q * (d.H_q / d.H_kv);
-    // `start` on the first kernel, `stop` on the last (the combine, if any)
-    const LaunchEvents first{ev.start, n_split <= 1 ? ev.stop : nullptr};
+    // `done` on the last kernel (the combine, if any)
+    hipEvent_t first = n_split <= 1 ? done : nullptr;
     hipError_t e;
     if (NC <= 1) e = launch_g<1>(d, a, s, first);
     else if (NC <= 2) e = launch_g<2>(d, a, s, first);
@@ -678,12 +678,12 @@ hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q, const ui
     else if (NC <= 8) e = launch_g<8>(d, a, s, first);
     else {
         dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)n_split);
-        hipExtLaunchKernelGGL(attn_pv_kernel, grid, dim3(kThreads), 0, s, first.start, first.stop, 0, a);
+        hipExtLaunchKernelGGL(attn_pv_kernel, grid, dim3(kThreads), 0, s, nullptr, first, 0, a);
         e = hipGetLastError();
     }
     if (e != hipSuccess || n_split <= 1) return e;
     hipExtLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(d.B * n_q * d.H_q)), dim3(kD), 0, s, nullptr,
-                          ev.stop, 0, ws, n_split, out, lse);
+                          done, 0, ws, n_split, out, lse);
     return hipGetLastError();
 }
 

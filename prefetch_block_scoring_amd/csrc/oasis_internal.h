@@ -49,30 +49,26 @@ int device_view(const void *p, const void **out, const char *name);
 // ---------------------------------------------------------------- launchers
 // Each launcher assumes its arguments were validated by the C entry point.
 
-// Events bound to a launcher's kernel dispatches (hipExtLaunchKernelGGL):
-// `start` completes as the first kernel starts, `stop` as the last one ends,
-// with the kernels' timestamps.  A bound event costs the queue nothing, where
-// a hipEventRecord after the kernel adds a marker packet that holds the
-// queue ~3 us on MI355X (ROCm 7.2; 24.1 against 21.0 us per 20 us kernel
-// back to back).  A launcher that launches nothing records both on the
-// stream instead (record_events), so they still complete in stream order.
-struct LaunchEvents {
-    hipEvent_t start = nullptr, stop = nullptr;
-};
-hipError_t record_events(const LaunchEvents &ev, hipStream_t s);
+// `done` (optional): an event bound to a launcher's last kernel dispatch
+// (hipExtLaunchKernelGGL stop event), completing as that kernel ends, with
+// its timestamp.  A bound event costs the queue nothing, where a
+// hipEventRecord after the kernel adds a marker packet that holds the queue
+// ~3 us on MI355X (ROCm 7.2; 24.1 against 21.0 us per 20 us kernel back to
+// back).  (Binding a start event as well would cost the enqueuing thread
+// 9-19 us per launch.)  A launcher that launches nothing records `done` on
+// the stream instead (record_done), so it still completes in stream order.
+hipError_t record_done(hipEvent_t done, hipStream_t s);
 
-// The entry points of the same names with events bound to their kernels (the
-// layer pipeline's completion and timing events).  stage_plan: `start` on the
-// plan kernel, args.plan_event on the prefix kernel that ends the plan.
+// The entry points of the same names with `done` bound to their last kernel
+// (the layer pipeline's completion and timing events).
 int score_blocks(const oasis_dims *dims, const uint16_t *q_look, int32_t J, const uint16_t *kminmax,
-                 const int32_t *ctx_len, float *scores, void *stream, const LaunchEvents &ev);
+                 const int32_t *ctx_len, float *scores, void *stream, hipEvent_t done);
 int select_topk(const oasis_dims *dims, const float *scores, const int32_t *ctx_len, int32_t K_b, int32_t *sel,
-                int32_t *n_sel, void *stream, const LaunchEvents &ev);
-int stage_plan(const oasis_dims *dims, const oasis_stage_args *a, hipEvent_t start);
+                int32_t *n_sel, void *stream, hipEvent_t done);
 int lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q, const uint16_t *kv_pool, int32_t P,
                    const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n, int32_t T,
                    const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,
-                   int32_t n_split, void *stream, const LaunchEvents &ev);
+                   int32_t n_split, void *stream, hipEvent_t done);
 
 hipError_t launch_build_summaries(const oasis_dims &d, const uint16_t *kv,
                                   const int32_t *ctx_len, uint16_t *kminmax,
@@ -80,18 +76,18 @@ hipError_t launch_build_summaries(const oasis_dims &d, const uint16_t *kv,
 
 hipError_t launch_score(const oasis_dims &d, const uint16_t *q_look, int J,
                         const uint16_t *kminmax, const int32_t *ctx_len,
-                        float *scores, hipStream_t s, const LaunchEvents &ev = {});
+                        float *scores, hipStream_t s, hipEvent_t done = nullptr);
 
 hipError_t launch_topk(const oasis_dims &d, const float *scores,
                        const int32_t *ctx_len, int K_b, int32_t *sel,
-                       int32_t *n_sel, hipStream_t s, const LaunchEvents &ev = {});
+                       int32_t *n_sel, hipStream_t s, hipEvent_t done = nullptr);
 
 hipError_t launch_stage_plan(const oasis_dims &d, const oasis_stage_args &a,
-                             hipStream_t s, const LaunchEvents &ev = {});
+                             hipStream_t s);
 
 hipError_t launch_stage_gather(const oasis_dims &d, const oasis_stage_args &a,
                                const void *host_pool_dev, hipStream_t s,
-                               const LaunchEvents &ev = {});
+                               hipEvent_t done = nullptr);
 
 hipError_t launch_append(const oasis_dims &d, const uint16_t *k_new,
                          const uint16_t *v_new, int32_t *ctx_len,
@@ -124,7 +120,7 @@ hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q,
                        const int32_t *tbl_block, const int32_t *tbl_n, int T,
                        const int32_t *ctx_len, float sm_scale, uint16_t *out,
                        float *lse, float *ws, int n_split, hipStream_t s,
-                       const LaunchEvents &ev = {});
+                       hipEvent_t done = nullptr);
 
 // Plan workspace: per (r, h) a row of int32
 //   [0] admits, [1] evictions, [2] packed position of the first admit (the
@@ -139,7 +135,7 @@ __host__ __device__ inline int plan_row(int C) { return kPlanHead + 2 * (C > 0 ?
 inline size_t plan_ints(int pairs, int C) { return (size_t)pairs * plan_row(C) + kPlanTail; }
 
 hipError_t launch_stage_prefix(const oasis_dims &d, const oasis_stage_args &a, hipStream_t s,
-                               const LaunchEvents &ev = {});
+                               hipEvent_t done = nullptr);
 
 // Copy the admitted blocks of packed positions [lo, hi) from the device
 // staging buffer (position lo at its start) into their working-set slots.

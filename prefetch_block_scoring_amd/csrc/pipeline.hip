@@ -34,6 +34,9 @@ constexpr int kRing = 4;
 constexpr double kLinkBytesPerS = 57e9;
 constexpr double kHbmBytesPerS = 6e12;
 constexpr double kSummaryBytes = 2 * kD * 2;  // one block's min and max key, bf16
+// GPU time (HBM, seconds) of an unstaged layer-step from which on the issue
+// threads' host waits pay (see oasis_pipeline_create)
+constexpr double kMinThreadedStepS = 40e-6;
 constexpr int kTimedKinds = 4;
 
 struct Job {
@@ -102,15 +105,19 @@ namespace {
         return (code);                                    \
     } while (0)
 
-// The timing events of the next launch of `kind`, bound to its kernels, or
-// none when that kind is not timed (or its capacity is used up).  Kind 0 is
-// taken by the calling thread, kinds 1-3 by whichever thread issues the
-// chain.
-LaunchEvents timed(oasis_pipeline *p, int kind) {
-    if (!(p->t_kinds >> kind & 1u) || p->t_n[kind] >= p->t_cap) return {};
-    if (p->t_seen[kind]++ % p->t_every != 0) return {};
+// Timing of the next launch of `kind` on stream s: records its start event
+// on s (a marker, ~3 us of queue time; binding a start event to the kernel
+// would cost the enqueuing thread 9-19 us per launch) and returns its stop
+// event, to be bound to the launch's last kernel.  nullptr when the launch is
+// not timed (kind not armed, not one in `every`, or capacity used up).
+// Kind 0 is taken by the calling thread, kinds 1-3 by whichever thread issues
+// the chain.
+hipEvent_t timed(oasis_pipeline *p, int kind, hipStream_t s) {
+    if (!(p->t_kinds >> kind & 1u) || p->t_n[kind] >= p->t_cap) return nullptr;
+    if (p->t_seen[kind]++ % p->t_every != 0) return nullptr;
     const int i = p->t_n[kind]++;
-    return {p->t_ev[kind][2 * i], p->t_ev[kind][2 * i + 1]};
+    (void)hipEventRecord(p->t_ev[kind][2 * i], s);
+    return p->t_ev[kind][2 * i + 1];
 }
 
 // The copy half of staging for one job; called by the calling thread
@@ -318,12 +325,26 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
             return fail(e, "hipEventCreateWithFlags");
     // issue threads: the chain and the copies are enqueued by two worker
     // threads of their own, so that the calling thread enqueues only the
-    // attention.  A stream wait on an event that is still pending costs the
-    // thread that enqueues it 8 to 24 us on MI355X (ROCm 7.2), and a staged
-    // layer-step makes three of them (for the attention, before the top-K,
-    // before the copies): with all of them on the calling thread, a layer with
-    // few (request, KV head) pairs is bound by that thread.
-    p->threaded = ds.staged && !p->comp_on_main && ds.issue_threads >= 0;
+    // attention, and the cross-stream waits of the chain (the top-K's on the
+    // attention of step t - 1, a gather's on its plan) and, without staging,
+    // the attention's on the selection of step t - 1 are made on the host by
+    // the thread that enqueues the waiting work, after the work it waits for
+    // was enqueued.  Those queues then carry no barrier packets, each of
+    // which holds its queue ~3 us even when its event has completed, and a
+    // stream wait on a pending event costs the enqueuing thread 8 to 24 us
+    // (MI355X, ROCm 7.2).  A host wait on work that is still running adds a
+    // GPU -> host -> GPU round trip (10-20 us) to that dependency, which a
+    // layer-step hides only when its GPU work is much longer: automatic
+    // (issue_threads = 0) uses them for staged steps and for steps whose
+    // attention and scores take HBM at least 40 us.  Measured: the ragged
+    // 32B-class staged layer 155k -> 176k tok/s (with the events bound to
+    // the kernels); Qwen3-8B in HBM at batch 32 (67 us) 388k -> 414k; the
+    // B = 1 parity layer (0.4 us) 35.7k -> 23.9k with them.
+    const double step_hbm_s = (double)dims->B * dims->H_kv *
+                              ((double)ds.K_b * kBlockBytes + (double)dims->NB_max * kSummaryBytes) / kHbmBytesPerS;
+    const bool want_threads =
+        ds.issue_threads > 0 || (ds.issue_threads == 0 && (ds.staged || step_hbm_s >= kMinThreadedStepS));
+    p->threaded = !p->comp_on_main && want_threads;
     if (p->threaded) {
         p->chain.start(
             ds.n_layers,
@@ -367,7 +388,8 @@ static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look, 
     const int mode = layer_copy_mode(ds, l);
     int rc;
     hipStream_t cs = p->comp[p->comp[1] ? (l & 1) : 0];
-    if ((rc = score_blocks(d, q_look, ds.J, ds.kminmax, ds.ctx_len, b.scores, cs, timed(p, 1)))) return rc;
+    const hipEvent_t sc = timed(p, 1, cs);
+    if ((rc = score_blocks(d, q_look, ds.J, ds.kminmax, ds.ctx_len, b.scores, cs, sc))) return rc;
     if (t >= 2) {
         // unstaged: sel[j], read by the attention of step t - 1.  Staged: the
         // attention of step t - 1 covers every later reuse: table
@@ -389,11 +411,13 @@ static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look, 
             OASIS_HIP(stream_wait(cs, attn_prev));
         }
     }
-    LaunchEvents tk = timed(p, 2);
-    if (!ds.staged && !tk.stop) tk.stop = p->event(kEvSel, l, t);
+    hipEvent_t tk = timed(p, 2, cs);
+    if (!ds.staged && !tk) tk = p->event(kEvSel, l, t);
     if ((rc = select_topk(d, b.scores, ds.ctx_len, K_b, b.sel[j], b.n_sel[j], cs, tk))) return rc;
     if (!ds.staged) {
-        p->sel_last[l] = tk.stop;  // unstaged chains run on the calling thread
+        // read by the calling thread at step t + 1 (after the chain worker has
+        // run this job, when there is one)
+        p->sel_last[l] = tk;
         return OASIS_OK;
     }
 
@@ -435,10 +459,10 @@ static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look, 
     // the copies follow the plan, which followed the attention of step t - 1
     a.wait_event = nullptr;
     a.done_event = p->event(kEvStage, l, t);
-    const LaunchEvents pe = timed(p, 3);
-    a.plan_event = pe.stop ? pe.stop : p->event(kEvPlan, l, t);
+    const hipEvent_t pe = timed(p, 3, cs);
+    a.plan_event = pe ? pe : p->event(kEvPlan, l, t);
     a.stats_accum = ds.stage_stats;
-    if ((rc = stage_plan(d, &a, pe.start))) return rc;
+    if ((rc = oasis_stage_plan(d, &a))) return rc;
     if (mode == OASIS_COPY_DMA || p->threaded) {
         p->copies.push(job);
     } else if ((rc = run_copy(p, job))) {
@@ -466,26 +490,39 @@ int oasis_pipeline_layer_step(oasis_pipeline *p, int32_t l, int32_t t, const uin
     // foreground: attention of step t
     const hipEvent_t attn_prev = p->attn_last[l];
     if (t >= 1) {
-        LaunchEvents ev = timed(p, 0);
-        if (!ev.stop) ev.stop = p->event(kEvAttn, l, t);
+        hipEvent_t done = nullptr;
         if (ds.staged) {
             // the copy worker has recorded the copies of step t - 1
             if (mode == OASIS_COPY_DMA || p->threaded) (void)p->copies.wait_done(l, t - 1);
             if ((rc = worker_error(p))) return rc;
             OASIS_HIP(stream_wait(p->main, p->event(kEvStage, l, t - 1)));
             const int k = t % 3;
+            done = timed(p, 0, p->main);
+            if (!done) done = p->event(kEvAttn, l, t);
             rc = lookahead_attn(d, ds.n_q, q_attn, b.ws_pool, p->S, b.tbl_slot[k], b.tbl_block[k], b.tbl_n[k], K_b,
                                 ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes, ds.n_split, p->main,
-                                ev);
+                                done);
         } else {
             const int jp = (t - 1) % 2;
-            if (p->sel_last[l]) OASIS_HIP(stream_wait(p->main, p->sel_last[l]));
+            if (p->threaded) {
+                // the chain worker has bound the selection event of step t - 1;
+                // the wait itself is made on the host, so that the main stream
+                // carries only attention launches (a barrier packet holds a
+                // queue ~3 us even when its event has completed)
+                (void)p->chain.wait_done(l, t - 1);
+                if ((rc = worker_error(p))) return rc;
+                if (p->sel_last[l]) OASIS_HIP(hipEventSynchronize(p->sel_last[l]));
+            } else if (p->sel_last[l]) {
+                OASIS_HIP(stream_wait(p->main, p->sel_last[l]));
+            }
+            done = timed(p, 0, p->main);
+            if (!done) done = p->event(kEvAttn, l, t);
             rc = lookahead_attn(d, ds.n_q, q_attn, ds.pool, d->NB_max, b.sel[jp], b.sel[jp], b.n_sel[jp], K_b,
                                 ds.ctx_len, ds.sm_scale, out, lse, b.attn_ws, b.attn_ws_bytes, ds.n_split, p->main,
-                                ev);
+                                done);
         }
         if (rc) return rc;
-        p->attn_last[l] = ev.stop;
+        p->attn_last[l] = done;
     }
 
     p->next_step[l] = t + 1;
@@ -512,6 +549,13 @@ int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream) {
               : which == 1 ? (void *)p->comp[0]
               : which == 4 ? (void *)p->comp[1]
                            : (void *)p->copy[which - 2];
+    return OASIS_OK;
+}
+
+int oasis_pipeline_issue_threads(oasis_pipeline *p, int32_t *on) {
+    clear_error();
+    if (!p || !on) PFAIL(OASIS_EINVAL, "pipeline or on is NULL");
+    *on = p->threaded ? 1 : 0;
     return OASIS_OK;
 }
 

@@ -342,11 +342,11 @@ int score_grid(int n_items) {
 
 hipError_t launch_score(const oasis_dims &d, const uint16_t *q_look, int J,
                         const uint16_t *kminmax, const int32_t *ctx_len,
-                        float *scores, hipStream_t s, const LaunchEvents &ev) {
+                        float *scores, hipStream_t s, hipEvent_t done) {
     const int chunks = (d.NB_max + kItemBlocks - 1) / kItemBlocks;
     const int n_items = d.B * d.H_kv * chunks;  // at most this many items hold blocks
-    hipExtLaunchKernelGGL(score_kernel, dim3((unsigned)score_grid(n_items)), dim3(kThreads), 0, s, ev.start,
-                          ev.stop, 0, q_look, J, d.H_q, d.H_kv, reinterpret_cast<const uint4 *>(kminmax), ctx_len,
+    hipExtLaunchKernelGGL(score_kernel, dim3((unsigned)score_grid(n_items)), dim3(kThreads), 0, s, nullptr,
+                          done, 0, q_look, J, d.H_q, d.H_kv, reinterpret_cast<const uint4 *>(kminmax), ctx_len,
                           scores, d.NB_max, d.B);
     return hipGetLastError();
 }

@@ -452,8 +452,7 @@ size_t stage_plan_lds_bytes(int S, int K_sel) {
     return (size_t)(5 * S + 5 * K_sel) * sizeof(int);
 }
 
-hipError_t launch_stage_plan(const oasis_dims &d, const oasis_stage_args &a, hipStream_t s,
-                             const LaunchEvents &ev) {
+hipError_t launch_stage_plan(const oasis_dims &d, const oasis_stage_args &a, hipStream_t s) {
     PlanArgs p;
     p.sel = a.sel;
     p.n_sel = a.n_sel;
@@ -472,14 +471,14 @@ hipError_t launch_stage_plan(const oasis_dims &d, const oasis_stage_args &a, hip
     p.plan = a.plan;
     p.H_kv = d.H_kv;
     p.NB_max = d.NB_max;
-    hipExtLaunchKernelGGL(stage_plan_kernel, dim3((unsigned)(d.B * d.H_kv)), dim3(kThreads),
-                          stage_plan_lds_bytes(a.S, a.K_sel), s, ev.start, ev.stop, 0, p);
+    hipLaunchKernelGGL(stage_plan_kernel, dim3((unsigned)(d.B * d.H_kv)), dim3(kThreads),
+                       stage_plan_lds_bytes(a.S, a.K_sel), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_stage_prefix(const oasis_dims &d, const oasis_stage_args &a, hipStream_t s,
-                               const LaunchEvents &ev) {
-    hipExtLaunchKernelGGL(stage_prefix_kernel, dim3(1), dim3(1024), 0, s, ev.start, ev.stop, 0, a.plan,
+                               hipEvent_t done) {
+    hipExtLaunchKernelGGL(stage_prefix_kernel, dim3(1), dim3(1024), 0, s, nullptr, done, 0, a.plan,
                           plan_row(a.C), d.B * d.H_kv, reinterpret_cast<unsigned long long *>(a.stats_accum));
     return hipGetLastError();
 }
@@ -496,12 +495,12 @@ hipError_t launch_stage_scatter(const oasis_dims &d, const oasis_stage_args &a, 
 }
 
 hipError_t launch_stage_gather(const oasis_dims &d, const oasis_stage_args &a,
-                               const void *host_pool_dev, hipStream_t s, const LaunchEvents &ev) {
-    if (a.C <= 0) return record_events(ev, s);
+                               const void *host_pool_dev, hipStream_t s, hipEvent_t done) {
+    if (a.C <= 0) return record_done(done, s);
     const long most = (long)d.B * d.H_kv * a.C;  // admits of the step are at most this many
     const int want = most <= kFewAdmits ? kGatherWgsFew : kGatherWgs;
     const int wgs = most < want ? (int)most : want;
-    hipExtLaunchKernelGGL(stage_gather_kernel, dim3((unsigned)wgs), dim3(256), 0, s, ev.start, ev.stop, 0, a.plan,
+    hipExtLaunchKernelGGL(stage_gather_kernel, dim3((unsigned)wgs), dim3(256), 0, s, nullptr, done, 0, a.plan,
                           plan_row(a.C), d.B * d.H_kv, a.C, reinterpret_cast<const uint4 *>(host_pool_dev),
                           reinterpret_cast<uint4 *>(a.ws_pool), d.NB_max, a.S);
     return hipGetLastError();

@@ -150,14 +150,7 @@ hipError_t stream_wait(hipStream_t s, hipEvent_t e) {
     return hipStreamWaitEvent(s, e, 0);
 }
 
-hipError_t record_events(const LaunchEvents &ev, hipStream_t s) {
-    for (hipEvent_t e : {ev.start, ev.stop})
-        if (e) {
-            const hipError_t r = hipEventRecord(e, s);
-            if (r != hipSuccess) return r;
-        }
-    return hipSuccess;
-}
+hipError_t record_done(hipEvent_t done, hipStream_t s) { return done ? hipEventRecord(done, s) : hipSuccess; }
 
 int stage_dma(const oasis_dims &d, const oasis_stage_args &a, hipEvent_t plan_ready, hipStream_t cs) {
     const int pairs = d.B * d.H_kv;

@@ -177,9 +177,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
 }  // namespace
 
 hipError_t launch_topk(const oasis_dims &d, const float *scores, const int32_t *ctx_len,
-                       int K_b, int32_t *sel, int32_t *n_sel, hipStream_t s, const LaunchEvents &ev) {
+                       int K_b, int32_t *sel, int32_t *n_sel, hipStream_t s, hipEvent_t done) {
     const size_t lds = (size_t)d.NB_max * sizeof(uint32_t);
-    hipExtLaunchKernelGGL(topk_kernel, dim3((unsigned)(d.B * d.H_kv)), dim3(kThreads), lds, s, ev.start, ev.stop, 0,
+    hipExtLaunchKernelGGL(topk_kernel, dim3((unsigned)(d.B * d.H_kv)), dim3(kThreads), lds, s, nullptr, done, 0,
                           scores, ctx_len, d.H_kv, d.NB_max, K_b, sel, n_sel);
     return hipGetLastError();
 }

@@ -19,9 +19,12 @@ lays that out on one GPU's streams:
                   copy + scatter, or, mixed, DMA for even layers and gathers
                   for odd layers)
 
-With staging and compute streams of its own, the chain and the copies of a
-layer-step are enqueued by the pipeline's two issue threads, and the calling
-thread enqueues only the attention (`issue_threads`).
+With compute streams of its own, the chain and the copies of a layer-step
+are enqueued by the pipeline's two issue threads, which make the chain's
+cross-stream waits on the host, and the calling thread enqueues only the
+attention (`issue_threads`: automatic for staged steps and for unstaged
+steps with at least ~40 us of HBM work; without staging the calling thread
+then waits on the host for the selection its attention reads).
 
 `LayerPipeline` allocates the per-layer buffers the native pipeline works in
 (three attention tables, two selections and two plan buffers per layer, the
@@ -152,9 +155,8 @@ class LayerPipeline:
         self.comp = self.main if on_main else torch.cuda.ExternalStream(c1)
         self._comp_odd = torch.cuda.ExternalStream(odd) if odd else self.comp
         self.compute_streams = -1 if on_main else (2 if odd else 1)
-        # whether worker threads enqueue the chain and the copies (the
-        # library's rule for issue_threads)
-        self.issue_threads = bool(staged and not on_main and issue_threads >= 0)
+        # whether worker threads enqueue the chain and the copies
+        self.issue_threads = oa.oasis_pipeline_issue_threads(self._h)
         self.copy = [torch.cuda.ExternalStream(c) for c in
                      (oa.oasis_pipeline_stream(self._h, k) for k in (2, 3)) if c]
 

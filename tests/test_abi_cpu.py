@@ -224,6 +224,7 @@ def test_pipeline_calls_reject_null_handles():
     assert lib.oasis_pipeline_layer_step(None, 0, 0, None, None, None, None) == oa.OASIS_EINVAL
     assert lib.oasis_pipeline_drain(None) == oa.OASIS_EINVAL
     assert lib.oasis_pipeline_timing(None, 4, 1, 1) == oa.OASIS_EINVAL
+    assert lib.oasis_pipeline_issue_threads(None, None) == oa.OASIS_EINVAL
     assert lib.oasis_pipeline_destroy(None) == oa.OASIS_OK
 
 

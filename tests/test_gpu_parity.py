@@ -470,6 +470,50 @@ def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams, issue_
                 assert_attn_close(got[:, qi], ref)
 
 
+@pytest.mark.parametrize("compute_streams,issue_threads", [(0, 0), (0, 1), (2, 1), (2, -1)])
+def test_unstaged_pipeline_matches_oracle(compute_streams, issue_threads):
+    """The pipeline with K/V in HBM (no staging), three layers in flight:
+    every layer's attention at step t + 1 over the blocks the oracle selects
+    at step t equals the oracle's.  issue_threads 1: a worker thread enqueues
+    the scores and top-K, and the calling thread waits for the selection of
+    step t - 1 on the host before it enqueues the attention; -1: stream
+    waits; 0: automatic, off for a layer-step this small.  compute_streams 0
+    is the automatic choice (one stream)."""
+    from prefetch_block_scoring_amd.pipeline import LayerPipeline
+    w = wl.WORKLOADS["qwen3_8b_16k_b32_hbm"].shrink(B=3, ctx=(3000, 9000))
+    L, steps = 3, 6
+    ctx_cpu = wl.context_lengths(w)
+    ctx = ctx_cpu.to(DEV)
+    pool = wl.kv_pool(w, device=DEV)
+    summ = oa().oasis_build_summaries(pool, ctx)
+    looks = [wl.lookahead(w, s).to(DEV) for s in range(steps + 2 * L)]
+    attn_q = [looks[max(s - 1, 0)][:, 0].contiguous() for s in range(steps + 2 * L)]
+    pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=0, n_layers=L, staged=False, J=w.J,
+                         compute_streams=compute_streams, issue_threads=issue_threads)
+    assert pipe.compute_streams == (compute_streams or 1)
+    assert pipe.issue_threads == (issue_threads == 1)
+    outs = {}
+    for t in range(steps):
+        for l in range(L):
+            s = t + 2 * l
+            pipe.layer_step(l, t, looks[s], attn_q[s])
+            if t >= 1:
+                with torch.cuda.stream(pipe.main):
+                    outs[(l, t)] = pipe.layers[l].out.clone()
+    pipe.close()
+    torch.cuda.synchronize()
+    ctx_np = ctx_cpu.numpy()
+    kv = u16(pool)
+    summ_o = oracle.build_summaries(kv, ctx_np, w.bs)
+    for l in range(L):
+        for t in range(steps - 1):
+            s = t + 2 * l
+            sc = oracle.score(u16(looks[s]), summ_o, ctx_np, w.bs, w.H_kv)
+            sel, n = oracle.select(sc, ctx_np, w.bs, w.K_b)
+            ref, _ = oracle.attend(u16(attn_q[s + 1]), kv, ctx_np, sel, n, 1 / math.sqrt(w.D))
+            assert_attn_close(bf16_to_f64(u16(outs[(l, t + 1)])), ref)
+
+
 def test_pipeline_timing_values_match_totals():
     """Per-launch timings of the native pipeline: one value per timed launch
     of each kind (attention from step 1 on), all positive, summing to the
