@@ -544,8 +544,8 @@ typedef struct oasis_pipeline_desc {
                                  stream only adds a second score kernel
                                  beside the attention on HBM); staged, -1
                                  for a step that is bound by the link (C
-                                 blocks of 8 KiB at 57 GB/s take over 2.5
-                                 times as long as the pair's K_b blocks
+                                 blocks of 8 KiB at 57 GB/s take over
+                                 twice as long as the pair's K_b blocks
                                  and NB_max summaries of 512 B at 6 TB/s)
                                  and has at least as many (request, KV
                                  head) pairs as the device has compute

@@ -287,16 +287,17 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     // one another, only beside the copies, and the hardware queues go to two
     // gather streams.  The Qwen3-8B layer at batch 128 (1024 pairs, K_b 128,
     // 1024 blocks of context), fetch cap C blocks per pair per step, tok/s
-    // with the chain on the main stream / two compute streams: C = 3: 205k /
-    // 268k, C = 4: 175k / 205k, C = 6: 160k / 151k.  The link time of C blocks
-    // per pair over the HBM time of the pair's attention and score bytes is
-    // 2.2 at C = 4 and 3.3 at C = 6; the rule below switches at 2.5.
+    // with the chain on the main stream / two compute streams: C = 3: 248k /
+    // 271k, C = 4: 216k / 209k, C = 5: 175k / 169k, C = 6: 160k / 156k.  The
+    // link time of C blocks per pair over the HBM time of the pair's
+    // attention and score bytes is 1.65 at C = 3 and 2.2 at C = 4; the rule
+    // below switches at 2.
     int n_comp = ds.compute_streams;
     if (n_comp == 0) {
         const int64_t pairs = (int64_t)dims->B * dims->H_kv;
         const double link_s = (double)ds.C * kBlockBytes / kLinkBytesPerS;
         const double hbm_s = ((double)ds.K_b * kBlockBytes + (double)dims->NB_max * kSummaryBytes) / kHbmBytesPerS;
-        const bool link_bound = ds.staged && link_s > 2.5 * hbm_s;
+        const bool link_bound = ds.staged && link_s > 2.0 * hbm_s;
         n_comp = !ds.staged ? 1 : (pairs < device_cu_count() || !link_bound) ? 2 : -1;
     }
     if (n_comp < 0) {
