@@ -502,7 +502,7 @@ def main():
                          copy_mode=copy_mode, host_threads=args.host_threads, n_split=args.n_split, J=w.J,
                          n_q=n_q, compute_streams=args.compute_streams, issue_threads=args.issue_threads)
     T = K_b
-    splits = oa.oasis_attn_num_splits(B, H_q, H_kv, T, args.n_split)
+    splits, attn_waves = oa.oasis_attn_launch_shape(B, H_q, H_kv, n_q, T, args.n_split)
 
     def run(t0, t1, step_events=None):
         for t in range(t0, t1):
@@ -776,7 +776,7 @@ def main():
                    "kv_location": "pinned host pool + HBM working set" if staged else "HBM",
                    "copy_engine": args.copy_mode if staged else None,
                    "host_threads": args.host_threads if staged and copy_mode != oa.OASIS_COPY_KERNEL else None,
-                   "attn_splits": splits, "compute_streams": pipe.compute_streams,
+                   "attn_splits": splits, "attn_waves": attn_waves, "compute_streams": pipe.compute_streams,
                    "issue_threads": pipe.issue_threads,
                    "copy_streams": len(pipe.copy) if staged else None},
         "roofline": roofline,

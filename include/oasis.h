@@ -390,6 +390,15 @@ size_t oasis_attn_workspace_bytes(const oasis_dims *dims, int32_t T,
                                   int32_t n_split);
 int32_t oasis_attn_num_splits(const oasis_dims *dims, int32_t T,
                               int32_t n_split);
+/* The launch shape the attention entry points use for n_q queries per
+ * request: *splits partitions of each table row and *waves waves (4 or 8)
+ * per workgroup.  The library aims at two waves per SIMD: one split of
+ * four-wave workgroups when there are enough (request, KV head) pairs, else
+ * one split of eight-wave workgroups, else more splits (an explicit n_split
+ * fixes the splits; the waves follow).  OASIS_EINVAL for bad arguments. */
+int oasis_attn_launch_shape(const oasis_dims *dims, int32_t n_q, int32_t T,
+                            int32_t n_split, int32_t *splits,
+                            int32_t *waves);
 int oasis_sparse_decode_attn(const oasis_dims *dims, const uint16_t *q,
                              const uint16_t *kv_pool, int32_t P,
                              const int32_t *tbl_slot,

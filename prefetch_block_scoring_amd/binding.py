@@ -100,6 +100,8 @@ _SIGNATURES = {
     "oasis_stage_copy": (ctypes.c_int, [ctypes.POINTER(oasis_dims), ctypes.POINTER(oasis_stage_args)]),
     "oasis_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(oasis_dims), _I32, _I32]),
     "oasis_attn_num_splits": (_I32, [ctypes.POINTER(oasis_dims), _I32, _I32]),
+    "oasis_attn_launch_shape": (ctypes.c_int, [ctypes.POINTER(oasis_dims), _I32, _I32, _I32, ctypes.POINTER(_I32),
+                                               ctypes.POINTER(_I32)]),
     "oasis_sparse_decode_attn": (ctypes.c_int, [
         ctypes.POINTER(oasis_dims), _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _P, _P,
         ctypes.c_size_t, _I32, _P]),
@@ -525,6 +527,15 @@ def oasis_attn_workspace_bytes(B: int, H_q: int, H_kv: int, T: int, n_split: int
 def oasis_attn_num_splits(B: int, H_q: int, H_kv: int, T: int, n_split: int = 0) -> int:
     d = dims(B, H_q, H_kv, 1)
     return int(_lib.oasis_attn_num_splits(ctypes.byref(d), int(T), int(n_split)))
+
+
+def oasis_attn_launch_shape(B: int, H_q: int, H_kv: int, n_q: int, T: int, n_split: int = 0):
+    """(splits, waves per workgroup) of an attention launch with n_q queries per request."""
+    d = dims(B, H_q, H_kv, 1)
+    sp, wv = _I32(), _I32()
+    _check(_lib.oasis_attn_launch_shape(ctypes.byref(d), int(n_q), int(T), int(n_split), ctypes.byref(sp),
+                                        ctypes.byref(wv)))
+    return sp.value, wv.value
 
 
 def oasis_sparse_decode_attn(q: torch.Tensor, kv_pool: torch.Tensor, tbl_slot: torch.Tensor,

@@ -80,8 +80,9 @@ def resource_usage(names=("score.hip", "attn.hip", "topk.hip", "stage.hip")) -> 
             field, _, value = body.partition(": ")
             if field == "Function Name":
                 if kern is not None:
-                    m = re.search(r"\d([a-z][a-z0-9_]*_kernel)(ILi(\d+)E)?", kern)
-                    label = (m.group(1) + (f"<{m.group(3)}>" if m.group(3) else "")) if m else kern
+                    m = re.search(r"\d([a-z][a-z0-9_]*_kernel)((?:I|)(?:Li\d+E)+)?", kern)
+                    args = re.findall(r"Li(\d+)E", m.group(2) or "") if m else []
+                    label = (m.group(1) + (f"<{', '.join(args)}>" if args else "")) if m else kern
                     out.append(f"{name:11s} {label:34s} " + " ".join(f"{vals.get(k, '-'):>10s}" for k, _ in keys))
                 kern, vals = value, {}
             else:

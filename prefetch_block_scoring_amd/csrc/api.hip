@@ -472,6 +472,21 @@ int32_t oasis_attn_num_splits(const oasis_dims *dims, int32_t T, int32_t n_split
     return attn_splits(*dims, 1, T, n_split);
 }
 
+int oasis_attn_launch_shape(const oasis_dims *dims, int32_t n_q, int32_t T, int32_t n_split, int32_t *splits,
+                            int32_t *waves) {
+    clear_error();
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    NEED(splits);
+    NEED(waves);
+    if (n_q < 1) FAIL(OASIS_EINVAL, "n_q = %d < 1", n_q);
+    if (T < 0) FAIL(OASIS_EINVAL, "T = %d < 0", T);
+    if (n_split < 0 || n_split > 64) FAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", n_split);
+    *splits = attn_splits(*dims, n_q, T, n_split);
+    *waves = attn_waves(*dims, n_q, T, *splits);
+    return OASIS_OK;
+}
+
 int oasis_lookahead_attn(const oasis_dims *dims, int32_t n_q, const uint16_t *q, const uint16_t *kv_pool,
                          int32_t P, const int32_t *tbl_slot, const int32_t *tbl_block, const int32_t *tbl_n,
                          int32_t T, const int32_t *ctx_len, float sm_scale, uint16_t *out, float *lse, void *ws,

@@ -10,10 +10,13 @@
 // pairs of the KV group, column c = query (c / G), head (c % G), and every
 // K / V load serves all of them.  Plain decode attention is n_q = 1.
 //
-// Work split: a workgroup of four waves owns one (request, KV head) and one of
-// n_split contiguous ranges of its table; the waves take the range's entries
-// round-robin and keep private online-softmax states, merged in LDS at the end;
-// with n_split > 1 a second kernel merges the ranges by their log-sum-exp.
+// Work split: a workgroup of four or eight waves owns one (request, KV head)
+// and one of n_split contiguous ranges of its table; the waves take the
+// range's entries round-robin and keep private online-softmax states, merged
+// in LDS at the end; with n_split > 1 a second kernel merges the ranges by
+// their log-sum-exp.  The launch shape (attn_shape) aims at two waves per
+// SIMD: one split of four-wave workgroups when there are enough (request,
+// KV head) pairs, else one split of eight-wave workgroups, else more splits.
 //
 // Per 16-token block (8 KiB of K and V) a wave does:
 //   q . K   on the matrix cores: one v_mfma_f32_16x16x32_bf16 per 32 dims,
@@ -49,7 +52,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;  // waves per workgroup of attn_pv_kernel (attn_kernel: 4 or 8)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVecPerBlock = (int)(kBlockBytes / 16);  // uint4 per K+V block (512)
 constexpr float kLn2 = 0.693147180559945309f;
@@ -72,13 +75,13 @@ struct AttnArgs {
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// A wave's table entries i0 + wave + kWaves * k (k < nk): up to 64 at a time
-// sit in the lanes (one load), with a mask of the valid ones (slot in
-// [0, P), block in [0, nb)), so the loop takes (slot, block) from a lane
-// rather than reading memory before each block's loads.
+// A wave's table entries i0 + wave + W * k (k < nk), W the workgroup's
+// waves: up to 64 at a time sit in the lanes (one load), with a mask of the
+// valid ones (slot in [0, P), block in [0, nb)), so the loop takes (slot,
+// block) from a lane rather than reading memory before each block's loads.
 struct TableCursor {
     const int32_t *ts, *tb;
-    int base, nk, P, nb, lane;
+    int base, stride, nk, P, nb, lane;
     int slot = -1, blk = -1, chunk = 0;
     unsigned long long mask = 0;
 
@@ -87,8 +90,8 @@ struct TableCursor {
         const int k = c + lane;
         int s = -1, b = -1;
         if (k < nk) {
-            s = ts[base + k * kWaves];
-            b = tb[base + k * kWaves];
+            s = ts[base + k * stride];
+            b = tb[base + k * stride];
         }
         slot = s;
         blk = b;
@@ -111,23 +114,24 @@ struct TableCursor {
 };
 
 // GP: columns compiled in (a power of two >= n_q * G, at most 8); G = H_q /
-// H_kv at run time.  Waves per SIMD the kernel is compiled for: four for up
-// to four columns (1024 workgroups of the 8-KV-head layers at batch 128 then
-// fit the 256 compute units in one round); eight columns need more
-// registers: at least two (166 registers currently fit three).  More columns
-// run in attn_pv_kernel below.
+// H_kv at run time.  W: waves per workgroup (4 or 8).  Waves per SIMD the
+// kernel is compiled for: four for up to four columns (1024 workgroups of the
+// 8-KV-head layers at batch 128 then fit the 256 compute units in one round);
+// eight columns need more registers: at least two (166 registers currently
+// fit three).  More columns run in attn_pv_kernel below.
 template <int GP>
 constexpr int attn_waves_per_simd() { return GP <= 4 ? 4 : 2; }
 
-template <int GP>
-__global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kernel(AttnArgs a) {
-    __shared__ float p_lds[kWaves][17][16];  // per wave: p[token][head]; row 16 = rescale
+template <int GP, int W>
+__global__ __launch_bounds__(64 * W, attn_waves_per_simd<GP>()) void attn_kernel(AttnArgs a) {
+    constexpr int kWg = 64 * W;  // threads
+    __shared__ float p_lds[W][17][16];  // per wave: p[token][head]; row 16 = rescale
     // Q^T in the MFMA B layout, one 16-byte chunk per (head slot, 8 dims);
     // rows padded by 16 bytes so the 16 head slots fall in distinct banks
     __shared__ uint4 q_lds[16][17];
-    __shared__ float m_lds[kWaves][16];
-    __shared__ float l_lds[kWaves][16];
-    __shared__ float o_lds[kWaves][GP][kD];
+    __shared__ float m_lds[W][16];
+    __shared__ float l_lds[W][16];
+    __shared__ float o_lds[W][GP][kD];
 
     const int rh = blockIdx.x;
     const int split = blockIdx.y;
@@ -155,9 +159,9 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     // for the loads in flight.  The query load, the table load and the first
     // block's loads are all issued before the query goes to LDS, so their
     // latencies overlap (183 against 190 us alone at batch 128 / 16K).
-    const int qc = tid >> 4, qchunk = tid & 15;  // 256 threads = 16 columns x 16 chunks
+    const int qc = tid >> 4, qchunk = tid & 15;  // threads 0..255: 16 columns x 16 chunks
     uint4 qv = make_uint4(0, 0, 0, 0);
-    if (qc < NC) {
+    if (qc < NC) {  // NC <= 16, so only threads below 256
         const int qi = qc / G, g = qc - qi * G;
         qv = reinterpret_cast<const uint4 *>(a.q + (((size_t)r * a.n_q + qi) * a.H_q + (size_t)h * G + g) * kD)[qchunk];
     }
@@ -166,8 +170,7 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     const int32_t *tb = a.tbl_block + (size_t)rh * a.T;
     const uint4 *pool = reinterpret_cast<const uint4 *>(a.kv) + (size_t)rh * a.P * kVecPerBlock;
 
-    TableCursor cur{ts, tb, i0 + wave, i1 - i0 - wave > 0 ? (i1 - i0 - wave + kWaves - 1) / kWaves : 0, a.P, nb,
-                    lane};
+    TableCursor cur{ts, tb, i0 + wave, W, i1 - i0 - wave > 0 ? (i1 - i0 - wave + W - 1) / W : 0, a.P, nb, lane};
     cur.load(0);
     // next valid entry (wave-uniform); nullptr at the end
     auto next_valid = [&](int &blk) -> const uint4 * {
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     uint4 kc[4], vc[4];
     if (src_c) load(src_c, kc, vc);
 
-    q_lds[qc][qchunk] = qv;
+    if (tid < 256) q_lds[qc][qchunk] = qv;
     __syncthreads();
 
     float acc[GP][8];
@@ -307,15 +310,15 @@ __global__ __launch_bounds__(kThreads, attn_waves_per_simd<GP>()) void attn_kern
     __syncthreads();
 
     // merge the waves; one thread per (column, dim)
-    for (int idx = tid; idx < NC * kD; idx += kThreads) {
+    for (int idx = tid; idx < NC * kD; idx += kWg) {
         const int g = idx / kD, d = idx - g * kD;  // g: column
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) M = fmaxf(M, m_lds[w][g]);
+        for (int w = 0; w < W; w++) M = fmaxf(M, m_lds[w][g]);
         float o = 0.f, L = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < kWaves; w++) {
+            for (int w = 0; w < W; w++) {
                 const float mw = m_lds[w][g];
                 const float f = (mw == -INFINITY) ? 0.f : exp2_(mw - M);
                 o += f * o_lds[w][g][d];
@@ -395,8 +398,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_pv_kernel(AttnArgs a) {
     const uint4 *pool = reinterpret_cast<const uint4 *>(a.kv) + (size_t)rh * a.P * kVecPerBlock;
     uint16_t(*vt)[kVtStride] = reinterpret_cast<uint16_t(*)[kVtStride]>(scratch + wave * kVtBytes);
 
-    TableCursor cur{ts, tb, i0 + wave, i1 - i0 - wave > 0 ? (i1 - i0 - wave + kWaves - 1) / kWaves : 0, a.P, nb,
-                    lane};
+    TableCursor cur{ts, tb, i0 + wave, kWaves, i1 - i0 - wave > 0 ? (i1 - i0 - wave + kWaves - 1) / kWaves : 0, a.P,
+                    nb, lane};
     cur.load(0);
     // next valid entry (wave-uniform); nullptr at the end
     auto next_valid = [&](int &blk) -> const uint4 * {
@@ -583,9 +586,12 @@ __global__ __launch_bounds__(kD) void attn_combine_kernel(const float *__restric
 }
 
 template <int GP>
-hipError_t launch_g(const oasis_dims &d, const AttnArgs &a, hipStream_t s, hipEvent_t done) {
+hipError_t launch_g(const oasis_dims &d, const AttnArgs &a, int waves, hipStream_t s, hipEvent_t done) {
     dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)a.n_split);
-    hipExtLaunchKernelGGL(attn_kernel<GP>, grid, dim3(kThreads), 0, s, nullptr, done, 0, a);
+    if (waves == 8)
+        hipExtLaunchKernelGGL(attn_kernel<GP, 8>, grid, dim3(64 * 8), 0, s, nullptr, done, 0, a);
+    else
+        hipExtLaunchKernelGGL(attn_kernel<GP, 4>, grid, dim3(64 * 4), 0, s, nullptr, done, 0, a);
     return hipGetLastError();
 }
 
@@ -622,19 +628,37 @@ hipError_t attn_static_scratch(void **ptr) {
     return hipSuccess;
 }
 
+// The launch shape aims at two waves per SIMD (8 per compute unit) over the
+// (request, KV head) pairs: one split of four-wave workgroups when the pairs
+// alone fill the machine; otherwise eight-wave workgroups (VALU kernel) over
+// as few splits as reach the target, each split keeping at least two table
+// entries per wave.  A split adds a combine kernel and its partial outputs,
+// which in the pipeline cost more than wider workgroups: Qwen3-8B in HBM at
+// batch 32 (256 pairs, G = 4), one split of eight waves against two of four,
+// 462-466k against 413k tok/s (alone 50.0 against 52.1 us); the ragged
+// 32B-class layer (128 pairs, G = 8), two splits of eight waves against four
+// of four, alone 33.1 against 35.9 us.  Four-wave workgroups stay faster
+// wherever they fill the machine (the reasoning layer, 512 pairs: 356k
+// against 334k with eight waves).
+int attn_waves(const oasis_dims &d, int n_q, int T, int splits) {
+    if (n_q * (d.H_q / d.H_kv) > 8) return kWaves;  // attn_pv_kernel
+    const long pairs = (long)d.B * d.H_kv;
+    const long target = 8L * device_cu_count();
+    return pairs * splits * 4 < target && (long)T >= 16L * splits ? 8 : 4;
+}
+
 int attn_splits(const oasis_dims &d, int n_q, int T, int n_split) {
     if (n_split > 0) return n_split < 64 ? n_split : 64;
     const long pairs = (long)d.B * d.H_kv;
     if (pairs <= 0 || T <= 0) return 1;
-    // About two workgroups per compute unit, without splitting a row below
-    // eight entries (two per wave).  Measured: one round of the kernel's
-    // full residency (four per unit) wrote more partial outputs than it
-    // saved; with 256 pairs at G = 4, 2 splits ran 4% faster alone and 3%
-    // faster in the pipeline than 4; with 128 pairs at G = 8, 4 splits beat
-    // 6 and 8; and two leave unit slots to the pipeline's other kernels.
-    const long target = 2L * device_cu_count();
-    long s = (target + pairs - 1) / pairs;
-    const long cap = (T + 7) / 8;
+    const long target = 8L * device_cu_count();  // waves: two per SIMD
+    if (pairs * 4 >= target) return 1;
+    // eight-wave workgroups for the VALU kernel, four for attn_pv_kernel;
+    // a split keeps two table entries per wave
+    const bool valu = n_q * (d.H_q / d.H_kv) <= 8;
+    const long wg_waves = valu ? 8 : 4;
+    long s = (target + wg_waves * pairs - 1) / (wg_waves * pairs);
+    const long cap = valu ? T / 16 : (T + 7) / 8;
     if (s > cap) s = cap;
     if (s > 64) s = 64;
     if (s < 1) s = 1;
@@ -669,13 +693,14 @@ hipError_t launch_attn(const oasis_dims &d, int n_q, const uint16_t *q, const ui
     a.lse = lse;
     a.ws = ws;
     const int NC = n_q * (d.H_q / d.H_kv);
+    const int waves = attn_waves(d, n_q, T, n_split);
     // `done` on the last kernel (the combine, if any)
     hipEvent_t first = n_split <= 1 ? done : nullptr;
     hipError_t e;
-    if (NC <= 1) e = launch_g<1>(d, a, s, first);
-    else if (NC <= 2) e = launch_g<2>(d, a, s, first);
-    else if (NC <= 4) e = launch_g<4>(d, a, s, first);
-    else if (NC <= 8) e = launch_g<8>(d, a, s, first);
+    if (NC <= 1) e = launch_g<1>(d, a, waves, s, first);
+    else if (NC <= 2) e = launch_g<2>(d, a, waves, s, first);
+    else if (NC <= 4) e = launch_g<4>(d, a, waves, s, first);
+    else if (NC <= 8) e = launch_g<8>(d, a, waves, s, first);
     else {
         dim3 grid((unsigned)(d.B * d.H_kv), (unsigned)n_split);
         hipExtLaunchKernelGGL(attn_pv_kernel, grid, dim3(kThreads), 0, s, nullptr, first, 0, a);

@@ -105,6 +105,8 @@ hipError_t launch_topk_overlap(int pairs, const int32_t *a, const int32_t *na,
 
 // split count of an attention launch with n_q queries per request
 int attn_splits(const oasis_dims &d, int n_q, int T, int n_split);
+// waves per workgroup of an attention launch with `splits` splits
+int attn_waves(const oasis_dims &d, int n_q, int T, int splits);
 // split-K workspace for n_q queries per request
 size_t attn_ws_bytes(const oasis_dims &d, int n_q, int T, int n_split);
 

@@ -281,3 +281,30 @@ def test_static_attention_scratch_limit_is_checked_on_the_host():
     assert "fixed scratch" in oa.oasis_last_error()
     assert L.oasis_sparse_decode_attn_static(ctypes.byref(dd), p, p, 0, p, p, p, 128, p, 0.1, p, None, 16,
                                              None) == oa.OASIS_EINVAL
+
+
+def test_attention_launch_shape_rule():
+    """The attention launch shape (host logic; 256 compute units, as MI355X
+    has and as the library assumes where no GPU answers): one split of
+    four-wave workgroups with enough (request, KV head) pairs, else splits
+    of eight-wave workgroups (four past eight query columns) with at least
+    two table entries per wave; an explicit split count keeps its splits and
+    the waves follow."""
+    shape = oa.oasis_attn_launch_shape
+    assert shape(128, 32, 8, 1, 128) == (1, 4)    # 1024 pairs
+    assert shape(64, 32, 8, 1, 128) == (1, 4)     # 512 pairs
+    assert shape(32, 32, 8, 1, 128) == (1, 8)     # 256 pairs
+    assert shape(16, 64, 8, 1, 128) == (2, 8)     # 128 pairs: 2 splits of eight waves fill the machine
+    assert shape(32, 32, 8, 5, 128) == (2, 4)     # 20 columns: attn_pv_kernel, four waves
+    assert shape(1, 8, 2, 1, 32) == (2, 8)        # 2 pairs: splits of 16 entries, two per wave
+    assert shape(1, 8, 2, 1, 8) == (1, 4)         # 8 entries: one split, four waves
+    assert shape(32, 32, 8, 1, 128, 1) == (1, 8)
+    assert shape(32, 32, 8, 1, 128, 2) == (2, 4)
+    assert shape(16, 64, 8, 1, 128, 2) == (2, 8)
+    assert shape(128, 32, 8, 1, 128, 1) == (1, 4)
+    for B in (1, 7, 32, 128):
+        sp, _ = shape(B, 32, 8, 1, 128)
+        assert sp == oa.oasis_attn_num_splits(B, 32, 8, 128)
+    with pytest.raises(oa.OasisError):
+        shape(32, 32, 8, 0, 128)
+    assert binding.library().oasis_attn_launch_shape(None, 1, 128, 0, None, None) == oa.OASIS_EINVAL
