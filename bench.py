@@ -116,16 +116,29 @@ def rotation_count(nbytes, most=64):
 
 def time_rotated(torch, fns, n):
     """Mean microseconds per launch of n launches cycling through fns (one
-    launch per input copy), after one untimed round."""
+    launch per input copy), after one untimed round.  The launches run back
+    to back on the GPU: before the first, the stream is kept busy with fills
+    of a scratch buffer for longer than the host takes to enqueue all n, so
+    the figure is the kernels' own time and not the binding's per-call host
+    cost (which exceeds a 30 us kernel's)."""
     for f in fns:
         f()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for f in fns:
+        f()
+    host_s = (time.perf_counter() - t0) / len(fns)
+    torch.cuda.synchronize()
+    hold = torch.empty(64 << 20, dtype=torch.int32, device="cuda")  # 256 MiB: one fill takes ~50 us
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(int(math.ceil((2.0 * n * host_s + 500e-6) / 40e-6))):
+        hold.fill_(1)
     a.record()
     for i in range(n):
         fns[i % len(fns)]()
     b.record()
     torch.cuda.synchronize()
+    del hold
     return a.elapsed_time(b) / n * 1e3
 
 
