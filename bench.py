@@ -673,7 +673,7 @@ def main():
     n_alone = max(20, len(attn_fns))
     log("attention launches: " + json.dumps({"warmup": args.warmup * L, "timed": args.steps * L,
                                              "extra": n_extra * L if extra else 0,
-                                             "alone": len(attn_fns) + n_alone}))
+                                             "alone": 2 * len(attn_fns) + n_alone}))
     alone_us = time_rotated(torch, attn_fns, n_alone)
     kern["attn_alone"] = alone_entry(attn_bytes, alone_us, len(attn_fns), rot_how)
     del attn_fns
