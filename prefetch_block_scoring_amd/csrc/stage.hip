@@ -42,8 +42,8 @@ constexpr int kMaxSlotsPerThread = 2048 / kThreads;
 // the link at the pinned-memcpy rate (12 or 16: 1-2% slower; at a cap of two
 // blocks 16 is 17% slower).  With at most kFewAdmits admits per step, 16
 // leave more compute units to the latency-bound kernels beside them: the
-// ragged 32B-class layer (128 pairs, C = 6) runs at 154k tok/s against 149k
-// with 24 (12: 140k, 20: 154k).
+// ragged 32B-class layer (128 pairs, C = 6) runs at 176k tok/s against
+// 171-173k with 24 (12: 154-156k, 20: 173-176k).
 constexpr int kGatherWgs = 24;
 constexpr int kGatherWgsFew = 16;
 constexpr long kFewAdmits = 1024;
