@@ -592,11 +592,9 @@ typedef struct oasis_pipeline_desc {
                                  THE CALLING THREAD MAY BLOCK in
                                  oasis_pipeline_layer_step until the
                                  selection of (layer, step - 1) is done.
-                                 0 = automatic: on for staged steps and for
-                                 unstaged steps whose attention and score
-                                 bytes take HBM at least 40 us; 1 = on;
-                                 -1 = off, the calling thread enqueues
-                                 everything, with stream waits.  A chain on
+                                 0 (automatic) or 1 = on; -1 = off, the
+                                 calling thread enqueues everything, with
+                                 stream waits.  A chain on
                                  the main stream (compute_streams = -1)
                                  always uses the calling thread
                                  (oasis_pipeline_issue_threads tells). */
@@ -639,8 +637,8 @@ int oasis_pipeline_drain(oasis_pipeline *p);
  * stream of odd layers (NULL where not used). */
 int oasis_pipeline_stream(oasis_pipeline *p, int32_t which, void **stream);
 
-/* *on = 1 if the pipeline's chain and copies are enqueued by issue threads
- * (the automatic choice, or issue_threads = 1), else 0. */
+/* *on = 1 if the pipeline's chain and copies are enqueued by issue threads,
+ * else 0 (issue_threads = -1, or the chain on the main stream). */
 int oasis_pipeline_issue_threads(oasis_pipeline *p, int32_t *on);
 
 /* Event timing of the steps: capacity > 0 (re)arms timing of up to

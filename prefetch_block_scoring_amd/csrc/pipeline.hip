@@ -34,9 +34,6 @@ constexpr int kRing = 4;
 constexpr double kLinkBytesPerS = 57e9;
 constexpr double kHbmBytesPerS = 6e12;
 constexpr double kSummaryBytes = 2 * kD * 2;  // one block's min and max key, bf16
-// GPU time (HBM, seconds) of an unstaged layer-step from which on the issue
-// threads' host waits pay (see oasis_pipeline_create)
-constexpr double kMinThreadedStepS = 40e-6;
 constexpr int kTimedKinds = 4;
 
 struct Job {
@@ -68,9 +65,11 @@ struct oasis_pipeline {
     hipStream_t main = nullptr, comp[2] = {nullptr, nullptr}, copy[2] = {nullptr, nullptr};
     bool comp_on_main = false;  // compute_streams = -1: the chain runs on the main stream
     std::vector<hipEvent_t> ev;  // [kind][layer][kRing]
-    // per layer, written by the calling thread: the event that completes with
-    // the layer's latest attention, and (unstaged) with its latest top-K; the
-    // ring's event, or the timing event bound to the same kernel
+    // per layer: the event that completes with the layer's latest attention
+    // (written by the calling thread), and without staging with its latest
+    // top-K (written by whichever thread issues the chain, read by the calling
+    // thread once that chain job has run); the ring's event, or the timing
+    // event bound to the same kernel; nullptr after timing is re-armed
     std::vector<hipEvent_t> attn_last, sel_last;
 
     // timing
@@ -333,19 +332,11 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     // was enqueued.  Those queues then carry no barrier packets, each of
     // which holds its queue ~3 us even when its event has completed, and a
     // stream wait on a pending event costs the enqueuing thread 8 to 24 us
-    // (MI355X, ROCm 7.2).  A host wait on work that is still running adds a
-    // GPU -> host -> GPU round trip (10-20 us) to that dependency, which a
-    // layer-step hides only when its GPU work is much longer: automatic
-    // (issue_threads = 0) uses them for staged steps and for steps whose
-    // attention and scores take HBM at least 40 us.  Measured: the ragged
-    // 32B-class staged layer 155k -> 176k tok/s (with the events bound to
-    // the kernels); Qwen3-8B in HBM at batch 32 (67 us) 388k -> 414k; the
-    // B = 1 parity layer (0.4 us) 35.7k -> 23.9k with them.
-    const double step_hbm_s = (double)dims->B * dims->H_kv *
-                              ((double)ds.K_b * kBlockBytes + (double)dims->NB_max * kSummaryBytes) / kHbmBytesPerS;
-    const bool want_threads =
-        ds.issue_threads > 0 || (ds.issue_threads == 0 && (ds.staged || step_hbm_s >= kMinThreadedStepS));
-    p->threaded = !p->comp_on_main && want_threads;
+    // (MI355X, ROCm 7.2).  Measured against issue_threads = -1: the ragged
+    // 32B-class staged layer 155k -> 176k tok/s (with the events bound to the
+    // kernels), Qwen3-8B in HBM at batch 32 420k -> 472k, the B = 1 parity
+    // layer 50k -> 52.7k.
+    p->threaded = !p->comp_on_main && ds.issue_threads >= 0;
     if (p->threaded) {
         p->chain.start(
             ds.n_layers,
@@ -402,14 +393,12 @@ static int issue_chain(oasis_pipeline *p, int l, int t, const uint16_t *q_look, 
         // step t - 1 and everything it waits for are already enqueued, so the
         // worker cannot block anything it would have to enqueue itself, and
         // the compute stream gets no barrier packet, each of which holds its
-        // queue ~10 us after the event has completed (the ragged 32B-class
-        // layer: 159k against 155k tok/s).
-        // (no event: timing was re-armed since, after everything finished)
-        if (!attn_prev) {
-        } else if (p->threaded) {
-            OASIS_HIP(hipEventSynchronize(attn_prev));
-        } else {
-            OASIS_HIP(stream_wait(cs, attn_prev));
+        // queue ~3 us even when its event has completed (the ragged 32B-class
+        // layer: 159k against 155k tok/s).  No event: timing was re-armed
+        // since, after everything enqueued had finished.
+        if (attn_prev) {
+            if (p->threaded) OASIS_HIP(hipEventSynchronize(attn_prev));
+            else OASIS_HIP(stream_wait(cs, attn_prev));
         }
     }
     hipEvent_t tk = timed(p, 2, cs);
@@ -571,7 +560,8 @@ int oasis_pipeline_timing(oasis_pipeline *p, int32_t capacity, uint32_t kinds, i
     // The timing events are bound to launches again from the first one on, so
     // no wait still to be issued may name one: let everything enqueued
     // finish, after which the next steps need no wait on earlier launches.
-    for (hipStream_t c : {p->main, p->comp[0], p->comp[1], p->copy[0], p->copy[1]})
+    OASIS_HIP(hipStreamSynchronize(p->main));  // NULL: the default stream
+    for (hipStream_t c : {p->comp[0], p->comp[1], p->copy[0], p->copy[1]})
         if (c) OASIS_HIP(hipStreamSynchronize(c));
     std::fill(p->attn_last.begin(), p->attn_last.end(), nullptr);
     std::fill(p->sel_last.begin(), p->sel_last.end(), nullptr);

@@ -22,9 +22,8 @@ lays that out on one GPU's streams:
 With compute streams of its own, the chain and the copies of a layer-step
 are enqueued by the pipeline's two issue threads, which make the chain's
 cross-stream waits on the host, and the calling thread enqueues only the
-attention (`issue_threads`: automatic for staged steps and for unstaged
-steps with at least ~40 us of HBM work; without staging the calling thread
-then waits on the host for the selection its attention reads).
+attention (`issue_threads`; without staging the calling thread then waits
+on the host for the selection its attention reads).
 
 `LayerPipeline` allocates the per-layer buffers the native pipeline works in
 (three attention tables, two selections and two plan buffers per layer, the
