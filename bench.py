@@ -546,12 +546,14 @@ def main():
     n_timed = -(-args.steps * L // every)
     pipe.enable_timing(n_timed, timed_kinds, every=every)
     step_events = []
+    cpu0 = time.process_time()
     t0 = time.perf_counter()
     run(1 + args.warmup, n_steps, step_events=step_events)
     issued = time.perf_counter() - t0
     pipe.drain()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    host_cores = (time.process_time() - cpu0) / elapsed  # CPU time of all the process's threads / wall
     timed_stats = pipe.stage_stats() if staged else None
     layer_steps = args.steps * L
     ms_per_step = elapsed / layer_steps * 1e3
@@ -797,6 +799,7 @@ def main():
         "h2d": h2d,
         "kernels": kern,
         "host_issue_ms_per_step": round(issued / layer_steps * 1e3, 4),
+        "host_cores_busy": round(host_cores, 2),
         "layer_step_us": {**percentiles(step_us), "note": "per decode step of the timed region (main-stream "
                           "events between consecutive steps) / layers in flight"},
     }
