@@ -480,6 +480,9 @@ int oasis_attn_launch_shape(const oasis_dims *dims, int32_t n_q, int32_t T, int3
     NEED(splits);
     NEED(waves);
     if (n_q < 1) FAIL(OASIS_EINVAL, "n_q = %d < 1", n_q);
+    if ((int64_t)n_q * (dims->H_q / dims->H_kv) > kMaxG)
+        FAIL(OASIS_EUNSUPPORTED, "n_q * H_q / H_kv = %lld (at most %d)",
+             (long long)n_q * (dims->H_q / dims->H_kv), kMaxG);
     if (T < 0) FAIL(OASIS_EINVAL, "T = %d < 0", T);
     if (n_split < 0 || n_split > 64) FAIL(OASIS_EINVAL, "n_split = %d outside [0, 64]", n_split);
     *splits = attn_splits(*dims, n_q, T, n_split);

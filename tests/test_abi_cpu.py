@@ -295,7 +295,7 @@ def test_attention_launch_shape_rule():
     assert shape(64, 32, 8, 1, 128) == (1, 4)     # 512 pairs
     assert shape(32, 32, 8, 1, 128) == (1, 8)     # 256 pairs
     assert shape(16, 64, 8, 1, 128) == (2, 8)     # 128 pairs: 2 splits of eight waves fill the machine
-    assert shape(32, 32, 8, 5, 128) == (2, 4)     # 20 columns: attn_pv_kernel, four waves
+    assert shape(32, 32, 8, 3, 128) == (2, 4)     # 12 columns: attn_pv_kernel, four waves
     assert shape(1, 8, 2, 1, 32) == (2, 8)        # 2 pairs: splits of 16 entries, two per wave
     assert shape(1, 8, 2, 1, 8) == (1, 4)         # 8 entries: one split, four waves
     assert shape(32, 32, 8, 1, 128, 1) == (1, 8)
@@ -307,4 +307,6 @@ def test_attention_launch_shape_rule():
         assert sp == oa.oasis_attn_num_splits(B, 32, 8, 128)
     with pytest.raises(oa.OasisError):
         shape(32, 32, 8, 0, 128)
+    with pytest.raises(oa.OasisError):
+        shape(32, 64, 8, 3, 128)  # 24 query columns
     assert binding.library().oasis_attn_launch_shape(None, 1, 128, 0, None, None) == oa.OASIS_EINVAL
