@@ -470,7 +470,7 @@ def test_layer_pipeline_matches_oracle(copy_mode, joint, compute_streams, issue_
                 assert_attn_close(got[:, qi], ref)
 
 
-@pytest.mark.parametrize("compute_streams,issue_threads", [(0, 0), (0, -1), (2, 1), (2, -1)])
+@pytest.mark.parametrize("compute_streams,issue_threads", [(0, 0), (0, -1), (2, 1), (2, -1), (-1, 0)])
 def test_unstaged_pipeline_matches_oracle(compute_streams, issue_threads):
     """The pipeline with K/V in HBM (no staging), three layers in flight:
     every layer's attention at step t + 1 over the blocks the oracle selects
@@ -478,7 +478,7 @@ def test_unstaged_pipeline_matches_oracle(compute_streams, issue_threads):
     worker thread enqueues the scores and top-K, and the calling thread waits
     for the selection of step t - 1 on the host before it enqueues the
     attention; -1: stream waits.  compute_streams 0 is the automatic choice
-    (one stream)."""
+    (one stream); -1 runs the chain on the main stream (no issue threads)."""
     from prefetch_block_scoring_amd.pipeline import LayerPipeline
     w = wl.WORKLOADS["qwen3_8b_16k_b32_hbm"].shrink(B=3, ctx=(3000, 9000))
     L, steps = 3, 6
@@ -491,7 +491,7 @@ def test_unstaged_pipeline_matches_oracle(compute_streams, issue_threads):
     pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=0, n_layers=L, staged=False, J=w.J,
                          compute_streams=compute_streams, issue_threads=issue_threads)
     assert pipe.compute_streams == (compute_streams or 1)
-    assert pipe.issue_threads == (issue_threads >= 0)
+    assert pipe.issue_threads == (issue_threads >= 0 and compute_streams != -1)
     outs = {}
     for t in range(steps):
         for l in range(L):
