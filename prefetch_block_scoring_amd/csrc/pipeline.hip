@@ -272,14 +272,14 @@ int oasis_pipeline_create(const oasis_dims *dims, const oasis_pipeline_desc *des
     // compute streams: with two, even and odd layers alternate, so that one
     // layer's latency-bound top-K and plan overlap the next layer's scores.
     // That pays for a staged step with fewer (request, KV head) pairs than
-    // compute units (the 32B-class ragged layer, 128 pairs: 154k against
-    // 142k tok/s with one) and for a staged step that HBM binds (the Qwen3-8B
+    // compute units (the 32B-class ragged layer, 128 pairs: 176k against
+    // 143k tok/s with one) and for a staged step that HBM binds (the Qwen3-8B
     // layer at batch 128 with a fetch cap of one or two blocks: 393k / 360k
     // against 343k / 320k).  Without staging one compute stream is better:
     // its scores and the attention are the step's HBM traffic, and a second
     // stream only adds a second score kernel taking bandwidth from the
-    // attention (Qwen3-8B in HBM at batch 32: 361k against 354k; the
-    // reasoning layer: 355k against 345k).  A staged step whose admits can
+    // attention (Qwen3-8B in HBM at batch 32: 470k against 431k; the
+    // reasoning layer: 356k against 351k).  A staged step whose admits can
     // take the link much longer than its HBM kernels take HBM is link-bound:
     // the chain then runs on the main stream behind each attention
     // (compute_streams = -1), so the kernels that read HBM never run beside
