@@ -120,7 +120,11 @@ def time_rotated(torch, fns, n):
     to back on the GPU: before the first, the stream is kept busy with fills
     of a scratch buffer for longer than the host takes to enqueue all n, so
     the figure is the kernels' own time and not the binding's per-call host
-    cost (which exceeds a 30 us kernel's)."""
+    cost (which exceeds a 30 us kernel's).  A measurement in which the host
+    had not enqueued the last launch by the time the GPU finished the fills
+    (a pause of the host thread, seen up to ~36 ms) is taken again, up to
+    three times."""
+    import gc
     for f in fns:
         f()
     torch.cuda.synchronize()
@@ -129,15 +133,28 @@ def time_rotated(torch, fns, n):
         f()
     host_s = (time.perf_counter() - t0) / len(fns)
     torch.cuda.synchronize()
-    hold = torch.empty(64 << 20, dtype=torch.int32, device="cuda")  # 256 MiB: one fill takes ~50 us
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(int(math.ceil((2.0 * n * host_s + 500e-6) / 40e-6))):
-        hold.fill_(1)
-    a.record()
-    for i in range(n):
-        fns[i % len(fns)]()
-    b.record()
-    torch.cuda.synchronize()
+    hold = torch.empty(64 << 20, dtype=torch.int32, device="cuda")  # 256 MiB: one fill takes ~40 us
+    n_fill = int(math.ceil((2.0 * n * host_s + 500e-6) / 40e-6))
+    h, a, b = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for attempt in range(3):
+        gc_on = gc.isenabled()
+        gc.disable()
+        t0 = time.perf_counter()
+        h.record()
+        for _ in range(n_fill):
+            hold.fill_(1)
+        a.record()
+        for i in range(n):
+            fns[i % len(fns)]()
+        enqueue_ms = (time.perf_counter() - t0) * 1e3
+        b.record()
+        if gc_on:
+            gc.enable()
+        torch.cuda.synchronize()
+        if enqueue_ms < h.elapsed_time(a):
+            break
+        log(f"alone launches: the host fell behind the GPU (enqueue {enqueue_ms:.2f} ms, fills "
+            f"{h.elapsed_time(a):.2f} ms); measuring again")
     del hold
     return a.elapsed_time(b) / n * 1e3
 
@@ -546,6 +563,12 @@ def main():
     n_timed = -(-args.steps * L // every)
     pipe.enable_timing(n_timed, timed_kinds, every=every)
     step_events = []
+    # Python's garbage collector stays off over the timed steps: a collection
+    # pauses the issuing thread for tens of ms, which a caller in C++ would
+    # not see
+    import gc
+    gc.collect()
+    gc.disable()
     cpu0 = time.process_time()
     t0 = time.perf_counter()
     run(1 + args.warmup, n_steps, step_events=step_events)
@@ -553,6 +576,7 @@ def main():
     pipe.drain()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     host_cores = (time.process_time() - cpu0) / elapsed  # CPU time of all the process's threads / wall
     timed_stats = pipe.stage_stats() if staged else None
     layer_steps = args.steps * L
@@ -654,9 +678,10 @@ def main():
         tb = pipe.table(0, t_last)
         wsp = pipe.layers[0].ws_pool
         n_rot = rotation_count(attn_bytes)
-        pools = [wsp] + [wsp.clone() for _ in range(n_rot - 1)]
-        attn_fns = [lambda p=p_: oa.oasis_lookahead_attn(q4, p, tb[0], tb[1], tb[2], ctx, out=out_alone, ws=attn_ws,
-                                                          n_split=args.n_split) for p_ in pools]
+        rot_inputs = [wsp] + [wsp.clone() for _ in range(n_rot - 1)]
+
+        def attn_call(q_, p_, o_, w_):
+            return oa.oasis_lookahead_attn(q_, p_, tb[0], tb[1], tb[2], ctx, out=o_, ws=w_, n_split=args.n_split)
         rot_how = "copies of the working set"
     else:
         jp = (t_last - 1) % 2
@@ -665,11 +690,13 @@ def main():
         # (mod the request's blocks): other blocks of the same pool
         nbl = ((ctx + bs - 1) // bs).clamp(min=1).view(B, 1, 1)
         n_rot = min(rotation_count(attn_bytes), max(1, NB // K_b))
-        sels = [sel] + [torch.where(sel >= 0, (sel + k * K_b) % nbl, sel).to(torch.int32).contiguous()
-                        for k in range(1, n_rot)]
-        attn_fns = [lambda t_=t_: oa.oasis_lookahead_attn(q4, pool, t_, t_, ns, ctx, out=out_alone, ws=attn_ws,
-                                                           n_split=args.n_split) for t_ in sels]
+        rot_inputs = [sel] + [torch.where(sel >= 0, (sel + k * K_b) % nbl, sel).to(torch.int32).contiguous()
+                              for k in range(1, n_rot)]
+
+        def attn_call(q_, t_, o_, w_):
+            return oa.oasis_lookahead_attn(q_, pool, t_, t_, ns, ctx, out=o_, ws=w_, n_split=args.n_split)
         rot_how = "tables shifted to other blocks of the pool"
+    attn_fns = [lambda r_=r_: attn_call(q4, r_, out_alone, attn_ws) for r_ in rot_inputs]
     # attention launches of each phase in launch order, so that a profiled
     # run's kernel trace can be split the same way (--summarize-profile)
     n_alone = max(20, len(attn_fns))
@@ -679,10 +706,8 @@ def main():
     alone_us = time_rotated(torch, attn_fns, n_alone)
     kern["attn_alone"] = alone_entry(attn_bytes, alone_us, len(attn_fns), rot_how)
     del attn_fns
-    if staged:
-        del pools
-    else:
-        del sels
+    if not args.attn_sweep:
+        del rot_inputs
 
     # scores alone, over rotated copies of the summaries
     sc_out = pipe.layers[0].scores
@@ -705,36 +730,22 @@ def main():
 
     if args.attn_sweep:
         # look-ahead attention alone over the same blocks for n_q = 1, 2, ...
-        # query vectors per request (K / V read once for all of them)
+        # query vectors per request (K / V read once for all of them), over
+        # the attention alone leg's rotation of inputs
         sweep = {}
         gq = torch.Generator(device=dev).manual_seed(17)
-        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        if not staged:
-            jp = (t_last - 1) % 2
-            sel, ns = pipe.layers[0].sel[jp], pipe.layers[0].n_sel[jp]
         for nq in range(1, 16 // (H_q // H_kv) + 1):
             qs = torch.randn((B, nq, H_q, D), generator=gq, device=dev).to(torch.bfloat16)
             o_s = torch.empty_like(qs)
             ws_s = torch.empty((max(oa.oasis_lookahead_attn_workspace_bytes(B, H_q, H_kv, nq, T, args.n_split), 1),),
                                dtype=torch.uint8, device=dev)
-            if staged:
-                run_s = lambda: oa.oasis_lookahead_attn(qs, pipe.layers[0].ws_pool, tb[0], tb[1], tb[2], ctx,
-                                                        out=o_s, ws=ws_s, n_split=args.n_split)
-            else:
-                run_s = lambda: oa.oasis_lookahead_attn(qs, pool, sel, sel, ns, ctx, out=o_s, ws=ws_s,
-                                                        n_split=args.n_split)
-            run_s()
-            torch.cuda.synchronize()
-            ea.record()
-            for _ in range(20):
-                run_s()
-            eb.record()
-            torch.cuda.synchronize()
-            us = ea.elapsed_time(eb) / 20 * 1e3
+            fns = [lambda r_=r_: attn_call(qs, r_, o_s, ws_s) for r_ in rot_inputs]
+            us = time_rotated(torch, fns, max(20, len(fns)))
             kv_b = attn_bytes - 2 * n_q * B * H_q * D * 2
             sweep[str(nq)] = {"columns": nq * (H_q // H_kv), "avg_us": round(us, 2),
                               "kv_GBps": round(kv_b / (us * 1e-6) / 1e9, 1)}
         kern["lookahead_attn_alone"] = sweep
+        del rot_inputs
 
     a_us = kern["attn"]["avg_us"]
     achieved = attn_bytes / (a_us * 1e-6) / 1e9
