@@ -330,8 +330,9 @@ int score_grid(int n_items) {
     // fewer workgroups with longer item ranges pay the range set-up and the
     // Qp / Qm rebuilds less often: alone over rotated copies at batch 128 /
     // 16K, 96.6 against 98.8 us; in the reasoning pipeline 343k against
-    // 326k tok/s), but at least enough that no workgroup holds more than
-    // kMaxItems items
+    // 326k tok/s; at batch 32, 27.5 us alone and 462k tok/s against 28.3 us
+    // and 424k with four, 31.9 us and 420k with three), but at least enough
+    // that no workgroup holds more than kMaxItems items
     long g = (long)device_cu_count() * (occ < 2 ? occ : 2);
     const long need = (n_items + kMaxItems - 1) / kMaxItems;
     if (g < need) g = need;
