@@ -114,7 +114,7 @@ def rotation_count(nbytes, most=64):
     return int(min(most, max(3, -(-ROTATION_BYTES // max(int(nbytes), 1)))))
 
 
-def time_rotated(torch, fns, n):
+def time_rotated(torch, fns, n, label=None):
     """Mean microseconds per launch of n launches cycling through fns (one
     launch per input copy), after one untimed round.  The launches run back
     to back on the GPU: before the first, the stream is kept busy with fills
@@ -123,7 +123,8 @@ def time_rotated(torch, fns, n):
     cost (which exceeds a 30 us kernel's).  A measurement in which the host
     had not enqueued the last launch by the time the GPU finished the fills
     (a pause of the host thread, seen up to ~36 ms) is taken again, up to
-    three times."""
+    three times.  With a label, the number of launches made (untimed rounds
+    and every attempt) is logged, so that a kernel trace can be split."""
     import gc
     for f in fns:
         f()
@@ -136,6 +137,7 @@ def time_rotated(torch, fns, n):
     hold = torch.empty(64 << 20, dtype=torch.int32, device="cuda")  # 256 MiB: one fill takes ~40 us
     n_fill = int(math.ceil((2.0 * n * host_s + 500e-6) / 40e-6))
     h, a, b = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    made = 2 * len(fns)
     for attempt in range(3):
         gc_on = gc.isenabled()
         gc.disable()
@@ -147,6 +149,7 @@ def time_rotated(torch, fns, n):
         for i in range(n):
             fns[i % len(fns)]()
         enqueue_ms = (time.perf_counter() - t0) * 1e3
+        made += n
         b.record()
         if gc_on:
             gc.enable()
@@ -156,6 +159,8 @@ def time_rotated(torch, fns, n):
         log(f"alone launches: the host fell behind the GPU (enqueue {enqueue_ms:.2f} ms, fills "
             f"{h.elapsed_time(a):.2f} ms); measuring again")
     del hold
+    if label:
+        log(f"{label} alone launches made: {made}")
     return a.elapsed_time(b) / n * 1e3
 
 
@@ -235,6 +240,9 @@ def _attention_phases(trace_path, bench_log):
     for ln in open(bench_log):
         if "attention launches: " in ln:
             phases = json.loads(ln.split("attention launches: ", 1)[1])
+        elif "attention alone launches made: " in ln and phases is not None:
+            # the alone leg measured again (a host that fell behind the GPU)
+            phases["alone"] = int(ln.split("attention alone launches made: ", 1)[1])
         elif ln.startswith("{"):
             line = json.loads(ln)
     if phases is None:
@@ -703,7 +711,7 @@ def main():
     log("attention launches: " + json.dumps({"warmup": args.warmup * L, "timed": args.steps * L,
                                              "extra": n_extra * L if extra else 0,
                                              "alone": 2 * len(attn_fns) + n_alone}))
-    alone_us = time_rotated(torch, attn_fns, n_alone)
+    alone_us = time_rotated(torch, attn_fns, n_alone, label="attention")
     kern["attn_alone"] = alone_entry(attn_bytes, alone_us, len(attn_fns), rot_how)
     del attn_fns
     if not args.attn_sweep:
@@ -960,7 +968,7 @@ def cpu_baseline(w, pool, ctx_cpu, q_look, seconds, C):
         n_steps += 1
         t_total += dt
         s += 1
-        if t_total >= seconds or n_steps >= 64:
+        if t_total >= seconds or n_steps >= 100000:
             break
     log(f"cpu baseline: {n_steps} layer-steps in {t_total:.1f}s")
     return {"value": round(w.B * n_steps / t_total, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
