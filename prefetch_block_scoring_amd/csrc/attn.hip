@@ -631,15 +631,18 @@ hipError_t attn_static_scratch(void **ptr) {
 // The launch shape aims at two waves per SIMD (8 per compute unit) over the
 // (request, KV head) pairs: one split of four-wave workgroups when the pairs
 // alone fill the machine; otherwise eight-wave workgroups (VALU kernel) over
-// as few splits as reach the target, each split keeping at least two table
-// entries per wave.  A split adds a combine kernel and its partial outputs,
+// as few splits as reach the target, each split keeping at least four table
+// entries per wave (two in attn_pv_kernel's four-wave workgroups).  A split
+// adds a combine kernel and its partial outputs,
 // which in the pipeline cost more than wider workgroups: Qwen3-8B in HBM at
 // batch 32 (256 pairs, G = 4), one split of eight waves against two of four,
 // 462-466k against 413k tok/s (alone 50.0 against 52.1 us); the ragged
 // 32B-class layer (128 pairs, G = 8), two splits of eight waves against four
 // of four, alone 33.1 against 35.9 us.  Four-wave workgroups stay faster
 // wherever they fill the machine (the reasoning layer, 512 pairs: 356k
-// against 334k with eight waves).
+// against 334k with eight waves).  With few table entries the combine costs
+// more than a second split saves: one request of 8 / 2 heads over 32 blocks,
+// 60.2k tok/s with one split against 51.4k with two (two entries per wave).
 int attn_waves(const oasis_dims &d, int n_q, int T, int splits) {
     if (n_q * (d.H_q / d.H_kv) > 8) return kWaves;  // attn_pv_kernel
     const long pairs = (long)d.B * d.H_kv;
@@ -653,12 +656,12 @@ int attn_splits(const oasis_dims &d, int n_q, int T, int n_split) {
     if (pairs <= 0 || T <= 0) return 1;
     const long target = 8L * device_cu_count();  // waves: two per SIMD
     if (pairs * 4 >= target) return 1;
-    // eight-wave workgroups for the VALU kernel, four for attn_pv_kernel;
-    // a split keeps two table entries per wave
+    // eight-wave workgroups for the VALU kernel (a split keeps four table
+    // entries per wave), four for attn_pv_kernel (two per wave)
     const bool valu = n_q * (d.H_q / d.H_kv) <= 8;
     const long wg_waves = valu ? 8 : 4;
     long s = (target + wg_waves * pairs - 1) / (wg_waves * pairs);
-    const long cap = valu ? T / 16 : (T + 7) / 8;
+    const long cap = valu ? T / 32 : (T + 7) / 8;
     if (s > cap) s = cap;
     if (s > 64) s = 64;
     if (s < 1) s = 1;

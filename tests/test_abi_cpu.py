@@ -288,15 +288,18 @@ def test_attention_launch_shape_rule():
     has and as the library assumes where no GPU answers): one split of
     four-wave workgroups with enough (request, KV head) pairs, else splits
     of eight-wave workgroups (four past eight query columns) with at least
-    two table entries per wave; an explicit split count keeps its splits and
-    the waves follow."""
+    four table entries per wave (two with four waves); an explicit split
+    count keeps its splits and the waves follow."""
     shape = oa.oasis_attn_launch_shape
     assert shape(128, 32, 8, 1, 128) == (1, 4)    # 1024 pairs
     assert shape(64, 32, 8, 1, 128) == (1, 4)     # 512 pairs
     assert shape(32, 32, 8, 1, 128) == (1, 8)     # 256 pairs
     assert shape(16, 64, 8, 1, 128) == (2, 8)     # 128 pairs: 2 splits of eight waves fill the machine
     assert shape(32, 32, 8, 3, 128) == (2, 4)     # 12 columns: attn_pv_kernel, four waves
-    assert shape(1, 8, 2, 1, 32) == (2, 8)        # 2 pairs: splits of 16 entries, two per wave
+    assert shape(1, 8, 2, 1, 32) == (1, 8)        # 2 pairs, 32 entries: one split, four per wave
+    assert shape(1, 8, 2, 1, 64) == (2, 8)        # 64 entries: two splits of four per wave
+    assert shape(1, 8, 2, 2, 32) == (1, 8)        # 8 columns: still the VALU kernel
+    assert shape(1, 8, 2, 3, 32) == (4, 4)        # 12 columns: attn_pv_kernel, two entries per wave
     assert shape(1, 8, 2, 1, 8) == (1, 4)         # 8 entries: one split, four waves
     assert shape(32, 32, 8, 1, 128, 1) == (1, 8)
     assert shape(32, 32, 8, 1, 128, 2) == (2, 4)

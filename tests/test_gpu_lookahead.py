@@ -87,7 +87,7 @@ SHAPE_CASES = [
 ] + [
     (wl.Workload("pairs256_g8", B=32, H_q=64, H_kv=8, ctx=(17, 1500), budget=640, J=1, structure="none",
                  seed=83), 1),
-    # 128 pairs: eight-wave workgroups over two splits
+    # 128 pairs: eight-wave workgroups over two splits (72 table entries)
     (wl.Workload("pairs128_g8", B=16, H_q=64, H_kv=8, ctx=(1, 1500), budget=640, J=1, structure="none",
                  seed=85), 1),
 ]
@@ -100,7 +100,7 @@ def test_attention_launch_shapes_match_oracle(w, n_q, n_split):
     waves, as oasis_attn_launch_shape picks them from the pairs, the columns
     and the split count) against the oracle, per query, over ragged contexts
     and tables with padding."""
-    T = 40
+    T = 72
     splits, waves = oa().oasis_attn_launch_shape(w.B, w.H_q, w.H_kv, n_q, T, n_split)
     expect_waves = {("pairs256_g4", 0): 8, ("pairs256_g4", 1): 8, ("pairs256_g4", 2): 4,
                     ("pairs256_g8", 0): 8, ("pairs128_g8", 0): 8, ("pairs128_g8", 5): 4}
