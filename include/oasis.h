@@ -394,8 +394,10 @@ int32_t oasis_attn_num_splits(const oasis_dims *dims, int32_t T,
  * request: *splits partitions of each table row and *waves waves (4 or 8)
  * per workgroup.  The library aims at two waves per SIMD: one split of
  * four-wave workgroups when there are enough (request, KV head) pairs, else
- * one split of eight-wave workgroups, else more splits (an explicit n_split
- * fixes the splits; the waves follow).  OASIS_EINVAL for bad arguments,
+ * one split of eight-wave workgroups, else more splits as long as each
+ * keeps at least four table entries per wave (two past eight query columns,
+ * where the workgroups have four waves); an explicit n_split fixes the
+ * splits and the waves follow.  OASIS_EINVAL for bad arguments,
  * OASIS_EUNSUPPORTED past 16 query columns (n_q * H_q / H_kv). */
 int oasis_attn_launch_shape(const oasis_dims *dims, int32_t n_q, int32_t T,
                             int32_t n_split, int32_t *splits,
