@@ -389,6 +389,49 @@ def test_chain_end_to_end(name, B, ctx, copy_mode):
     assert compared == steps
 
 
+ODD_SHAPES = [
+    # name, B, H_q, H_kv, ctx, budget (tokens), J, cap, structure, copy engine
+    ("g1_tiny", 6, 4, 4, (1, 120), 96, 1, 0.1, "drift", 0),
+    ("g16_j2", 2, 32, 2, (900, 2100), 272, 2, 0.07, "drift", 1),
+    ("g2_j3", 5, 16, 8, (100, 5000), 208, 3, 0.2, "none", 0),
+    ("g8_hkv3", 1, 24, 3, 3333, 512, 1, 0.02, "drift", 1),
+    ("g8_hkv1_zipf", 4, 8, 1, (2000, 6000), 1024, 4, 0.05, "zipf", 0),
+    ("g3_fetch_all", 7, 12, 4, (16, 1600), 160, 1, 1.0, "none", 1),
+]
+
+
+@pytest.mark.parametrize("name,B,H_q,H_kv,ctx,budget,J,cap,structure,copy_mode", ODD_SHAPES,
+                         ids=[x[0] for x in ODD_SHAPES])
+def test_odd_shapes_chain_matches_oracle(name, B, H_q, H_kv, ctx, budget, J, cap, structure, copy_mode):
+    """The staged chain on shapes away from the workloads: groups of 1, 2, 3,
+    8 and 16 query heads, one or three KV heads, budgets that are not
+    multiples of 64 blocks' worth, contexts from one token to many blocks
+    past the budget, up to four drafts, caps from one block to fetch-all.
+    Each step is compared in full, as in test_chain_end_to_end."""
+    w = wl.Workload(name, B=B, H_q=H_q, H_kv=H_kv, ctx=ctx, budget=budget, J=J, cap=cap, structure=structure,
+                    seed=97)
+    C = oracle.fetch_cap_blocks(cap, w.K_b)
+    steps = 4
+    g = run_chain_gpu(w, steps, C, copy_mode)
+    ctx_np = wl.context_lengths(w).numpy()
+    kv = u16(wl.kv_pool(w))
+    summ = oracle.build_summaries(kv, ctx_np, w.bs)
+    st = oracle.StageState(w.B, w.H_kv, w.NB_max)
+    for s in range(steps):
+        gs, gsel, gn, gst, gout, gblk, gnblk = g[s]
+        os_ = oracle.score(u16(wl.lookahead(w, s)), summ, ctx_np, w.bs, w.H_kv)
+        osel, on = oracle.select(os_, ctx_np, w.bs, w.K_b)
+        assert_scores_close(gs, os_, ctx_np)
+        assert_selection_matches(gsel, gn, osel, on, os_)
+        oracle.stage(st, gsel, gn, gs, ctx_np, w.bs, w.K_b, w.K_b if s == 0 else C, s)
+        np.testing.assert_array_equal(gst, st.stamp, err_msg=f"step {s}")
+        for r in range(w.B):
+            for h in range(w.H_kv):
+                assert sorted(gblk[r, h, :gnblk[r, h]].tolist()) == st.resident(r, h).tolist()
+        oout, _ = oracle.attend(u16(wl.attention_query(w, s + 1)), kv, ctx_np, gblk, gnblk, 1 / math.sqrt(w.D))
+        assert_attn_close(bf16_to_f64(gout), oout)
+
+
 # ---------------------------------------------------------------- pipelined layers
 
 
