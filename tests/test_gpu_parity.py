@@ -557,6 +557,74 @@ def test_unstaged_pipeline_matches_oracle(compute_streams, issue_threads):
             assert_attn_close(bf16_to_f64(u16(outs[(l, t + 1)])), ref)
 
 
+ODD_PIPELINES = [
+    # name, B, H_q, H_kv, ctx, budget, J, cap (None: K/V in HBM), structure, copy engine
+    ("g16_zero_copy", 2, 32, 2, (900, 2100), 272, 2, 0.07, "drift", 0),
+    ("g3_fetch_all_dma", 3, 12, 4, (16, 1600), 160, 1, 1.0, "none", 1),
+    ("g8_hkv1_mixed", 2, 8, 1, (2000, 6000), 1024, 4, 0.05, "zipf", 2),
+    ("g1_hbm", 3, 4, 4, (1, 900), 96, 1, None, "none", 0),
+]
+
+
+@pytest.mark.parametrize("name,B,H_q,H_kv,ctx,budget,J,cap,structure,copy_mode", ODD_PIPELINES,
+                         ids=[x[0] for x in ODD_PIPELINES])
+def test_odd_shapes_pipeline_matches_oracle(name, B, H_q, H_kv, ctx, budget, J, cap, structure, copy_mode):
+    """The layer pipeline (three layers in flight, automatic streams and
+    issue threads) on shapes away from the workloads, staged through each
+    copy engine or with K/V in HBM: every layer's attention output at every
+    step equals the oracle chain run serially for that layer."""
+    from prefetch_block_scoring_amd.pipeline import LayerPipeline
+    m = oa()
+    staged = cap is not None
+    w = wl.Workload(name, B=B, H_q=H_q, H_kv=H_kv, ctx=ctx, budget=budget, J=J, cap=cap, structure=structure,
+                    seed=101)
+    C = oracle.fetch_cap_blocks(cap, w.K_b) if staged else 0
+    L, steps = 3, 5
+    ctx_cpu = wl.context_lengths(w)
+    ctx = ctx_cpu.to(DEV)
+    if staged:
+        pool = m.oasis_host_empty((w.B, w.H_kv, w.NB_max, 2, w.bs, w.D))
+        pool.copy_(wl.kv_pool(w))
+    else:
+        pool = wl.kv_pool(w, device=DEV)
+    summ = m.oasis_build_summaries(pool, ctx)
+    looks = [wl.lookahead(w, s).to(DEV) for s in range(steps + 2 * L)]
+    attn_q = [looks[max(s - 1, 0)][:, 0].contiguous() for s in range(steps + 2 * L)]
+    pipe = LayerPipeline(pool=pool, summ=summ, ctx=ctx, H_q=w.H_q, K_b=w.K_b, C=C, n_layers=L, staged=staged,
+                         J=w.J, copy_mode=copy_mode, host_threads=4)
+    outs = {}
+    for t in range(steps):
+        for l in range(L):
+            s = t + 2 * l
+            pipe.layer_step(l, t, looks[s], attn_q[s])
+            if t >= 1:
+                with torch.cuda.stream(pipe.main):
+                    outs[(l, t)] = pipe.layers[l].out.clone()
+    pipe.close()
+    torch.cuda.synchronize()
+    outs = {k: u16(v) for k, v in outs.items()}
+    ctx_np = ctx_cpu.numpy()
+    kv = u16(pool)
+    summ_o = oracle.build_summaries(kv, ctx_np, w.bs)
+    for l in range(L):
+        st = oracle.StageState(w.B, w.H_kv, w.NB_max)
+        for t in range(steps - 1):
+            s = t + 2 * l
+            sc = oracle.score(u16(looks[s]), summ_o, ctx_np, w.bs, w.H_kv)
+            sel, n = oracle.select(sc, ctx_np, w.bs, w.K_b)
+            if staged:
+                oracle.stage(st, sel, n, sc, ctx_np, w.bs, w.K_b, w.K_b if t == 0 else C, t)
+                sel = np.full((w.B, w.H_kv, w.K_b), -1, dtype=np.int32)
+                n = np.zeros((w.B, w.H_kv), dtype=np.int32)
+                for r in range(w.B):
+                    for h in range(w.H_kv):
+                        res = st.resident(r, h)
+                        sel[r, h, :len(res)] = res
+                        n[r, h] = len(res)
+            ref, _ = oracle.attend(u16(attn_q[s + 1]), kv, ctx_np, sel, n, 1 / math.sqrt(w.D))
+            assert_attn_close(bf16_to_f64(outs[(l, t + 1)]), ref)
+
+
 def test_pipeline_timing_values_match_totals():
     """Per-launch timings of the native pipeline: one value per timed launch
     of each kind (attention from step 1 on), all positive, summing to the
